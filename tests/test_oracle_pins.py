@@ -1,0 +1,422 @@
+"""Pins for the CPU oracle: each test ties the oracle to something other than
+itself -- a dense brute force built with numpy/scipy on tiny inputs,
+invariants of the method, closed forms, and exhaustive checks of the e4m3
+codec against the bit-field definition, a brute-force nearest search and
+torch's float8_e4m3fn cast.  CPU only.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp, softmax
+
+import oracle
+from mla_paged_kv_05_amd import workloads as W
+
+SCALE = 576 ** -0.5
+
+
+def bf16(bits):
+    """Independent bf16 widening via torch (bit reinterpretation)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def dense_keys(p, b):
+    """Logical-order K of sequence b gathered with numpy fancy indexing."""
+    L = int(p.seqlens[b])
+    j = np.arange(L)
+    return bf16(p.kv[p.block_table[b, j // 64], j % 64])
+
+
+def brute_row(q, K, scale, d_v=512):
+    if K.shape[0] == 0:
+        return np.zeros(d_v), -np.inf
+    s = scale * (K @ q)
+    return softmax(s) @ K[:, :d_v], logsumexp(s)
+
+
+def brute_decode(p):
+    o = np.zeros((p.batch, p.s_q, p.h_q, p.d_v))
+    lse = np.zeros((p.batch, p.s_q, p.h_q))
+    for b in range(p.batch):
+        Kall = dense_keys(p, b)
+        L = Kall.shape[0]
+        for t in range(p.s_q):
+            if p.indices is not None:
+                ids = p.indices[b, t]
+                ids = ids[ids >= 0]
+                flat = p.kv.reshape(-1, p.kv.shape[-1])
+                K = bf16(flat[ids])
+            else:
+                vis = L if not p.causal else max(0, min(L, L - p.s_q + t + 1))
+                K = Kall[:vis]
+            for h in range(p.h_q):
+                o[b, t, h], lse[b, t, h] = brute_row(bf16(p.q[b, t, h]), K, p.scale)
+    return o, lse
+
+
+def tiny(seqlens=(37, 100, 1), s_q=1, h_q=4, causal=False, seed=7):
+    return W.make_dense("t", list(seqlens), s_q=s_q, h_q=h_q, seed=seed, causal=causal)
+
+
+@pytest.mark.parametrize("seqlens,s_q,causal", [
+    ((37, 100, 1), 1, False),
+    ((64, 200, 129), 2, True),
+    ((5, 65), 3, True),
+])
+def test_paged_matches_dense_bruteforce(seqlens, s_q, causal):
+    p = tiny(seqlens, s_q=s_q, causal=causal)
+    r = oracle.decode(p)
+    o, lse = brute_decode(p)
+    assert np.max(np.abs(r["o"] - o)) < 1e-12
+    assert np.max(np.abs(r["lse"] - lse)) < 1e-12
+
+
+def test_sparse_matches_dense_bruteforce():
+    p = W.make_sparse_bf16_from_dense(tiny((37, 150, 3), s_q=2), topk=70, seed=3)
+    r = oracle.decode(p)
+    o, lse = brute_decode(p)
+    assert np.max(np.abs(r["o"] - o)) < 1e-12
+    np.testing.assert_array_equal(np.isinf(r["lse"]), np.isinf(lse))
+    fin = np.isfinite(lse)
+    assert np.max(np.abs(r["lse"][fin] - lse[fin])) < 1e-12
+
+
+def test_block_table_permutation_is_bitwise_invariant():
+    p = tiny((100, 190, 64), h_q=3)
+    r1 = oracle.decode(p)
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(p.num_blocks)          # new physical home of block x
+    kv2 = np.empty_like(p.kv)
+    kv2[perm] = p.kv
+    bt2 = np.where(p.block_table >= 0, perm[np.maximum(p.block_table, 0)], -1).astype(np.int32)
+    p2 = W.Problem(**{**p.__dict__, "kv": kv2, "block_table": bt2})
+    r2 = oracle.decode(p2)
+    assert np.array_equal(r1["o"], r2["o"]) and np.array_equal(r1["lse"], r2["lse"])
+
+
+@pytest.mark.parametrize("nparts", [2, 3, 7])
+def test_split_combine_equals_unsplit(nparts):
+    p = tiny((300, 129), h_q=2)
+    full = oracle.decode(p)
+    rng = np.random.default_rng(nparts)
+    for b in range(p.batch):
+        L = int(p.seqlens[b])
+        lab = rng.integers(0, nparts, size=L)   # random (non-contiguous) partition
+        for h in range(p.h_q):
+            ls, os_ = [], []
+            for s in range(nparts):
+                o, l = oracle.decode_row_subset(p, b, 0, h, np.nonzero(lab == s)[0])
+                ls.append(l)
+                os_.append(o)
+            o, l = oracle.combine(np.array(ls), np.array(os_))
+            ref = full["o"][b, 0, h]
+            assert np.max(np.abs(o - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+            assert abs(l - full["lse"][b, 0, h]) < 1e-12
+
+
+def test_combine_empty_parts():
+    o, l = oracle.combine(np.array([-np.inf, -np.inf]), np.ones((2, 512)))
+    assert l == -np.inf and np.all(o == 0)
+    o, l = oracle.combine(np.array([-np.inf, 0.5]), np.stack([np.full(512, np.nan), np.ones(512)]))
+    assert l == 0.5 and np.all(o == 1.0)
+
+
+def test_closed_forms():
+    rng = np.random.default_rng(0)
+    K = rng.standard_normal((9, 576))
+    # q = 0: uniform weights, O = mean of V rows, LSE = ln n
+    o, l = oracle.attend(np.zeros(576), K, 512, SCALE)
+    assert np.max(np.abs(o - K[:, :512].mean(0))) < 1e-14 and abs(l - math.log(9)) < 1e-15
+    # n = 1: O = V_0 exactly, LSE = s_0
+    q = rng.standard_normal(576)
+    o, l = oracle.attend(q, K[:1], 512, SCALE)
+    assert np.array_equal(o, K[0, :512]) and abs(l - SCALE * float(q @ K[0])) < 1e-12
+    # all keys equal: O = V, LSE = s + ln n
+    Ke = np.repeat(K[:1], 5, axis=0)
+    o, l = oracle.attend(q, Ke, 512, SCALE)
+    assert np.max(np.abs(o - K[0, :512])) < 1e-13
+    assert abs(l - (SCALE * float(q @ K[0]) + math.log(5))) < 1e-12
+    # empty key set
+    o, l = oracle.attend(q, np.zeros((0, 576)), 512, SCALE)
+    assert l == -np.inf and np.all(o == 0)
+
+
+def test_two_key_worked_example():
+    """q = 24*e0, K0 = e0, K1 = 2*e0 gives scores 1 and 2 under scale 1/24:
+    LSE = 2 + ln(1 + e^-1), O_0 = (1 + 2e)/(1 + e), other dims 0."""
+    q = np.zeros(576); q[0] = 24.0
+    K = np.zeros((2, 576)); K[0, 0] = 1.0; K[1, 0] = 2.0
+    o, l = oracle.attend(q, K, 512, SCALE)
+    assert abs(l - (2.0 + math.log1p(math.exp(-1.0)))) < 1e-15
+    assert abs(o[0] - (1 + 2 * math.e) / (1 + math.e)) < 1e-15 and np.all(o[1:] == 0)
+
+
+def test_v_is_leading_512_dims_of_k():
+    """Only the first 512 dims enter O; the 64 RoPE dims enter scores only."""
+    rng = np.random.default_rng(1)
+    K = rng.standard_normal((4, 576))
+    q = np.zeros(576); q[520] = 3.0  # score from a RoPE dim only
+    o, l = oracle.attend(q, K, 512, SCALE)
+    w = softmax(SCALE * 3.0 * K[:, 520])
+    assert np.max(np.abs(o - w @ K[:, :512])) < 1e-13
+
+
+def test_causal_special_cases():
+    p = tiny((77, 130), s_q=2, causal=True, h_q=3)
+    rc = oracle.decode(p)
+    pn = W.Problem(**{**p.__dict__, "causal": False})
+    rn = oracle.decode(pn)
+    # token 1 (the last) sees everything: equals non-causal
+    assert np.array_equal(rc["o"][:, 1], rn["o"][:, 1])
+    # token 0 sees L-1 keys: equals non-causal over the first L-1 positions
+    for b in range(p.batch):
+        for h in range(p.h_q):
+            o, l = oracle.decode_row_subset(p, b, 0, h, np.arange(int(p.seqlens[b]) - 1))
+            assert np.max(np.abs(o - rc["o"][b, 0, h])) < 1e-13
+            assert abs(l - rc["lse"][b, 0, h]) < 1e-13
+    # s_q = 1: causal equals non-causal
+    p1 = tiny((77, 130), s_q=1, causal=True)
+    r1 = oracle.decode(p1)
+    r1n = oracle.decode(W.Problem(**{**p1.__dict__, "causal": False}))
+    assert np.array_equal(r1["o"], r1n["o"])
+
+
+def test_empty_rows():
+    p = tiny((0, 5), s_q=3, causal=True, h_q=2)  # seq 1: token 0 sees 3 keys
+    r = oracle.decode(p)
+    assert np.all(r["o"][0] == 0) and np.all(r["lse"][0] == -np.inf)
+    assert np.all(np.isfinite(r["lse"][1]))
+    p2 = tiny((2, 5), s_q=4, causal=True, h_q=2)  # seq 0: tokens 0,1 see nothing
+    r2 = oracle.decode(p2)
+    assert np.all(r2["lse"][0, :2] == -np.inf) and np.all(r2["o"][0, :2] == 0)
+    assert np.all(np.isfinite(r2["lse"][0, 2:]))
+
+
+def test_sparse_special_cases():
+    p = tiny((90, 140), s_q=1, h_q=3)
+    dense = oracle.decode(p)
+    # indices enumerating every position equal dense attention
+    topk = 140
+    idx = np.full((2, 1, topk), -1, dtype=np.int32)
+    for b in range(2):
+        L = int(p.seqlens[b])
+        j = np.arange(L)
+        idx[b, 0, :L] = p.block_table[b, j // 64] * 64 + j % 64
+    ps = W.Problem(**{**p.__dict__, "indices": idx, "topk": topk})
+    rs = oracle.decode(ps)
+    assert np.max(np.abs(rs["o"] - dense["o"])) < 1e-13
+    assert np.max(np.abs(rs["lse"] - dense["lse"])) < 1e-13
+    # order of indices does not matter
+    rng = np.random.default_rng(2)
+    idx2 = idx.copy()
+    for b in range(2):
+        rng.shuffle(idx2[b, 0])
+    rs2 = oracle.decode(W.Problem(**{**ps.__dict__, "indices": idx2}))
+    assert np.max(np.abs(rs2["o"] - rs["o"])) < 1e-13
+    # all -1: empty row
+    rs3 = oracle.decode(W.Problem(**{**ps.__dict__, "indices": np.full_like(idx, -1)}))
+    assert np.all(rs3["o"] == 0) and np.all(rs3["lse"] == -np.inf)
+
+
+# ----------------------------------------------------------------- e4m3
+def e4m3_bitfield(c):
+    s = -1.0 if c & 0x80 else 1.0
+    e, m = (c >> 3) & 15, c & 7
+    if e == 15 and m == 7:
+        return math.nan
+    return s * (m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+
+
+def test_e4m3_decode_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_decode(codes)
+    ref = np.array([e4m3_bitfield(int(c)) for c in codes])
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin]) and np.array_equal(got[fin], lib[fin])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+    assert got[0x38] == 1.0 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+
+
+def brute_encode(x):
+    """Nearest finite e4m3 code by exhaustive search; ties to the even code;
+    |x| >= 448 saturates."""
+    if math.isnan(x):
+        return 0xFF if math.copysign(1, x) < 0 else 0x7F
+    sign = 0x80 if math.copysign(1, x) < 0 else 0
+    a = abs(x)
+    if a >= 448:
+        return sign | 0x7E
+    best, bd = None, None
+    for c in range(0x7F):
+        d = abs(e4m3_bitfield(c) - a)
+        if bd is None or d < bd or (d == bd and (c & 1) == 0 and (best & 1) == 1):
+            best, bd = c, d
+    return sign | best
+
+
+def test_e4m3_encode_against_bruteforce():
+    pos = np.array([e4m3_bitfield(c) for c in range(0x7F)])
+    mids = (pos[:-1] + pos[1:]) / 2
+    rng = np.random.default_rng(11)
+    sweep = np.concatenate([
+        pos, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+        rng.uniform(0, 460, 400), np.exp2(rng.uniform(-12, 9, 400)),
+        [447.9, 448.0, 463.9, 464.0, 1e6, np.inf, 2.0 ** -10, 2.0 ** -11, 1e-30],
+    ])
+    sweep = np.concatenate([sweep, -sweep])
+    got = oracle.e4m3_encode(sweep)
+    ref = np.array([brute_encode(float(v)) for v in sweep], dtype=np.uint8)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (sweep[bad[:5]], got[bad[:5]], ref[bad[:5]])
+    # torch's RNE cast agrees wherever it does not overflow; torch narrows
+    # fp64 to fp32 first, so only fp32-exact inputs avoid its double rounding
+    inr = (np.abs(sweep) < 448) & (sweep.astype(np.float32).astype(np.float64) == sweep)
+    lib = torch.from_numpy(sweep[inr].astype(np.float64)).to(torch.float8_e4m3fn)
+    assert np.array_equal(lib.view(torch.uint8).numpy(), got[inr])
+
+
+def test_fp8_record_dequant():
+    """A V3.2 record dequantises as code * tile scale for dims < 512 and bf16
+    for the 64 RoPE dims: compare the oracle's sparse read of one token with
+    a key built by hand from the record's fields."""
+    p = W.make_sparse_fp8("f", batch=1, s_q=1, h_q=1, cache_len=128, topk=1, seed=3, pad_frac=0)
+    tok = int(p.indices[0, 0, 0])
+    rec = p.kv.reshape(-1, 656)[tok]
+    sc = np.frombuffer(rec[512:528].tobytes(), dtype=np.float32).astype(np.float64)
+    key = np.concatenate([
+        np.array([e4m3_bitfield(int(c)) for c in rec[:512]]) * np.repeat(sc, 128),
+        bf16(np.frombuffer(rec[528:].tobytes(), dtype=np.uint16)),
+    ])
+    # with one key, O = V exactly
+    r = oracle.decode(p)
+    assert np.array_equal(r["o"][0, 0, 0], key[:512])
+    assert abs(r["lse"][0, 0, 0] - p.scale * float(bf16(p.q[0, 0, 0]) @ key)) < 1e-12
+
+
+# ------------------------------------------------------- norm and rope
+def test_rmsnorm_closed_form():
+    w = np.linspace(0.5, 1.5, 576)
+    for c in (0.0, 1.0, -3.25, 1e-4):
+        y = oracle.rmsnorm(np.full(576, c), w, 1e-6)
+        assert np.max(np.abs(y - w * c / math.sqrt(c * c + 1e-6))) < 1e-14
+    x = np.random.default_rng(3).standard_normal(576)
+    y = oracle.rmsnorm(x, np.ones(576), 0.0)
+    assert abs(math.sqrt(np.mean(y * y)) - 1.0) < 1e-14
+
+
+def test_rope_identities():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(64)
+    assert np.array_equal(oracle.rope(x, 0.0), x)
+    for pos in (1.0, 17.0, 16383.0):
+        y = oracle.rope(x, pos)
+        z = oracle.rope(y, pos, sign=-1.0)
+        assert np.max(np.abs(z - x)) < 1e-12
+        n0 = np.hypot(x[0::2], x[1::2])
+        assert np.max(np.abs(np.hypot(y[0::2], y[1::2]) - n0)) < 1e-12
+        # pair 0 turns by exactly pos radians; pair 16 by pos * 10000^(-1/2) = pos/100
+        for i, ang in ((0, pos), (16, pos / 100.0)):
+            c, s = math.cos(ang), math.sin(ang)
+            a, b = x[2 * i], x[2 * i + 1]
+            assert abs(y[2 * i] - (a * c - b * s)) < 1e-12
+            assert abs(y[2 * i + 1] - (a * s + b * c)) < 1e-12
+
+
+def test_fused_pipeline_order_and_cast():
+    """Fused decode = RMSNorm -> RoPE on q, attention, conjugate RoPE on O's
+    last 64 dims, amax/448 scale, e4m3 codes of O/scale."""
+    p = W.make_dense("f", [70, 3], s_q=1, h_q=2, seed=9, fused=True)
+    r = oracle.decode(p)
+    w = bf16(p.norm_w)
+    for b in range(p.batch):
+        K = dense_keys(p, b)
+        pos = float(p.seqlens[b] - 1)
+        for h in range(p.h_q):
+            q = bf16(p.q[b, 0, h])
+            qn = q * w / math.sqrt(np.mean(q * q) + 1e-6)
+            th = pos * 10000.0 ** (-np.arange(32) * 2 / 64)
+            a, c = qn[512::2].copy(), qn[513::2].copy()
+            qn[512::2], qn[513::2] = a * np.cos(th) - c * np.sin(th), a * np.sin(th) + c * np.cos(th)
+            o, l = brute_row(qn, K, p.scale)
+            a, c = o[448::2].copy(), o[449::2].copy()
+            o[448::2], o[449::2] = a * np.cos(th) + c * np.sin(th), -a * np.sin(th) + c * np.cos(th)
+            assert np.max(np.abs(r["o"][b, 0, h] - o)) < 1e-12
+            assert abs(r["lse"][b, 0, h] - l) < 1e-12
+            sc = np.max(np.abs(o)) / 448
+            assert abs(r["oscale"][b, 0, h] - sc) <= 1e-12 * sc
+            o = r["o"][b, 0, h]  # the codes encode the oracle's own O (pinned above)
+            sc = r["oscale"][b, 0, h]
+            codes = r["codes"][b, 0, h]
+            assert codes[np.argmax(np.abs(o))] & 0x7F == 0x7E
+            deq = np.array([e4m3_bitfield(int(c)) for c in codes]) * sc
+            # within half an e4m3 step of the value being encoded
+            ulp = np.where(np.abs(o / sc) < 2 ** -6, 2.0 ** -9,
+                           2.0 ** (np.floor(np.log2(np.maximum(np.abs(o / sc), 1e-300))) - 3))
+            assert np.all(np.abs(deq - o) <= 0.5 * ulp * sc * (1 + 1e-12))
+
+
+# ----------------------------------------------------------- scheduler
+def sched_check(seqlens, rows, topk, S):
+    meta, ns = oracle.sched_plan(seqlens, rows, topk, S)
+    B = len(seqlens)
+    nb = [(-(-topk // 64)) if topk else -(-max(int(L), 0) // 64) for L in seqlens]
+    items = [max(n, 1) for n in nb]
+    F = max(1, -(-min(rows, 128) // 32))
+    # walk the slots: every (b, item) exactly once, in order, contiguous
+    seen = []
+    for s in range(S):
+        b0, j0, b1, j1, k0, cnt = meta[s, :6]
+        if b0 < 0:
+            assert cnt == 0
+            continue
+        run = []
+        for b in range(b0, b1 + 1):
+            lo = j0 if b == b0 else 0
+            hi = j1 if b == b1 else items[b]
+            run += [(b, j) for j in range(lo, hi)]
+        assert len(run) == cnt
+        cost = len(run) + F * sum(1 for (b, j) in run if j == 0)
+        tot = sum(items) + F * B
+        assert cost <= max(-(-(tot + 1) // S), 2 * F) + F
+        seen += run
+    assert seen == [(b, j) for b in range(B) for j in range(items[b])]
+    # splits per batch = number of slots touching it; k0 numbers them in order
+    touch = [[] for _ in range(B)]
+    for s in range(S):
+        b0, j0, b1, j1, k0, cnt = meta[s, :6]
+        if b0 < 0:
+            continue
+        for b in range(b0, b1 + 1):
+            touch[b].append(s)
+        assert k0 == (len(touch[b0]) - 1)
+    assert ns[0] == 0
+    for b in range(B):
+        assert ns[b + 1] - ns[b] == len(touch[b])
+    assert ns[B] <= B + S - 1
+    return meta, ns
+
+
+@pytest.mark.parametrize("seqlens,rows,topk,S", [
+    ([37, 100], 16, 0, 8),
+    ([0, 0, 5, 0], 128, 0, 4),
+    (list(range(0, 4000, 97)), 128, 0, 256),
+    ([65536] * 3 + [300] * 20, 256, 0, 128),
+    ([10] * 64, 128, 2048, 256),
+    ([1], 128, 0, 1),
+    ([], 128, 0, 16),
+])
+def test_sched_plan_invariants(seqlens, rows, topk, S):
+    sched_check(np.array(seqlens, dtype=np.int32), rows, topk, S)
+
+
+def test_sched_plan_workload_sizes():
+    for p in (W.config1(),):
+        sched_check(p.seqlens, p.rows, 0, 256)
+    rng = np.random.default_rng(0)
+    sched_check(rng.integers(1024, 8193, 64).astype(np.int32), 128, 0, 256)
+    sched_check(rng.integers(0, 3000, 300).astype(np.int32), 32, 0, 80)
