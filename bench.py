@@ -1,0 +1,222 @@
+"""Benchmark of the paged MLA decode hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: the split-KV metadata
+call, the decode kernel and the LSE combine.  The default workload is the
+memory-bound bf16 decode (batch 64, s_q 1, h_q 128, d_qk 576, d_v 512,
+seqlens ~ U{1024..8192}, 64-token pages, shuffled block table over a 1.2x
+pool), seeded and synthetic.  Inputs are resident in HBM before timing; the
+KV pool and queries are replicated into several copies that steps rotate
+through, so a step never finds its KV in the 256 MB Infinity Cache left by
+the previous step.
+
+Prints one JSON line with the metric (effective HBM GB/s of algorithmic
+bytes per step), the TFLOPS, the decode kernel's roofline position and the
+CPU oracle's rate on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(p):
+    """Bytes and flops the method must move / do (visible keys only)."""
+    L = p.seqlens.astype(np.int64)
+    rows = p.s_q * p.h_q
+    if p.indices is None:
+        if p.causal:
+            vis = np.stack([np.clip(L - p.s_q + t + 1, 0, L) for t in range(p.s_q)], 1)
+        else:
+            vis = np.repeat(L[:, None], p.s_q, 1)
+        keys_flops = int(vis.sum()) * p.h_q
+        kv = int(L.sum()) * 1152
+        tables = int(((L + 63) // 64).sum()) * 4
+    else:
+        valid = (p.indices >= 0)
+        keys_flops = int(valid.sum()) * p.h_q
+        per = 656 if p.kv_format == "fp8v32" else 1152
+        kv = sum(len(np.unique(p.indices[b][p.indices[b] >= 0])) for b in range(p.batch)) * per
+        tables = p.indices.size * 4
+    q = p.batch * rows * 576 * 2
+    o = p.batch * rows * (512 + 4 if p.fused else 512 * 2)
+    lse = p.batch * rows * 4
+    nbytes = kv + q + o + lse + tables + p.batch * 4
+    flops = 2 * keys_flops * (576 + 512)
+    return nbytes, flops
+
+
+def make_workload(name):
+    from mla_paged_kv_05_amd import workloads as W
+    return {"dense_b64_h128_L1k-8k": W.config2, "splitkv_b128_sq2_causal": W.config3,
+            "sparse_fp8_b64_top2048": W.config4, "fused_b32_h128": lambda: W.config5(32),
+            "fused_b1_h128": lambda: W.config5(1)}[name]()
+
+
+def traffic_record(kernel_src):
+    """HBM traffic measured by rocprofv3 PMC counters for the current kernel
+    source, or None when the counters were taken on other code."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    return rec if rec.get("kernel_sha") == h else None
+
+
+def cpu_baseline(p, nbytes):
+    import oracle
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.decode(p, nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole workload ({p.batch} sequences), fp64, {dt:.2f} s",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense_b64_h128_L1k-8k")
+    ap.add_argument("--rotate", type=int, default=0, help="KV copies (0 = enough for >= 1 GiB)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences shard across GPUs with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mla_paged_kv_05_amd import binding as B
+
+    dev = torch.device("cuda", 0)
+    t0 = time.time()
+    p = make_workload(args.workload)
+    nbytes, flops = algorithmic(p)
+    log(f"workload {p.name}: generated in {time.time() - t0:.1f}s; algorithmic "
+        f"{nbytes / 1e6:.1f} MB, {flops / 1e9:.1f} GFLOP per step")
+
+    kv_np = p.kv.view(np.int16) if p.kv_format == "bf16" else p.kv
+    kv_bytes = kv_np.nbytes
+    R = args.rotate or max(2, int(np.ceil(1.0 * 2 ** 30 / kv_bytes)))
+    kv_host = torch.from_numpy(kv_np)
+    kvs = [kv_host.to(dev) for _ in range(R)]
+    if p.kv_format == "bf16":
+        kvs = [k.view(torch.bfloat16) for k in kvs]
+    qs = [torch.from_numpy(p.q.view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(R)]
+    bt = torch.from_numpy(np.ascontiguousarray(p.block_table)).to(dev)
+    sl = torch.from_numpy(np.ascontiguousarray(p.seqlens)).to(dev)
+    idx = None if p.indices is None else torch.from_numpy(p.indices).to(dev)
+    topk = p.topk if idx is not None else 0
+    rows = p.s_q * p.h_q
+    lib = B.load_library()
+    S = B.num_sched_slots(rows, dev)
+    meta = torch.empty((S, 8), dtype=torch.int32, device=dev)
+    ns = torch.empty(p.batch + 1, dtype=torch.int32, device=dev)
+    ws = torch.empty(B.workspace_bytes(p.batch, p.s_q, p.h_q, S), dtype=torch.uint8, device=dev)
+    out = torch.empty((p.batch, p.s_q, p.h_q, 512), dtype=torch.uint8 if p.fused else torch.bfloat16,
+                      device=dev)
+    lse = torch.empty((p.batch, p.s_q, p.h_q), dtype=torch.float32, device=dev)
+    fused = None
+    if p.fused:
+        fused = {"norm_weight": torch.from_numpy(p.norm_w.view(np.int16)).view(torch.bfloat16).to(dev),
+                 "eps": p.eps, "rope_base": p.rope_base,
+                 "out_scale": torch.empty((p.batch, p.s_q, p.h_q), dtype=torch.float32, device=dev)}
+    params = []
+    for r in range(R):
+        pr = B._params(qs[r], kvs[r], bt if idx is None else None, sl, meta, ns, p.causal, idx, p.scale,
+                       p.kv_format, ws, out, lse, fused)
+        pr.flags = B.MLA_FLAG_DEFER_COMBINE
+        params.append(pr)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    sl_p, meta_p, ns_p = ctypes.c_void_p(sl.data_ptr()), ctypes.c_void_p(meta.data_ptr()), ctypes.c_void_p(ns.data_ptr())
+
+    def step(i, ev=None):
+        pr = params[i % R]
+        if ev is not None:
+            ev[0].record(stream)
+        st = lib.mla_get_metadata(sl_p, p.batch, rows, 1, topk, S, meta_p, ns_p, sh)
+        if ev is not None:
+            ev[1].record(stream)
+        st |= lib.mla_decode(ctypes.byref(pr), sh)
+        if ev is not None:
+            ev[2].record(stream)
+        st |= lib.mla_combine(ctypes.byref(pr), sh)
+        if st != 0:
+            raise RuntimeError(lib.mla_last_error().decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    dec_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)]
+    meta_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
+    dec_avg = float(np.mean(dec_ms))
+    log(f"step {ms * 1e3:.1f} us (wall {wall / args.steps * 1e6:.1f} us); decode kernel avg "
+        f"{dec_avg * 1e3:.1f} us (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 "
+        f"{np.percentile(dec_ms, 90) * 1e3:.1f}); metadata {np.mean(meta_ms) * 1e3:.1f} us; rotation {R}")
+
+    value = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    achieved = nbytes / (dec_avg * 1e-3) / 1e9
+    src = os.path.join(ROOT, "mla_paged_kv_05_amd", "csrc", "mla_kernels.hip")
+    tr = traffic_record(src)
+    traffic = None if tr is None else tr["bytes_per_launch"]
+    res = {
+        "metric": "MLA paged decode effective HBM GB/s (algorithmic bytes) + TFLOPS, b=64 h_q=128 seq<=8K",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, shaped like the workload)",
+        "config": {"workload": p.name, "batch": p.batch, "s_q": p.s_q, "h_q": p.h_q, "d_qk": 576,
+                   "d_v": 512, "page": 64, "kv_format": p.kv_format, "causal": bool(p.causal),
+                   "sparse_topk": topk, "fused": bool(p.fused), "parallelism": "single GPU",
+                   "kv_copies_rotated": R},
+        "tflops": round(tflops, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "k_decode", "kernel_avg_us": round(dec_avg * 1e3, 2),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle on the same workload ...")
+        res["cpu_baseline"] = cpu_baseline(p, nbytes)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * mla.h -- C ABI of libmla.so: paged Multi-head Latent Attention decoding
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For every sequence b, query token t and head h, one query
+ * row of d_qk = 576 dims (512 latent + 64 decoupled-RoPE dims) attends to a
+ * single shared latent KV head stored in a paged cache of 64-token blocks;
+ * V is the first d_v = 512 dims of K.  The result is the softmax-weighted
+ * sum O (d_v dims) and the log-sum-exp of the scaled scores.
+ *   - "FlashMLA" (AI Wiki), section "How is FlashMLA designed?": fused,
+ *     tiled attention with an online softmax over KV streamed through
+ *     on-chip memory; a paged KV cache of fixed-size blocks (64 tokens,
+ *     section "What is FlashMLA?") and variable-length sequences.
+ *   - "FlashMLA" Ampere-adaptation README (gitlite), section "Usage": a
+ *     scheduling-metadata call made once per decoding step, taking
+ *     cache_seqlens, s_q*h_q/h_kv and h_kv, whose results feed every
+ *     per-layer decode call; the decode call takes q, the paged cache,
+ *     block_table, cache_seqlens, dv, the metadata and a causal flag and
+ *     returns (o, lse).
+ *   - "FlashMLA" (AI Wiki), section "Interfaces": sparse decoding takes an
+ *     indices tensor (batch, s_q, topk) whose entries encode the page block
+ *     and the offset (here: flat token id = block*64 + offset), -1 marking
+ *     an invalid entry, with block_table then ignored.
+ *   - Same page, section "The FP8 and FP4 KV cache": the V3.2 token record,
+ *     512 e4m3 values + four fp32 scales (one per 128 dims) + 64 bf16 RoPE
+ *     values, 656 bytes, data before scales.
+ *   - "FlashMLA fused norm-RoPE-attention-RoPE-cast kernel" card, section
+ *     "Arithmetic intensity": optional Q-RMSNorm and Q-RoPE before
+ *     attention and conjugate O-RoPE plus an FP8 cast after it, fused.
+ *
+ * Conventions.  Every pointer is DEVICE memory unless marked [host].  All
+ * calls that take a `stream` (a hipStream_t; NULL = the null stream) are
+ * asynchronous on it and never synchronise the host.  The caller allocates
+ * and owns every buffer, including metadata and workspace; the library
+ * keeps only a per-device cache of device properties.  Validation reads
+ * scalar arguments only (never device memory).  Errors are returned, never
+ * thrown; mla_last_error() gives a thread-local message for the last
+ * non-OK status.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad alignment, bad struct_size */
+  MLA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (shape outside the supported set) */
+  MLA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than mla_workspace_bytes()   */
+  MLA_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed                */
+} mla_status;
+
+typedef enum {
+  MLA_KV_BF16 = 0,     /* [num_blocks][64][576] bf16, 1152 B per token                  */
+  MLA_KV_FP8_V32 = 1   /* [num_blocks][64][656] bytes: 512 e4m3 | 4 fp32 LE | 64 bf16    */
+} mla_kv_format;
+
+#define MLA_PAGE_SIZE 64
+#define MLA_D_QK 576
+#define MLA_D_V 512
+#define MLA_MAX_BATCH 16384
+
+/* [host] Number of scheduler slots S to use on `device` for decode calls
+ * with `rows_per_kv_head` = s_q*h_q/h_kv query rows: one slot per compute
+ * unit per 128-row group.  Returns a value >= 1, or 0 on error. */
+int32_t mla_num_sched_slots(int32_t device, int32_t rows_per_kv_head);
+
+/* [host] int32 element counts of the two metadata arrays. */
+size_t mla_sched_meta_ints(int32_t num_slots);  /* = 8 * num_slots  */
+size_t mla_num_splits_ints(int32_t batch);      /* = batch + 1      */
+
+/* Split-KV scheduling metadata (once per decoding step; reusable by every
+ * decode call with the same cache_seqlens contents, rows and topk).
+ *   cache_seqlens     int32 [batch], each >= 0 (read on the device)
+ *   rows_per_kv_head  s_q*h_q/h_kv (>= 1)
+ *   h_kv              must be 1
+ *   topk              0 = dense; > 0: sparse with topk indices per query row
+ *   num_slots         S, normally mla_num_sched_slots()
+ *   sched_meta        int32 [S][8] out: per slot {b0, j0, b1, j1_end, k0, items, 0, 0}
+ *   num_splits        int32 [batch+1] out: prefix offsets of per-sequence splits
+ * The split rule: a sequence has n_b = ceil(len/64) work items (ceil(topk/64)
+ * when sparse; an empty sequence keeps one item with no KV); with
+ * F = max(1, ceil(min(rows,128)/32)), the items are laid on a line where
+ * sequence b starts at U_b = sum_{b'<b}(F + n_b') and its item j sits at
+ * U_b + F + j; with cap = max(ceil((U_batch+1)/S), 2F), slot s takes the
+ * items at positions [s*cap, (s+1)*cap).  Errors: INVALID_ARG for null
+ * pointers or bad sizes, UNSUPPORTED for h_kv != 1 or batch > MLA_MAX_BATCH. */
+mla_status mla_get_metadata(const int32_t* cache_seqlens, int32_t batch,
+                            int32_t rows_per_kv_head, int32_t h_kv, int32_t topk,
+                            int32_t num_slots, int32_t* sched_meta, int32_t* num_splits,
+                            void* stream);
+
+/* [host] Workspace bytes a decode call needs (fp32 split partials). */
+size_t mla_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int32_t num_slots);
+
+typedef struct mla_decode_params {
+  uint32_t struct_size;        /* sizeof(mla_decode_params)                                */
+  int32_t batch, s_q, h_q, h_kv, d_qk, d_v;  /* h_kv == 1, d_qk == 576, d_v == 512          */
+  const void* q;               /* bf16 [batch][s_q][h_q][576], 16-byte aligned              */
+  const void* kv;              /* paged cache, format below, 16-byte aligned                */
+  int32_t kv_format;           /* mla_kv_format                                            */
+  int32_t page_size;           /* must be 64                                               */
+  int64_t num_blocks;          /* blocks in the pool                                       */
+  const int32_t* block_table;  /* int32 [batch][max_blocks_per_seq]; may be NULL if sparse  */
+  int32_t max_blocks_per_seq;
+  const int32_t* cache_seqlens;/* int32 [batch]                                            */
+  float softmax_scale;         /* applied to q.K (typically 576^-0.5)                     */
+  int32_t causal;              /* bottom-right aligned: token t sees keys j <= len-s_q+t    */
+  const int32_t* indices;      /* NULL = dense; else int32 [batch][s_q][topk] flat token ids, -1 = masked */
+  int32_t topk;
+  const int32_t* sched_meta;   /* from mla_get_metadata with the same rows and topk         */
+  const int32_t* num_splits;
+  int32_t num_slots;
+  void* workspace;             /* >= mla_workspace_bytes(), 256-byte aligned                */
+  size_t workspace_bytes;
+  void* out;                   /* bf16 [batch][s_q][h_q][512]; fused: e4m3 bytes, same shape */
+  float* lse;                  /* fp32 [batch][s_q][h_q], natural log of sum exp(scaled scores); -inf for an empty row */
+  int32_t fused;               /* 1 = RMSNorm+RoPE on q, conjugate RoPE + FP8 cast on O      */
+  const void* norm_weight;     /* fused: bf16 [576]                                        */
+  float norm_eps;              /* fused: RMSNorm epsilon                                   */
+  float rope_base;             /* fused: RoPE base (positions are len - s_q + t)           */
+  float* out_scale;            /* fused: fp32 [batch][s_q][h_q], O = codes * scale          */
+  uint32_t flags;              /* MLA_FLAG_* bits; 0 = decode and merge in one call         */
+} mla_decode_params;
+
+/* mla_decode leaves split partials in the workspace for a later
+ * mla_combine call on the same stream (e.g. to time or overlap it). */
+#define MLA_FLAG_DEFER_COMBINE 1u
+
+/* Paged MLA decode: O and LSE for every query row (see the file comment).
+ * A row that sees no key gets O = 0 and LSE = -inf.  Sequences whose work
+ * the schedule splits write fp32 partials to the workspace and a combine
+ * pass merges them by LSE; others write their output directly.
+ * Supported: h_kv = 1, d_qk = 576, d_v = 512, page 64, s_q*h_q <= 65536;
+ * sparse needs causal = 0 and (s_q == 1 or h_q % 128 == 0); FP8 KV needs
+ * indices; fused needs s_q*h_q of whole heads as above.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP (launch failure). */
+mla_status mla_decode(const mla_decode_params* params, void* stream);
+
+/* The LSE merge of split partials ("FlashMLA" Ampere-adaptation README,
+ * section "Usage": the decode returns (o, lse) over the whole KV length).
+ * For every sequence the schedule split, every row: lse = ln sum_s e^{lse_s},
+ * O = sum_s e^{lse_s - lse} O_s (splits in ascending order; -inf partials
+ * weigh 0), then the bf16 (or fused FP8) output and LSE are written.  Only
+ * needed after mla_decode with MLA_FLAG_DEFER_COMBINE; same params, same
+ * stream.  Errors as mla_decode. */
+mla_status mla_combine(const mla_decode_params* params, void* stream);
+
+/* Test hook: the 64 x 576 bf16 tile the KV loader stages for work item j
+ * of sequence b (query token t when sparse), written un-swizzled to
+ * dst [64][576] bf16: gathered rows, dequantised when FP8, zero rows past
+ * the sequence or for -1 indices. */
+mla_status mla_debug_gather(const mla_decode_params* params, int32_t b, int32_t t, int32_t j,
+                            void* dst, void* stream);
+
+const char* mla_status_string(mla_status s);
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H_ */

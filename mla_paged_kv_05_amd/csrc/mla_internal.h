@@ -1,0 +1,65 @@
+// Internal interface between the C ABI (mla_api.cpp) and the gfx950 kernels
+// (mla_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace mla {
+
+constexpr int kPage = 64;             // tokens per KV block
+constexpr int kDqk = 576;             // 512 latent + 64 RoPE dims
+constexpr int kDv = 512;              // V = K[:, :512]
+constexpr int kRowsPerWg = 128;       // query rows one workgroup owns
+constexpr int kWaves = 4;             // one wave per SIMD
+constexpr int kThreads = kWaves * 64;
+constexpr int kFp8TokenBytes = 656;
+constexpr int kMaxBatch = 16384;
+constexpr int kMaxRows = 65536;
+
+// Piece cost F of the split rule (in KV-block units).
+inline int sched_piece_cost(int rows) {
+  int m = rows < kRowsPerWg ? rows : kRowsPerWg;
+  int f = (m + 31) / 32;
+  return f < 1 ? 1 : f;
+}
+
+// Row groups of 128 rows a decode call is cut into.
+inline int row_groups(int rows) { return (rows + kRowsPerWg - 1) / kRowsPerWg; }
+
+// Partial results of one (split, row group): 128 rows x 512 fp32 in the
+// decode kernel's register order plus 128 fp32 LSEs.
+constexpr size_t kPartialOFloats = (size_t)kRowsPerWg * kDv;
+constexpr size_t kPartialLseFloats = kRowsPerWg;
+
+struct DecodeArgs {
+  const uint16_t* q;         // bf16 [batch][rows][576]
+  const uint8_t* kv;         // paged pool
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const int32_t* indices;    // sparse only
+  const int32_t* meta;       // [S][8]
+  const int32_t* num_splits; // [batch+1]
+  float* part_o;             // [max_partials][G][128*512] (register order)
+  float* part_lse;           // [max_partials][G][128]
+  void* out;                 // bf16 or e4m3 [batch][rows][512]
+  float* lse;                // [batch][rows]
+  float* out_scale;          // fused only
+  const uint16_t* norm_w;    // fused only
+  int64_t num_blocks;
+  int batch, s_q, h_q, rows, groups, max_blocks, topk, causal, num_slots;
+  float scale_log2;          // softmax_scale * log2(e)
+  float norm_eps, rope_base;
+};
+
+enum KvFormat { kKvBf16 = 0, kKvFp8V32 = 1 };
+
+hipError_t launch_sched(const int32_t* seqlens, int batch, int rows, int topk, int num_slots,
+                        int32_t* meta, int32_t* num_splits, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool fused,
+                         hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs& a, bool fused, hipStream_t stream);
+hipError_t launch_debug_gather(const DecodeArgs& a, int kv_format, bool sparse, int b, int t,
+                               int j, uint16_t* dst, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,1059 @@
+// gfx950 (CDNA4) kernels for paged MLA decoding.
+//
+// What is computed: for each query row (sequence b, token t, head h) the
+// softmax attention of a 576-dim query over the sequence's latent KV head
+// held in a paged cache of 64-token blocks, V being the first 512 dims of K;
+// outputs O and the log-sum-exp ("FlashMLA", AI Wiki, sections "What is
+// FlashMLA?" and "How is FlashMLA designed?"; Ampere-adaptation README,
+// section "Usage").  The work of a sequence may be split over several
+// workgroups along the KV length; the partial results are merged by their
+// LSEs in a second kernel.
+//
+// Design for MI355X (not a translation of any CUDA kernel):
+//  * One workgroup = 4 waves (one per SIMD) owning 128 query rows; wave w
+//    owns rows 32w..32w+31 for both contractions, so every per-row
+//    operation (mask, max, sum, rescale, epilogue) stays inside the pair of
+//    lanes (l, l+32) that hold the row.
+//  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: K (from LDS) is the A
+//    operand, Q^T lives in registers as the B operand (36 fragments).  The
+//    accumulator layout of S^T is directly the B operand layout P^T of the
+//    second product, so P never goes through LDS.
+//  * O^T = V^T . P^T: V^T fragments come from the same LDS tile as K via
+//    ds_read_b64_tr_b16 transposed reads (V = K[:, :512], no second load).
+//  * KV blocks are staged with LDS-DMA (buffer_load ... lds, 16 B per lane)
+//    into a double-buffered, XOR-swizzled [64][576] bf16 tile.  The buffer
+//    resource of a block covers only its valid tokens, so rows past the
+//    sequence length are written as zeros by the hardware and poisoned
+//    (NaN) tail slots are never read.
+//  * Lazy rescaling: the running max used for exponentiation only moves
+//    when a new block max exceeds it by more than 2^8, so the 256-register
+//    O accumulator is almost never rescaled ("skip scale", AI Wiki, section
+//    "The Ascend kernel deep-dive"); exact up to rounding.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <cmath>
+
+#include "mla_internal.h"
+
+namespace mla {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+typedef __attribute__((ext_vector_type(2))) short s16x2;
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int kRowBytes = kDqk * 2;             // 1152
+constexpr int kChunksPerRow = kDqk / 8;         // 72 chunks of 16 B
+constexpr int kTileBytes = kPage * kRowBytes;   // 73728
+constexpr int kTileChunks = kPage * kChunksPerRow;  // 4608
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleThreshold = 8.0f;       // log2 units
+constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer, dword3 for gfx9 family
+
+// Values every lane of the wave holds identically (sequence, block and
+// slot indices): move them to scalar registers so buffer descriptors, LDS
+// bases and loop bounds stay scalar.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// An opaque copy of a per-lane value: loader address arithmetic derived from
+// it is recomputed at each use instead of being hoisted out of the KV loop
+// (where 18+ hoisted offsets would only crowd the register file).
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// S^T = K Q^T step on v_mfma_f32_32x32x16_bf16 with the accumulator held in
+// VGPRs.  Written as inline asm because the builtin lets the compiler move
+// every MFMA accumulator to AGPRs, and the 256 AGPRs are exactly the O
+// accumulator of a 32-row wave tile; S then overflows and spills.  The asm is
+// not volatile, so the scheduler still hoists the LDS reads feeding it.
+__device__ __forceinline__ void mfma_s_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s_acc(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+// The hardware does not interlock a VALU read of an MFMA result; the compiler
+// inserts those wait states for builtins but cannot see into the asm above,
+// so S is passed through 24 explicit wait states before any VALU use (more
+// than the XDL-write -> VALU-read requirement of a 32x32 op).
+__device__ __forceinline__ void mfma_s_settle(f32x16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
+}
+
+__device__ __forceinline__ float wave_bcast_partner(float v) {
+  // value held by lane l ^ 32 (the other half of the same row)
+  return __shfl_xor(v, 32, 64);
+}
+
+// ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Split-KV scheduler (one workgroup).  Implements the split rule stated in
+// mla.h; every per-sequence quantity is a prefix sum, every slot finds its
+// first item by binary search, so there is no serial walk.
+// ---------------------------------------------------------------------------
+constexpr int kSchedThreads = 1024;
+
+__device__ int block_scan_exclusive(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < kSchedThreads / 64 ? wsum[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(s, o, 64);
+      if (lane >= o) s += y;
+    }
+    if (lane < kSchedThreads / 64) wsum[lane] = s;
+  }
+  __syncthreads();
+  int base = w > 0 ? wsum[w - 1] : 0;
+  *total = wsum[kSchedThreads / 64 - 1];
+  __syncthreads();
+  return base + x - v;
+}
+
+__global__ void __launch_bounds__(kSchedThreads)
+k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
+        int32_t* __restrict__ meta, int32_t* __restrict__ num_splits) {
+  __shared__ int32_t U[kMaxBatch + 1];   // cost prefix: start of sequence b on the line
+  __shared__ int32_t I[kMaxBatch + 1];   // item prefix
+  __shared__ int wsum[kSchedThreads / 64];
+  const int tid = threadIdx.x;
+  const int F = [&] {
+    int m = rows < kRowsPerWg ? rows : kRowsPerWg;
+    int f = (m + 31) / 32;
+    return f < 1 ? 1 : f;
+  }();
+  const int per = (B + kSchedThreads - 1) / kSchedThreads;
+  const int lo = tid * per, hi = min(B, lo + per);
+  auto nblk = [&](int b) -> int {
+    if (topk > 0) return (topk + kPage - 1) / kPage;
+    int L = seqlens[b];
+    return L > 0 ? (L + kPage - 1) / kPage : 0;
+  };
+  // pass 1: U and I
+  int cs = 0, is = 0;
+  for (int b = lo; b < hi; ++b) {
+    int n = nblk(b);
+    cs += F + n;
+    is += n > 0 ? n : 1;
+  }
+  int tot_c, tot_i;
+  int c0 = block_scan_exclusive(cs, wsum, &tot_c);
+  int i0 = block_scan_exclusive(is, wsum, &tot_i);
+  for (int b = lo; b < hi; ++b) {
+    int n = nblk(b);
+    U[b] = c0;
+    I[b] = i0;
+    c0 += F + n;
+    i0 += n > 0 ? n : 1;
+  }
+  if (tid == 0) {
+    U[B] = tot_c;
+    I[B] = tot_i;
+  }
+  __syncthreads();
+  const int T = tot_c;
+  int cap = (T + 1 + S - 1) / S;
+  if (cap < 2 * F) cap = 2 * F;
+  // pass 2: splits per sequence -> num_splits prefix
+  int ss = 0;
+  for (int b = lo; b < hi; ++b) {
+    int items = U[b + 1] - U[b] - F;
+    items = items > 0 ? items : 1;
+    int p0 = U[b] + F;
+    ss += (p0 + items - 1) / cap - p0 / cap + 1;
+  }
+  int tot_s;
+  int s0 = block_scan_exclusive(ss, wsum, &tot_s);
+  for (int b = lo; b < hi; ++b) {
+    num_splits[b] = s0;
+    int items = U[b + 1] - U[b] - F;
+    items = items > 0 ? items : 1;
+    int p0 = U[b] + F;
+    s0 += (p0 + items - 1) / cap - p0 / cap + 1;
+  }
+  if (tid == 0) num_splits[B] = tot_s;
+  // pass 3: each slot's first and last item
+  auto last_pos = [&](int b) {  // position of the last item of sequence b
+    int n = U[b + 1] - U[b] - F;
+    return U[b] + F + (n > 0 ? n : 1) - 1;
+  };
+  // first item at position >= x, as (b, j); b == B if none
+  auto first_at = [&](int x, int& b, int& j) {
+    int l = 0, h = B;  // find the first b with last_pos(b) >= x
+    while (l < h) {
+      int mid = (l + h) >> 1;
+      if (last_pos(mid) >= x) h = mid; else l = mid + 1;
+    }
+    b = l;
+    if (l < B) {
+      int p0 = U[l] + F;
+      j = x > p0 ? x - p0 : 0;
+    } else {
+      j = 0;
+    }
+  };
+  for (int s = tid; s < S; s += kSchedThreads) {
+    int32_t* ms = meta + 8 * s;
+    int ba, ja, bz, jz;
+    first_at(s * cap, ba, ja);
+    first_at((s + 1) * cap, bz, jz);
+    bool empty = (ba >= B) || (U[ba] + F + ja >= (s + 1) * cap);
+    if (empty) {
+      ms[0] = -1; ms[1] = 0; ms[2] = -1; ms[3] = 0; ms[4] = 0; ms[5] = 0; ms[6] = 0; ms[7] = 0;
+      continue;
+    }
+    // last item = the one before (bz, jz)
+    int bl, jl;
+    if (jz > 0) { bl = bz; jl = jz - 1; }
+    else {
+      bl = bz - 1;
+      int n = U[bl + 1] - U[bl] - F;
+      jl = (n > 0 ? n : 1) - 1;
+    }
+    ms[0] = ba; ms[1] = ja; ms[2] = bl; ms[3] = jl + 1;
+    ms[4] = s - (U[ba] + F) / cap;
+    ms[5] = (I[bl] + jl + 1) - (I[ba] + ja);
+    ms[6] = 0; ms[7] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KV staging.  The unit of work is a half block of 32 tokens.  A bf16 half
+// tile in LDS is [32][576] with token r's 16-byte chunk c at
+// r*1152 + ((c ^ (r & 7)) << 4): the 32 rows a wave reads at one column fall
+// on distinct LDS banks.  Half tiles rotate through a ring of 3 slots, so two
+// halves (72 KB) are in flight while the third is computed on.
+// ---------------------------------------------------------------------------
+constexpr int kHalfRows = 32;
+constexpr int kHalfBytes = kHalfRows * kRowBytes;          // 36864
+constexpr int kHalfChunks = kHalfRows * kChunksPerRow;     // 2304 = 36 wave-loads
+constexpr int kRing = 3;
+
+// All-zero source for rows that hold no token (masked sparse entries).
+__device__ __attribute__((aligned(16))) const uint8_t g_zero_row[kRowBytes] = {0};
+
+// Dense bf16: half `h` of pool block `phys` whose first `valid` tokens are
+// real.  The buffer resource covers exactly those tokens, so the hardware
+// writes zeros for the others and never reads past the sequence.  Each wave
+// issues 9 LDS-DMA loads; load i fills slot bytes [i*1024, i*1024+1024).
+__device__ __forceinline__ void load_half_bf16_dense(uint8_t* slot, const uint8_t* kv, int64_t phys,
+                                                     int valid, int h, int wave, int lane) {
+  lane = opaque(lane);
+  const uint8_t* page = kv + phys * (int64_t)kTileBytes;
+  __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, valid * kRowBytes, kBufferFlags);
+#pragma unroll
+  for (int ii = 0; ii < kHalfChunks / 64 / kWaves; ++ii) {
+    const int i = ii * kWaves + wave;
+    const int pos_all = i * 64 + lane;
+    const int r = pos_all / kChunksPerRow;
+    const int pos = pos_all - r * kChunksPerRow;
+    const int c = pos ^ (r & 7);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(slot + i * 1024), 16,
+                                             (h * kHalfRows + r) * kRowBytes + c * 16, 0, 0, 0);
+  }
+}
+
+// Sparse bf16: row r is flat pool token ids[r] when r < nvalid and
+// ids[r] >= 0, else zeros.
+__device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8_t* kv,
+                                                      const int32_t* ids, int nvalid, int wave,
+                                                      int lane) {
+  lane = opaque(lane);
+#pragma unroll
+  for (int ii = 0; ii < kHalfChunks / 64 / kWaves; ++ii) {
+    const int i = ii * kWaves + wave;
+    const int pos_all = i * 64 + lane;
+    const int r = pos_all / kChunksPerRow;
+    const int pos = pos_all - r * kChunksPerRow;
+    const int c = pos ^ (r & 7);
+    const int id = r < nvalid ? ids[r] : -1;
+    const uint8_t* g = id >= 0 ? kv + (int64_t)id * kRowBytes + c * 16 : g_zero_row + c * 16;
+    __builtin_amdgcn_global_load_lds((const void*)g, LDS_PTR(slot + i * 1024), 16, 0, 0);
+  }
+}
+
+// FP8 V3.2 records of one half (32 x 656 B = 1312 chunks) are staged raw by
+// LDS-DMA into a 24 KB slot (24 loads per half, 6 per wave; the tail of the
+// slot is padding), then dequantised LDS -> LDS into a bf16 half tile.
+constexpr int kFp8ChunksPerTok = kFp8TokenBytes / 16;        // 41
+constexpr int kRawHalfChunks = kHalfRows * kFp8ChunksPerTok;  // 1312
+constexpr int kRawSlotBytes = 24 * 1024;
+constexpr int kRawLoadsPerWave = kRawSlotBytes / 1024 / kWaves;  // 6
+
+__device__ __forceinline__ void load_half_fp8_dense(uint8_t* raw, const uint8_t* kv, int64_t phys,
+                                                    int valid, int h, int wave, int lane) {
+  lane = opaque(lane);
+  const uint8_t* page = kv + phys * (int64_t)(kPage * kFp8TokenBytes);
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)page, (short)0, valid * kFp8TokenBytes, kBufferFlags);
+#pragma unroll
+  for (int ii = 0; ii < kRawLoadsPerWave; ++ii) {
+    const int i = ii * kWaves + wave;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(raw + i * 1024), 16,
+                                             h * kHalfRows * kFp8TokenBytes + (i * 64 + lane) * 16,
+                                             0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t* kv,
+                                                     const int32_t* ids, int nvalid, int wave,
+                                                     int lane) {
+  lane = opaque(lane);
+#pragma unroll
+  for (int ii = 0; ii < kRawLoadsPerWave; ++ii) {
+    const int i = ii * kWaves + wave;
+    const int pos_all = i * 64 + lane;
+    const int r = pos_all / kFp8ChunksPerTok;
+    const int c = pos_all - r * kFp8ChunksPerTok;
+    const int id = (pos_all < kRawHalfChunks && r < nvalid) ? ids[r] : -1;
+    const uint8_t* g =
+        id >= 0 ? kv + (int64_t)id * kFp8TokenBytes + c * 16 : g_zero_row + (pos_all & 63) * 16;
+    __builtin_amdgcn_global_load_lds((const void*)g, LDS_PTR(raw + i * 1024), 16, 0, 0);
+  }
+}
+
+// Dequantise 32 raw records into the bf16 half tile: dims < 512 are
+// e4m3 * fp32 tile scale computed in fp32 and rounded once to bf16 (RNE);
+// dims 512..575 are copied.  An all-zero record gives a zero row.
+__device__ __forceinline__ void dequant_half(uint8_t* tile, const uint8_t* raw, int tid) {
+#pragma unroll
+  for (int kk = 0; kk < kHalfChunks / kThreads; ++kk) {
+    const int k = kk * kThreads + tid;
+    const int r = k / kChunksPerRow;
+    const int c = k - r * kChunksPerRow;
+    const uint8_t* rec = raw + r * kFp8TokenBytes;
+    uint32_t w[4];
+    if (c < 64) {
+      const uint2 code = *reinterpret_cast<const uint2*>(rec + c * 8);
+      const float sc = *reinterpret_cast<const float*>(rec + 512 + (c >> 4) * 4);
+      const uint32_t cw[2] = {code.x, code.y};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        typedef __attribute__((ext_vector_type(2))) float f2;
+        f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], false);
+        f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], true);
+        __bf16 b0 = (__bf16)(lo[0] * sc), b1 = (__bf16)(lo[1] * sc);
+        __bf16 b2 = (__bf16)(hi[0] * sc), b3 = (__bf16)(hi[1] * sc);
+        w[2 * hh] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        w[2 * hh + 1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+      }
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(rec + 528 + (c - 64) * 16);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    }
+    *reinterpret_cast<uint4*>(tile + r * kRowBytes + ((c ^ (r & 7)) << 4)) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// The 32 sparse ids of half `h` of work item j of (sequence b, query token
+// t) -> LDS (one LDS-DMA dword per lane; lanes past topk read 0 and are
+// excluded by position, never by value).
+__device__ __forceinline__ void fetch_ids_dma(int32_t* ids_lds, const int32_t* indices,
+                                              int64_t row_off, int topk, int j, int h) {
+  const int first = j * kPage + h * kHalfRows;
+  const int32_t* base = indices + row_off + first;
+  const int n = max(0, min(kHalfRows, topk - first));
+  __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n * 4, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(ids_lds), 4, (threadIdx.x & 63) * 4, 0, 0,
+                                           0);
+}
+
+// ---------------------------------------------------------------------------
+// Fused prologue / epilogue helpers.  RoPE angles are formed and reduced in
+// fp64 (positions reach 10^4 radians) before an fp32 sincos.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rope_cs(double pos, int pair, float base, float sign, float& c,
+                                        float& s) {
+  // theta = pos * base^(-2*pair/64)
+  double th = sign * pos * exp2(-(double)(2 * pair) / 64.0 * log2((double)base));
+  double red = th - 6.283185307179586 * rint(th / 6.283185307179586);
+  sincosf((float)red, &s, &c);
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel
+//
+// Query fragments: dims 0..383 (k-steps 0..23) stay in VGPRs, dims 384..575
+// (k-steps 24..35) in a per-wave LDS region [32 rows][24 chunks] swizzled
+// like the KV tile.  This keeps the wave's register file at
+// 96 (Q) + 256 (O, AGPRs) + working set, with no spills.
+// ---------------------------------------------------------------------------
+constexpr int kQRegSteps = 24;
+constexpr int kQLdsSteps = 36 - kQRegSteps;               // 12
+constexpr int kQLdsRowBytes = kQLdsSteps * 2 * 16;        // 384
+constexpr int kQLdsWaveBytes = 32 * kQLdsRowBytes;        // 12288
+constexpr int kIdsSlots = 6;
+
+template <int KVF, bool SPARSE>
+struct DecodeLayout {
+  static constexpr int kTileOff = 0;                                   // bf16 half tiles
+  static constexpr int kTiles = KVF == kKvBf16 ? kRing : 1;
+  static constexpr int kRawOff = kTiles * kHalfBytes;                  // fp8 raw slots
+  static constexpr int kQOff = kRawOff + (KVF == kKvBf16 ? 0 : kRing * kRawSlotBytes);
+  static constexpr int kIdsOff = kQOff + kWaves * kQLdsWaveBytes;
+  static constexpr int kSmem = kIdsOff + (SPARSE ? kIdsSlots * 256 : 0);
+  // per-step VMEM instructions issued by every wave (loads + id fetch)
+  static constexpr int kVmPerStep =
+      (KVF == kKvBf16 ? kHalfChunks / 64 / kWaves : kRawLoadsPerWave) + (SPARSE ? 1 : 0);
+};
+
+__device__ __forceinline__ int seq_items(const DecodeArgs& a, int b) {
+  if (a.topk > 0) return (a.topk + kPage - 1) / kPage;
+  int L = uni(a.seqlens[b]);
+  return L > 0 ? (L + kPage - 1) / kPage : 0;
+}
+
+// s_waitcnt with only a vmcnt limit (expcnt and lgkmcnt left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int KVF, bool SPARSE, bool FUSED>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_decode(DecodeArgs a) {
+  using Lay = DecodeLayout<KVF, SPARSE>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Lay::kSmem];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+  const int half = lane >> 5, r32 = lane & 31;
+
+  // blockIdx -> (slot, row group); the G row groups of one slot are
+  // dispatched back to back onto the same XCD (ids s, s+8, ...) so their
+  // shared KV reads meet in that XCD's L2.
+  int slot, g;
+  {
+    const int G = a.groups, wg = blockIdx.x;
+    if (G == 1) { slot = wg; g = 0; }
+    else {
+      const int xcd = wg & 7, k = wg >> 3;
+      g = k % G;
+      slot = (k / G) * 8 + xcd;
+    }
+  }
+  const int32_t* ms = a.meta + 8 * slot;
+  const int b0 = uni(ms[0]);
+  if (b0 < 0) return;
+  const int j0 = uni(ms[1]), b1 = uni(ms[2]), j1 = uni(ms[3]), nitems = uni(ms[5]);
+  int split_k = uni(ms[4]);
+  const int nsteps = 2 * nitems;
+
+  // this lane's query row within the sequence
+  const int row = g * kRowsPerWg + wave * 32 + r32;
+  const bool row_ok = row < a.rows;
+  const int tok = row_ok ? row / a.h_q : 0;
+  const int gtok = (g * kRowsPerWg) / a.h_q;   // sparse: the row group's query token
+
+  auto item_end = [&](int b) { return b == b1 ? j1 : max(seq_items(a, b), 1); };
+  // step -> (sequence, item, half) by walking forward from a known step
+  auto advance = [&](int& b, int& j, int& h) {
+    if (h == 0) { h = 1; return; }
+    h = 0;
+    ++j;
+    if (j >= item_end(b)) { ++b; j = 0; }
+    b = uni(b); j = uni(j);
+  };
+  auto ids_slot = [&](int step) {
+    return reinterpret_cast<int32_t*>(smem + Lay::kIdsOff) + (step % kIdsSlots) * 64;
+  };
+  auto fetch_ids = [&](int b, int j, int h, int step) {
+    if constexpr (SPARSE)
+      fetch_ids_dma(ids_slot(step), a.indices, ((int64_t)b * a.s_q + gtok) * a.topk, a.topk, j, h);
+  };
+  // stage step `step` = (b, j, h) into its ring slot
+  auto issue_load = [&](int b, int j, int h, int step) {
+    const int rs = step % kRing;
+    if constexpr (!SPARSE) {
+      const int L = uni(a.seqlens[b]);
+      const bool any = j * kPage < L;
+      const int64_t phys = any ? uni(a.block_table[(int64_t)b * a.max_blocks + j]) : 0;
+      const int valid = any ? min(kPage, L - j * kPage) : 0;
+      if constexpr (KVF == kKvBf16)
+        load_half_bf16_dense(smem + Lay::kTileOff + rs * kHalfBytes, a.kv, phys, valid, h, wave, lane);
+      else
+        load_half_fp8_dense(smem + Lay::kRawOff + rs * kRawSlotBytes, a.kv, phys, valid, h, wave, lane);
+    } else {
+      const int nvalid = min(kHalfRows, a.topk - j * kPage - h * kHalfRows);
+      if constexpr (KVF == kKvBf16)
+        load_half_bf16_sparse(smem + Lay::kTileOff + rs * kHalfBytes, a.kv, ids_slot(step), nvalid,
+                              wave, lane);
+      else
+        load_half_fp8_sparse(smem + Lay::kRawOff + rs * kRawSlotBytes, a.kv, ids_slot(step), nvalid,
+                             wave, lane);
+    }
+  };
+
+  // ---- prologue: ids of steps 0..3, loads of steps 0 and 1
+  int lb = b0, lj = j0, lh = 0;   // next step to load
+  int fb = b0, fj = j0, fh = 0;   // next step whose ids to fetch
+  if constexpr (SPARSE) {
+    for (int s = 0; s < min(4, nsteps); ++s) {
+      fetch_ids(fb, fj, fh, s);
+      advance(fb, fj, fh);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  for (int s = 0; s < min(2, nsteps); ++s) {
+    issue_load(lb, lj, lh, s);
+    advance(lb, lj, lh);
+  }
+
+  uint8_t* qlds = smem + Lay::kQOff + wave * kQLdsWaveBytes;
+  const int x = lane & 7;
+  bf16x8 qf[kQRegSteps];
+  f32x16 o[16];
+
+  int cb = b0, cj = j0, step = 0;
+  while (step < nsteps) {
+    // ======== one piece: sequence cb, items cj .. piece_end-1
+    const int Lb = uni(a.seqlens[cb]);
+    const int piece_end = item_end(cb);
+    const int piece_first_step = step;
+    float m_used = -INFINITY, lsum = 0.f;
+    int vis_end = 0;  // dense: keys < vis_end are visible to this row
+    if constexpr (!SPARSE) {
+      int ve = Lb;
+      if (a.causal) ve = min(Lb, Lb - a.s_q + tok + 1);
+      vis_end = row_ok ? max(ve, 0) : 0;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) o[mt] = f32x16{};
+
+    for (; cj < piece_end; ++cj) {
+#pragma unroll 1
+      for (int h = 0; h < 2; ++h, ++step) {
+        // ======== one step: 32 keys
+        // This step's loads were issued two steps ago; the previous step then
+        // issued the loads of step+1 (if any) and, sparse, the ids of step+3
+        // (if any).  Wait for everything older than those.  A piece's first
+        // step drains everything (the previous piece's stores are in flight).
+        constexpr int kLoadsPerStep = Lay::kVmPerStep - (SPARSE ? 1 : 0);
+        if (step == piece_first_step || step + 1 >= nsteps) wait_vmcnt<0>();
+        else if (SPARSE && step + 3 >= nsteps) wait_vmcnt<kLoadsPerStep>();
+        else wait_vmcnt<Lay::kVmPerStep>();
+        __syncthreads();  // every wave's loads of this step landed; slot (step+2)%3 is free
+        if (step == piece_first_step) {
+          // query fragments of the new piece (issued before the next loads so
+          // that waiting for them does not wait for those)
+          const uint16_t* qrow = a.q + ((int64_t)cb * a.rows + (row_ok ? row : 0)) * kDqk;
+          bf16x8 qraw[36];
+#pragma unroll
+          for (int ks = 0; ks < 36; ++ks)
+            qraw[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
+          if (step + 2 < nsteps) {
+            issue_load(lb, lj, lh, step + 2);
+            advance(lb, lj, lh);
+          }
+          if constexpr (SPARSE) {
+            if (step + 4 < nsteps) {
+              fetch_ids(fb, fj, fh, step + 4);
+              advance(fb, fj, fh);
+            }
+          }
+          if constexpr (FUSED) {
+            // RMSNorm over the row's 576 dims (lanes l and l^32 hold it), then
+            // RoPE on dims 512..575 at position len - s_q + t.
+            float ss = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 36; ++ks)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) { float v = (float)qraw[ks][e]; ss += v * v; }
+            ss += wave_bcast_partner(ss);
+            const float inv = 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
+            const double pos = (double)Lb - (double)a.s_q + (double)tok;
+#pragma unroll
+            for (int ks = 0; ks < 36; ++ks) {
+              const int c = 2 * ks + half;
+              const bf16x8 wv = *reinterpret_cast<const bf16x8*>(a.norm_w + c * 8);
+              float y[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) y[e] = (float)qraw[ks][e] * (float)wv[e] * inv;
+              if (ks >= 32) {
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                  float cs, sn;
+                  rope_cs(pos, (c * 8 - 512) / 2 + pp, a.rope_base, 1.0f, cs, sn);
+                  const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
+                  y[2 * pp] = x0 * cs - x1 * sn;
+                  y[2 * pp + 1] = x0 * sn + x1 * cs;
+                }
+              }
+#pragma unroll
+              for (int e = 0; e < 8; ++e) qraw[ks][e] = (__bf16)y[e];
+            }
+          }
+#pragma unroll
+          for (int ks = 0; ks < 36; ++ks) {
+            const bf16x8 v = row_ok ? qraw[ks] : bf16x8{};
+            if (ks < kQRegSteps) {
+              qf[ks] = v;
+            } else {
+              const int cq = 2 * (ks - kQRegSteps) + half;
+              *reinterpret_cast<bf16x8*>(qlds + r32 * kQLdsRowBytes + ((cq ^ x) << 4)) = v;
+            }
+          }
+        } else {
+          if (step + 2 < nsteps) {
+            issue_load(lb, lj, lh, step + 2);
+            advance(lb, lj, lh);
+          }
+          if constexpr (SPARSE) {
+            if (step + 4 < nsteps) {
+              fetch_ids(fb, fj, fh, step + 4);
+              advance(fb, fj, fh);
+            }
+          }
+        }
+
+        const uint8_t* tile;
+        if constexpr (KVF == kKvBf16) {
+          tile = smem + Lay::kTileOff + (step % kRing) * kHalfBytes;
+        } else {
+          tile = smem + Lay::kTileOff;
+          dequant_half(smem + Lay::kTileOff, smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
+          __syncthreads();
+        }
+        const int key0 = cj * kPage + h * kHalfRows;  // first key of this step
+        const bool any_key = SPARSE ? (key0 < a.topk) : (key0 < Lb);
+        if (any_key) {
+          // ---- lane-constant LDS offsets for this step (opaque bases; the
+          // rest are DS immediates).  K rows = keys (A operand of S^T = K Q^T),
+          // chunk 2*ks + half; V^T via transposed reads: lane supplies key
+          // 16*kk + 4*half + (lane&15)/4 (+8 for k-slots 4..7) and dims
+          // 32*mt + 16*((lane>>4)&1) + 4*(lane&3).
+          const int tb = (int)(tile - smem);
+          int koff[4], qoff[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            koff[e] = opaque(tb + r32 * kRowBytes + ((((2 * e) | half) ^ x) << 4));
+            qoff[e] = opaque((int)(qlds - smem) + r32 * kQLdsRowBytes + ((((2 * e) | half) ^ x) << 4));
+          }
+          const int kr = 4 * half + ((lane & 15) >> 2);
+          const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+          const int vlo = tb + ((cl ^ ((lane >> 2) & 3)) << 4) + 8 * (lane & 1) + kr * kRowBytes;
+          const int voff0 = opaque(vlo + ((0 ^ half) << 6)), voff1 = opaque(vlo + ((1 ^ half) << 6));
+
+          // ---- S^T for these 32 keys (rows = lanes), VGPR accumulator
+          f32x16 sc;
+#pragma unroll
+          for (int ks = 0; ks < 36; ++ks) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(smem + koff[ks & 3] + (ks >> 2) * 128);
+            bf16x8 qb;
+            if (ks < kQRegSteps) qb = qf[ks];
+            else qb = *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegSteps) & 3] +
+                                                       ((ks - kQRegSteps) >> 2) * 128);
+            if (ks == 0) mfma_s_first(sc, ka, qb);
+            else mfma_s_acc(sc, ka, qb);
+          }
+          mfma_s_settle(sc);
+
+          // ---- mask + online softmax (log2 domain); register i holds key
+          // key0 + 8*(i/4) + 4*half + i%4
+          float mx = -INFINITY;
+          if constexpr (SPARSE) {
+            const int32_t* ids = ids_slot(step);
+            const int nvalid = row_ok ? min(kHalfRows, a.topk - key0) : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int k = 8 * (i >> 2) + 4 * half + (i & 3);
+              float v = sc[i] * a.scale_log2;
+              v = (k < nvalid && ids[k] >= 0) ? v : -INFINITY;
+              sc[i] = v;
+              mx = fmaxf(mx, v);
+            }
+          } else {
+            const int lim = vis_end - key0;  // keys < lim visible in this step
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int k = 8 * (i >> 2) + 4 * half + (i & 3);
+              float v = sc[i] * a.scale_log2;
+              v = k < lim ? v : -INFINITY;
+              sc[i] = v;
+              mx = fmaxf(mx, v);
+            }
+          }
+          mx = fmaxf(mx, wave_bcast_partner(mx));
+          const bool need = mx > m_used + kRescaleThreshold;
+          if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+            const float alpha = need ? exp2f(m_used - mx) : 1.0f;  // exp2(-inf) = 0
+            if (need) m_used = mx;
+            // Scale the AGPR-resident O in place, one register at a time inside
+            // inline asm: written as plain C++ the compiler copies the whole
+            // 256-register accumulator through VGPRs for this rare path and
+            // spills the hot loop's working set to make room.
+#pragma unroll
+            for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                float t;
+                asm volatile(
+                    "v_accvgpr_read_b32 %1, %0\n\t"
+                    "s_nop 1\n\t"
+                    "v_mul_f32 %1, %1, %2\n\t"
+                    "v_accvgpr_write_b32 %0, %1"
+                    : "+a"(o[mt][i]), "=&v"(t)
+                    : "v"(alpha));
+              }
+            // accvgpr writes -> next MFMA reading them as accumulator
+            asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+            lsum *= alpha;
+          }
+          const float mref = m_used == -INFINITY ? 0.f : m_used;
+          bf16x8 pf[2];
+          float ps = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(sc[i] - mref);
+            ps += pv;
+            pf[i >> 3][i & 7] = (__bf16)pv;
+          }
+          lsum += ps;
+
+          // ---- O^T += V^T P^T over these 32 keys (2 k-steps x 16 d-tiles)
+#pragma unroll
+          for (int kq = 0; kq < 2; ++kq) {
+#pragma unroll
+            for (int mt = 0; mt < 16; ++mt) {
+              const uint8_t* p = smem + ((mt & 1) ? voff1 : voff0) + kq * 16 * kRowBytes + (mt >> 1) * 128;
+              const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) s16x4*)(p));
+              const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) s16x4*)(p + 8 * kRowBytes));
+              const s16x8 v8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+              o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pf[kq],
+                                                              o[mt], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+
+    // ======== finalize the piece: O / l and LSE; direct output or partial
+    {
+      const float lt = lsum + wave_bcast_partner(lsum);
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      const float lse2 = lt > 0.f ? m_used + __builtin_amdgcn_logf(lt) : -INFINITY;
+      const int nsplit = uni(a.num_splits[cb + 1] - a.num_splits[cb]);
+      if (nsplit == 1) {
+        const int64_t orow = (int64_t)cb * a.rows + row;
+        if constexpr (!FUSED) {
+          if (row_ok) {
+            uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + orow * kDv;
+#pragma unroll
+            for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+              for (int qd = 0; qd < 4; ++qd) {
+                const int d = 32 * mt + 8 * qd + 4 * half;
+                const __bf16 v0 = (__bf16)(o[mt][4 * qd] * inv), v1 = (__bf16)(o[mt][4 * qd + 1] * inv);
+                const __bf16 v2 = (__bf16)(o[mt][4 * qd + 2] * inv), v3 = (__bf16)(o[mt][4 * qd + 3] * inv);
+                uint2 pk;
+                pk.x = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+                pk.y = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+                *reinterpret_cast<uint2*>(op + d) = pk;
+              }
+            if (half == 0) a.lse[orow] = lse2 * kLn2;
+          }
+        } else {
+          // conjugate RoPE on dims 448..511, amax over the row, e4m3 cast
+          const double pos = (double)Lb - (double)a.s_q + (double)tok;
+#pragma unroll
+          for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[mt][i] *= inv;
+#pragma unroll
+          for (int mt = 14; mt < 16; ++mt)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+              for (int pp = 0; pp < 2; ++pp) {
+                const int d = 32 * mt + 8 * qd + 4 * half + 2 * pp;
+                float cs, sn;
+                rope_cs(pos, (d - 448) / 2, a.rope_base, -1.0f, cs, sn);
+                const float x0 = o[mt][4 * qd + 2 * pp], x1 = o[mt][4 * qd + 2 * pp + 1];
+                o[mt][4 * qd + 2 * pp] = x0 * cs - x1 * sn;
+                o[mt][4 * qd + 2 * pp + 1] = x0 * sn + x1 * cs;
+              }
+          float amax = 0.f;
+#pragma unroll
+          for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[mt][i]));
+          amax = fmaxf(amax, wave_bcast_partner(amax));
+          const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+          const float rs = amax > 0.f ? 448.0f / amax : 1.0f;
+          if (row_ok) {
+            uint8_t* op = reinterpret_cast<uint8_t*>(a.out) + orow * kDv;
+#pragma unroll
+            for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+              for (int qd = 0; qd < 4; ++qd) {
+                const int d = 32 * mt + 8 * qd + 4 * half;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(o[mt][4 * qd + e] * rs, -448.f), 448.f);
+                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+                pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], pk, true);
+                *reinterpret_cast<int*>(op + d) = pk;
+              }
+            if (half == 0) {
+              a.lse[orow] = lse2 * kLn2;
+              a.out_scale[orow] = sc;
+            }
+          }
+        }
+      } else {
+        // partial of split `split_k` of sequence cb, row group g, stored in
+        // register order: [wave][d-tile][quad][lane][4]
+        const int64_t pidx = (int64_t)uni(a.num_splits[cb] + split_k) * a.groups + g;
+        float* po = a.part_o + pidx * kPartialOFloats + (size_t)wave * (16 * 4 * 64 * 4);
+#pragma unroll
+        for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 v = {o[mt][4 * qd] * inv, o[mt][4 * qd + 1] * inv, o[mt][4 * qd + 2] * inv,
+                             o[mt][4 * qd + 3] * inv};
+            *reinterpret_cast<f32x4*>(po + ((mt * 4 + qd) * 64 + lane) * 4) = v;
+          }
+        if (half == 0) a.part_lse[pidx * kPartialLseFloats + wave * 32 + r32] = lse2 * kLn2;
+      }
+    }
+    // next piece: first item of the following sequence
+    cb = uni(cb + 1);
+    cj = 0;
+    split_k = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LSE combine: one workgroup per (sequence, row group, 32-row wave tile).
+// Thread (sub, lane): lane's row, 16 of the 64 (d-tile, quad) float4s.
+// ---------------------------------------------------------------------------
+template <bool FUSED>
+__global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
+  const int wt = blockIdx.x & 3;
+  const int g = (blockIdx.x >> 2) % a.groups;
+  const int b = (blockIdx.x >> 2) / a.groups;
+  const int s0 = a.num_splits[b], ns = a.num_splits[b + 1] - s0;
+  if (ns <= 1) return;
+  const int tid = threadIdx.x, lane = tid & 63, sub = tid >> 6;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int row = g * kRowsPerWg + wt * 32 + r32;
+  const bool row_ok = row < a.rows;
+  __shared__ float amax_s[4][64];
+
+  float m = -INFINITY;
+  for (int s = 0; s < ns; ++s) {
+    const float l = a.part_lse[((int64_t)(s0 + s) * a.groups + g) * kPartialLseFloats + wt * 32 + r32];
+    m = fmaxf(m, l);
+  }
+  float tot = 0.f;
+  if (m != -INFINITY)
+    for (int s = 0; s < ns; ++s) {
+      const float l = a.part_lse[((int64_t)(s0 + s) * a.groups + g) * kPartialLseFloats + wt * 32 + r32];
+      tot += l == -INFINITY ? 0.f : expf(l - m);
+    }
+  const float lse = m == -INFINITY ? -INFINITY : m + logf(tot);
+  f32x4 acc[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc[k] = f32x4{};
+  if (m != -INFINITY) {
+    for (int s = 0; s < ns; ++s) {
+      const int64_t pidx = (int64_t)(s0 + s) * a.groups + g;
+      const float l = a.part_lse[pidx * kPartialLseFloats + wt * 32 + r32];
+      if (l == -INFINITY) continue;  // lane-divergent skip is fine: loads below are per lane
+      const float w = expf(l - lse);
+      const float* po = a.part_o + pidx * kPartialOFloats + (size_t)wt * (16 * 4 * 64 * 4);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int e = sub * 16 + k;  // (mt, qd) = (e / 4, e % 4)
+        f32x4 v = *reinterpret_cast<const f32x4*>(po + (e * 64 + lane) * 4);
+        acc[k] += w * v;
+      }
+    }
+  }
+  const int64_t orow = (int64_t)b * a.rows + row;
+  if constexpr (!FUSED) {
+    if (row_ok) {
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + orow * kDv;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int e = sub * 16 + k, mt = e >> 2, qd = e & 3;
+        const int d = 32 * mt + 8 * qd + 4 * half;
+        uint2 pk;
+        pk.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[k][0]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[k][1]) << 16);
+        pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[k][2]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[k][3]) << 16);
+        *reinterpret_cast<uint2*>(op + d) = pk;
+      }
+      if (half == 0 && sub == 0) a.lse[orow] = lse;
+    }
+  } else {
+    // conjugate RoPE on dims 448..511 (sub 3 holds d-tiles 12..15)
+    const int Lb = a.seqlens[b];
+    const int tok = row_ok ? row / a.h_q : 0;
+    const double pos = (double)Lb - (double)a.s_q + (double)tok;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int e = sub * 16 + k, mt = e >> 2, qd = e & 3;
+      if (mt < 14) continue;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int d = 32 * mt + 8 * qd + 4 * half + 2 * pp;
+        float cs, sn;
+        rope_cs(pos, (d - 448) / 2, a.rope_base, -1.0f, cs, sn);
+        const float x0 = acc[k][2 * pp], x1 = acc[k][2 * pp + 1];
+        acc[k][2 * pp] = x0 * cs - x1 * sn;
+        acc[k][2 * pp + 1] = x0 * sn + x1 * cs;
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(acc[k][e]));
+    amax = fmaxf(amax, wave_bcast_partner(amax));
+    amax_s[sub][lane] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(amax_s[0][lane], amax_s[1][lane]), fmaxf(amax_s[2][lane], amax_s[3][lane]));
+    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+    const float rs = amax > 0.f ? 448.0f / amax : 1.0f;
+    if (row_ok) {
+      uint8_t* op = reinterpret_cast<uint8_t*>(a.out) + orow * kDv;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int e = sub * 16 + k, mt = e >> 2, qd = e & 3;
+        const int d = 32 * mt + 8 * qd + 4 * half;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = fminf(fmaxf(acc[k][i] * rs, -448.f), 448.f);
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], pk, true);
+        *reinterpret_cast<int*>(op + d) = pk;
+      }
+      if (half == 0 && sub == 0) {
+        a.lse[orow] = lse;
+        a.out_scale[orow] = sc;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Debug gather: stage both halves of one work item with the decode kernel's
+// loaders (and dequantiser), copy them out un-swizzled as [64][576] bf16.
+// ---------------------------------------------------------------------------
+template <int KVF, bool SPARSE>
+__global__ void __launch_bounds__(kThreads) k_debug_gather(DecodeArgs a, int b, int t, int j,
+                                                          uint16_t* dst) {
+  constexpr int kSmem = kHalfBytes + kRawSlotBytes + 256;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
+  uint8_t* tile = smem;
+  uint8_t* raw = smem + kHalfBytes;
+  int32_t* ids = reinterpret_cast<int32_t*>(smem + kHalfBytes + kRawSlotBytes);
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+  for (int h = 0; h < 2; ++h) {
+    __syncthreads();
+    if constexpr (SPARSE) {
+      fetch_ids_dma(ids, a.indices, ((int64_t)b * a.s_q + t) * a.topk, a.topk, j, h);
+      __builtin_amdgcn_s_waitcnt(0);
+      const int nvalid = min(kHalfRows, a.topk - j * kPage - h * kHalfRows);
+      if constexpr (KVF == kKvBf16) load_half_bf16_sparse(tile, a.kv, ids, nvalid, wave, lane);
+      else load_half_fp8_sparse(raw, a.kv, ids, nvalid, wave, lane);
+    } else {
+      const int L = a.seqlens[b];
+      const bool any = j * kPage < L;
+      const int64_t phys = any ? a.block_table[(int64_t)b * a.max_blocks + j] : 0;
+      const int valid = any ? min(kPage, L - j * kPage) : 0;
+      if constexpr (KVF == kKvBf16) load_half_bf16_dense(tile, a.kv, phys, valid, h, wave, lane);
+      else load_half_fp8_dense(raw, a.kv, phys, valid, h, wave, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if constexpr (KVF != kKvBf16) {
+      dequant_half(tile, raw, tid);
+      __syncthreads();
+    }
+    for (int k = tid; k < kHalfChunks; k += kThreads) {
+      const int r = k / kChunksPerRow, c = k - r * kChunksPerRow;
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + r * kRowBytes + ((c ^ (r & 7)) << 4));
+      *reinterpret_cast<uint4*>(dst + (h * kHalfRows + r) * kDqk + c * 8) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_sched(const int32_t* seqlens, int batch, int rows, int topk, int num_slots,
+                        int32_t* meta, int32_t* num_splits, hipStream_t stream) {
+  hipLaunchKernelGGL(k_sched, dim3(1), dim3(kSchedThreads), 0, stream, seqlens, batch, rows, topk,
+                     num_slots, meta, num_splits);
+  return hipGetLastError();
+}
+
+template <int KVF, bool SPARSE, bool FUSED>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  const int grid = a.num_slots * a.groups;
+  hipLaunchKernelGGL((k_decode<KVF, SPARSE, FUSED>), dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool fused,
+                         hipStream_t stream) {
+  if (kv_format == kKvBf16) {
+    if (!sparse) return fused ? launch_decode_t<kKvBf16, false, true>(a, stream)
+                              : launch_decode_t<kKvBf16, false, false>(a, stream);
+    return fused ? launch_decode_t<kKvBf16, true, true>(a, stream)
+                 : launch_decode_t<kKvBf16, true, false>(a, stream);
+  }
+  if (!sparse) return fused ? launch_decode_t<kKvFp8V32, false, true>(a, stream)
+                            : launch_decode_t<kKvFp8V32, false, false>(a, stream);
+  return fused ? launch_decode_t<kKvFp8V32, true, true>(a, stream)
+               : launch_decode_t<kKvFp8V32, true, false>(a, stream);
+}
+
+hipError_t launch_combine(const DecodeArgs& a, bool fused, hipStream_t stream) {
+  const int grid = a.batch * a.groups * 4;
+  if (grid == 0) return hipSuccess;
+  if (fused) hipLaunchKernelGGL(k_combine<true>, dim3(grid), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(k_combine<false>, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_gather(const DecodeArgs& a, int kv_format, bool sparse, int b, int t, int j,
+                               uint16_t* dst, hipStream_t stream) {
+  if (kv_format == kKvBf16) {
+    if (sparse) hipLaunchKernelGGL((k_debug_gather<kKvBf16, true>), dim3(1), dim3(kThreads), 0, stream, a, b, t, j, dst);
+    else hipLaunchKernelGGL((k_debug_gather<kKvBf16, false>), dim3(1), dim3(kThreads), 0, stream, a, b, t, j, dst);
+  } else {
+    if (sparse) hipLaunchKernelGGL((k_debug_gather<kKvFp8V32, true>), dim3(1), dim3(kThreads), 0, stream, a, b, t, j, dst);
+    else hipLaunchKernelGGL((k_debug_gather<kKvFp8V32, false>), dim3(1), dim3(kThreads), 0, stream, a, b, t, j, dst);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla
