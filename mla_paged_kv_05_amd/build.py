@@ -26,6 +26,9 @@ COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops are kept out of all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # O lives in AGPRs through inline-asm operands; a VGPR spilled into an
+    # "unused" AGPR would overwrite it, so spills never go to AGPRs
+    "-mllvm", "-amdgpu-spill-vgpr-to-agpr=0",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

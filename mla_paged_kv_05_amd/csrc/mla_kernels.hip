@@ -60,6 +60,55 @@ constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer, dword3 for gfx9 f
 // bases and loop bounds stay scalar.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Read-only int32 arrays indexed by wave-uniform values (schedule, lengths,
+// block table): read through the constant address space so they become
+// scalar loads (lgkmcnt), not vector loads whose vmcnt wait would also wait
+// for the KV prefetch in flight.
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+__device__ __forceinline__ int sload(const int32_t* p, int64_t i) {
+  return ((cint_ptr)(p))[i];
+}
+
+// Workgroup barrier for the KV pipeline: waits for this wave's LDS traffic
+// only.  __syncthreads() would also drain every outstanding vector memory
+// op, i.e. the prefetch of the next two steps.  KV arrival is awaited
+// explicitly with vmcnt before this barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS-DMA (global -> LDS, 16 or 4 bytes per lane at M0 + 16*lane) issued as
+// inline asm.  Through the builtins the compiler treats every later LDS read
+// as possibly aliasing the DMA and waits for all vector memory first, which
+// would stall on the KV prefetch each step.  Completion of these loads is
+// awaited explicitly (vmcnt) before the barrier that publishes a step.
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)nbytes);                           // num_records
+  r[3] = (int)kBufferFlags;
+  return r;
+}
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint8_t*)p));
+}
+__device__ __forceinline__ void dma_buf16(uint32_t lds, int voff, i32x4 rs) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_buf4(uint32_t lds, int voff, i32x4 rs) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_glb16(uint32_t lds, const void* g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(g) : "memory", "m0");
+}
+
 // An opaque copy of a per-lane value: loader address arithmetic derived from
 // it is recomputed at each use instead of being hoisted out of the KV loop
 // (where 18+ hoisted offsets would only crowd the register file).
@@ -79,12 +128,67 @@ __device__ __forceinline__ void mfma_s_first(f32x16& c, const bf16x8& a, const b
 __device__ __forceinline__ void mfma_s_acc(f32x16& c, const bf16x8& a, const bf16x8& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
+// O^T += V^T P^T step with the accumulator pinned to AGPRs for its whole
+// life (a builtin leaves O's register class to the allocator, which then
+// shuffles the 256 accumulators between VGPRs and AGPRs inside the loop).
+// Back-to-back accumulation into the same registers needs no wait states.
+__device__ __forceinline__ void mfma_o(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// VALU-written B operand -> MFMA read.
+__device__ __forceinline__ void valu_to_mfma_settle(bf16x8& p0, bf16x8& p1) {
+  asm volatile("s_nop 4" : "+v"(p0), "+v"(p1));
+}
+// Last MFMA into O -> VALU / accvgpr reads of O (finalize): 24 wait states,
+// more than a 32x32 XDL op's write -> read requirement.
+__device__ __forceinline__ void o_settle(f32x16 (&o)[16]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                 "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
+                 "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
+}
 // The hardware does not interlock a VALU read of an MFMA result; the compiler
 // inserts those wait states for builtins but cannot see into the asm above,
 // so S is passed through 24 explicit wait states before any VALU use (more
 // than the XDL-write -> VALU-read requirement of a 32x32 op).
 __device__ __forceinline__ void mfma_s_settle(f32x16& c) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
+}
+
+// o *= alpha on one 16-register AGPR accumulator tile when `cond` (a
+// wave-uniform SGPR value) is non-zero; otherwise nothing.  Wait states
+// around the accvgpr moves are explicit: the compiler does not look inside.
+__device__ __forceinline__ void rescale_tile(f32x16& o, float alpha, uint32_t cond) {
+  float t;
+  asm volatile(
+      "s_cmp_eq_u32 %17, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "v_accvgpr_read_b32 %16, %0\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %0, %16\n\t"
+      "v_accvgpr_read_b32 %16, %1\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %1, %16\n\t"
+      "v_accvgpr_read_b32 %16, %2\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %2, %16\n\t"
+      "v_accvgpr_read_b32 %16, %3\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %3, %16\n\t"
+      "v_accvgpr_read_b32 %16, %4\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %4, %16\n\t"
+      "v_accvgpr_read_b32 %16, %5\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %5, %16\n\t"
+      "v_accvgpr_read_b32 %16, %6\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %6, %16\n\t"
+      "v_accvgpr_read_b32 %16, %7\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %7, %16\n\t"
+      "v_accvgpr_read_b32 %16, %8\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %8, %16\n\t"
+      "v_accvgpr_read_b32 %16, %9\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %9, %16\n\t"
+      "v_accvgpr_read_b32 %16, %10\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %10, %16\n\t"
+      "v_accvgpr_read_b32 %16, %11\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %11, %16\n\t"
+      "v_accvgpr_read_b32 %16, %12\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %12, %16\n\t"
+      "v_accvgpr_read_b32 %16, %13\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %13, %16\n\t"
+      "v_accvgpr_read_b32 %16, %14\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %14, %16\n\t"
+      "v_accvgpr_read_b32 %16, %15\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %15, %16\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n"
+      "1:"
+      : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]),
+        "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]),
+        "+a"(o[14]), "+a"(o[15]), "=&v"(t)
+      : "s"(cond), "v"(alpha)
+      : "scc");
 }
 
 __device__ __forceinline__ float wave_bcast_partner(float v) {
@@ -256,8 +360,8 @@ __device__ __forceinline__ void load_half_bf16_dense(uint8_t* slot, const uint8_
                                                      int valid, int h, int wave, int lane) {
   lane = opaque(lane);
   const uint8_t* page = kv + phys * (int64_t)kTileBytes;
-  __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, valid * kRowBytes, kBufferFlags);
+  const i32x4 rs = make_rsrc(page, valid * kRowBytes);
+  const uint32_t base = lds_off(slot);
 #pragma unroll
   for (int ii = 0; ii < kHalfChunks / 64 / kWaves; ++ii) {
     const int i = ii * kWaves + wave;
@@ -265,8 +369,7 @@ __device__ __forceinline__ void load_half_bf16_dense(uint8_t* slot, const uint8_
     const int r = pos_all / kChunksPerRow;
     const int pos = pos_all - r * kChunksPerRow;
     const int c = pos ^ (r & 7);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(slot + i * 1024), 16,
-                                             (h * kHalfRows + r) * kRowBytes + c * 16, 0, 0, 0);
+    dma_buf16(base + i * 1024, (h * kHalfRows + r) * kRowBytes + c * 16, rs);
   }
 }
 
@@ -285,7 +388,7 @@ __device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8
     const int c = pos ^ (r & 7);
     const int id = r < nvalid ? ids[r] : -1;
     const uint8_t* g = id >= 0 ? kv + (int64_t)id * kRowBytes + c * 16 : g_zero_row + c * 16;
-    __builtin_amdgcn_global_load_lds((const void*)g, LDS_PTR(slot + i * 1024), 16, 0, 0);
+    dma_glb16(lds_off(slot) + i * 1024, g);
   }
 }
 
@@ -301,14 +404,12 @@ __device__ __forceinline__ void load_half_fp8_dense(uint8_t* raw, const uint8_t*
                                                     int valid, int h, int wave, int lane) {
   lane = opaque(lane);
   const uint8_t* page = kv + phys * (int64_t)(kPage * kFp8TokenBytes);
-  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)page, (short)0, valid * kFp8TokenBytes, kBufferFlags);
+  const i32x4 rs = make_rsrc(page, valid * kFp8TokenBytes);
+  const uint32_t base = lds_off(raw);
 #pragma unroll
   for (int ii = 0; ii < kRawLoadsPerWave; ++ii) {
     const int i = ii * kWaves + wave;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(raw + i * 1024), 16,
-                                             h * kHalfRows * kFp8TokenBytes + (i * 64 + lane) * 16,
-                                             0, 0, 0);
+    dma_buf16(base + i * 1024, h * kHalfRows * kFp8TokenBytes + (i * 64 + lane) * 16, rs);
   }
 }
 
@@ -325,7 +426,7 @@ __device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t
     const int id = (pos_all < kRawHalfChunks && r < nvalid) ? ids[r] : -1;
     const uint8_t* g =
         id >= 0 ? kv + (int64_t)id * kFp8TokenBytes + c * 16 : g_zero_row + (pos_all & 63) * 16;
-    __builtin_amdgcn_global_load_lds((const void*)g, LDS_PTR(raw + i * 1024), 16, 0, 0);
+    dma_glb16(lds_off(raw) + i * 1024, g);
   }
 }
 
@@ -373,10 +474,7 @@ __device__ __forceinline__ void fetch_ids_dma(int32_t* ids_lds, const int32_t* i
   const int first = j * kPage + h * kHalfRows;
   const int32_t* base = indices + row_off + first;
   const int n = max(0, min(kHalfRows, topk - first));
-  __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n * 4, kBufferFlags);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(ids_lds), 4, (threadIdx.x & 63) * 4, 0, 0,
-                                           0);
+  dma_buf4(lds_off(ids_lds), (threadIdx.x & 63) * 4, make_rsrc(base, n * 4));
 }
 
 // ---------------------------------------------------------------------------
@@ -420,7 +518,7 @@ struct DecodeLayout {
 
 __device__ __forceinline__ int seq_items(const DecodeArgs& a, int b) {
   if (a.topk > 0) return (a.topk + kPage - 1) / kPage;
-  int L = uni(a.seqlens[b]);
+  int L = uni(sload(a.seqlens, b));
   return L > 0 ? (L + kPage - 1) / kPage : 0;
 }
 
@@ -454,10 +552,11 @@ k_decode(DecodeArgs a) {
     }
   }
   const int32_t* ms = a.meta + 8 * slot;
-  const int b0 = uni(ms[0]);
+  const int b0 = uni(sload(ms, 0));
   if (b0 < 0) return;
-  const int j0 = uni(ms[1]), b1 = uni(ms[2]), j1 = uni(ms[3]), nitems = uni(ms[5]);
-  int split_k = uni(ms[4]);
+  const int j0 = uni(sload(ms, 1)), b1 = uni(sload(ms, 2)), j1 = uni(sload(ms, 3)),
+            nitems = uni(sload(ms, 5));
+  int split_k = uni(sload(ms, 4));
   const int nsteps = 2 * nitems;
 
   // this lane's query row within the sequence
@@ -486,9 +585,9 @@ k_decode(DecodeArgs a) {
   auto issue_load = [&](int b, int j, int h, int step) {
     const int rs = step % kRing;
     if constexpr (!SPARSE) {
-      const int L = uni(a.seqlens[b]);
+      const int L = uni(sload(a.seqlens, b));
       const bool any = j * kPage < L;
-      const int64_t phys = any ? uni(a.block_table[(int64_t)b * a.max_blocks + j]) : 0;
+      const int64_t phys = any ? uni(sload(a.block_table, (int64_t)b * a.max_blocks + j)) : 0;
       const int valid = any ? min(kPage, L - j * kPage) : 0;
       if constexpr (KVF == kKvBf16)
         load_half_bf16_dense(smem + Lay::kTileOff + rs * kHalfBytes, a.kv, phys, valid, h, wave, lane);
@@ -505,9 +604,23 @@ k_decode(DecodeArgs a) {
     }
   };
 
-  // ---- prologue: ids of steps 0..3, loads of steps 0 and 1
+  // loads of step+2 and (sparse) ids of step+4, issued at step `step`
   int lb = b0, lj = j0, lh = 0;   // next step to load
   int fb = b0, fj = j0, fh = 0;   // next step whose ids to fetch
+  auto issue_next = [&](int step) {
+    if (step + 2 < nsteps) {
+      issue_load(lb, lj, lh, step + 2);
+      advance(lb, lj, lh);
+    }
+    if constexpr (SPARSE) {
+      if (step + 4 < nsteps) {
+        fetch_ids(fb, fj, fh, step + 4);
+        advance(fb, fj, fh);
+      }
+    }
+  };
+
+  // ---- prologue: ids of steps 0..3, loads of steps 0 and 1
   if constexpr (SPARSE) {
     for (int s = 0; s < min(4, nsteps); ++s) {
       fetch_ids(fb, fj, fh, s);
@@ -528,9 +641,8 @@ k_decode(DecodeArgs a) {
   int cb = b0, cj = j0, step = 0;
   while (step < nsteps) {
     // ======== one piece: sequence cb, items cj .. piece_end-1
-    const int Lb = uni(a.seqlens[cb]);
+    const int Lb = uni(sload(a.seqlens, cb));
     const int piece_end = item_end(cb);
-    const int piece_first_step = step;
     float m_used = -INFINITY, lsum = 0.f;
     int vis_end = 0;  // dense: keys < vis_end are visible to this row
     if constexpr (!SPARSE) {
@@ -541,90 +653,77 @@ k_decode(DecodeArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) o[mt] = f32x16{};
 
-    for (; cj < piece_end; ++cj) {
-#pragma unroll 1
-      for (int h = 0; h < 2; ++h, ++step) {
-        // ======== one step: 32 keys
-        // This step's loads were issued two steps ago; the previous step then
-        // issued the loads of step+1 (if any) and, sparse, the ids of step+3
-        // (if any).  Wait for everything older than those.  A piece's first
-        // step drains everything (the previous piece's stores are in flight).
-        constexpr int kLoadsPerStep = Lay::kVmPerStep - (SPARSE ? 1 : 0);
-        if (step == piece_first_step || step + 1 >= nsteps) wait_vmcnt<0>();
-        else if (SPARSE && step + 3 >= nsteps) wait_vmcnt<kLoadsPerStep>();
-        else wait_vmcnt<Lay::kVmPerStep>();
-        __syncthreads();  // every wave's loads of this step landed; slot (step+2)%3 is free
-        if (step == piece_first_step) {
-          // query fragments of the new piece (issued before the next loads so
-          // that waiting for them does not wait for those)
+    // ---- piece prologue: drain (the previous piece's stores are in flight),
+    // then the query fragments, issued before the next loads so that waiting
+    // for them does not wait for those
+    wait_vmcnt<0>();
+    lds_barrier();  // every wave's loads of the first step landed
+    {
           const uint16_t* qrow = a.q + ((int64_t)cb * a.rows + (row_ok ? row : 0)) * kDqk;
-          bf16x8 qraw[36];
+      bf16x8 qraw[36];
 #pragma unroll
-          for (int ks = 0; ks < 36; ++ks)
-            qraw[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
-          if (step + 2 < nsteps) {
-            issue_load(lb, lj, lh, step + 2);
-            advance(lb, lj, lh);
-          }
-          if constexpr (SPARSE) {
-            if (step + 4 < nsteps) {
-              fetch_ids(fb, fj, fh, step + 4);
-              advance(fb, fj, fh);
-            }
-          }
-          if constexpr (FUSED) {
-            // RMSNorm over the row's 576 dims (lanes l and l^32 hold it), then
-            // RoPE on dims 512..575 at position len - s_q + t.
-            float ss = 0.f;
+      for (int ks = 0; ks < 36; ++ks)
+        qraw[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
+      if constexpr (FUSED) {
+        // RMSNorm over the row's 576 dims (lanes l and l^32 hold it), then
+        // RoPE on dims 512..575 at position len - s_q + t.
+        float ss = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < 36; ++ks)
+        for (int ks = 0; ks < 36; ++ks)
 #pragma unroll
-              for (int e = 0; e < 8; ++e) { float v = (float)qraw[ks][e]; ss += v * v; }
-            ss += wave_bcast_partner(ss);
-            const float inv = 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
-            const double pos = (double)Lb - (double)a.s_q + (double)tok;
+          for (int e = 0; e < 8; ++e) { float v = (float)qraw[ks][e]; ss += v * v; }
+        ss += wave_bcast_partner(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
+        const double pos = (double)Lb - (double)a.s_q + (double)tok;
 #pragma unroll
-            for (int ks = 0; ks < 36; ++ks) {
-              const int c = 2 * ks + half;
-              const bf16x8 wv = *reinterpret_cast<const bf16x8*>(a.norm_w + c * 8);
-              float y[8];
+        for (int ks = 0; ks < 36; ++ks) {
+          const int c = 2 * ks + half;
+          const bf16x8 wv = *reinterpret_cast<const bf16x8*>(a.norm_w + c * 8);
+          float y[8];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) y[e] = (float)qraw[ks][e] * (float)wv[e] * inv;
-              if (ks >= 32) {
+          for (int e = 0; e < 8; ++e) y[e] = (float)qraw[ks][e] * (float)wv[e] * inv;
+          if (ks >= 32) {
 #pragma unroll
-                for (int pp = 0; pp < 4; ++pp) {
-                  float cs, sn;
-                  rope_cs(pos, (c * 8 - 512) / 2 + pp, a.rope_base, 1.0f, cs, sn);
-                  const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
-                  y[2 * pp] = x0 * cs - x1 * sn;
-                  y[2 * pp + 1] = x0 * sn + x1 * cs;
-                }
-              }
-#pragma unroll
-              for (int e = 0; e < 8; ++e) qraw[ks][e] = (__bf16)y[e];
+            for (int pp = 0; pp < 4; ++pp) {
+              float cs, sn;
+              rope_cs(pos, (c * 8 - 512) / 2 + pp, a.rope_base, 1.0f, cs, sn);
+              const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
+              y[2 * pp] = x0 * cs - x1 * sn;
+              y[2 * pp + 1] = x0 * sn + x1 * cs;
             }
           }
 #pragma unroll
-          for (int ks = 0; ks < 36; ++ks) {
-            const bf16x8 v = row_ok ? qraw[ks] : bf16x8{};
-            if (ks < kQRegSteps) {
-              qf[ks] = v;
-            } else {
-              const int cq = 2 * (ks - kQRegSteps) + half;
-              *reinterpret_cast<bf16x8*>(qlds + r32 * kQLdsRowBytes + ((cq ^ x) << 4)) = v;
-            }
-          }
+          for (int e = 0; e < 8; ++e) qraw[ks][e] = (__bf16)y[e];
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 36; ++ks) {
+        const bf16x8 v = row_ok ? qraw[ks] : bf16x8{};
+        if (ks < kQRegSteps) {
+          qf[ks] = v;
         } else {
-          if (step + 2 < nsteps) {
-            issue_load(lb, lj, lh, step + 2);
-            advance(lb, lj, lh);
-          }
-          if constexpr (SPARSE) {
-            if (step + 4 < nsteps) {
-              fetch_ids(fb, fj, fh, step + 4);
-              advance(fb, fj, fh);
-            }
-          }
+          const int cq = 2 * (ks - kQRegSteps) + half;
+          *reinterpret_cast<bf16x8*>(qlds + r32 * kQLdsRowBytes + ((cq ^ x) << 4)) = v;
+        }
+      }
+    }
+    issue_next(step);
+
+    for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
+      const int h = ps & 1;
+      const int cjs = cj + (ps >> 1);
+      {
+        // ======== one step: 32 keys
+        if (ps > 0) {
+          // This step's loads were issued two steps ago; the previous step
+          // then issued the loads of step+1 (if any) and, sparse, the ids of
+          // step+3 (if any).  Wait for everything older than those.
+          constexpr int kLoadsPerStep = Lay::kVmPerStep - (SPARSE ? 1 : 0);
+          if (step + 1 >= nsteps) wait_vmcnt<0>();
+          else if (SPARSE && step + 3 >= nsteps) wait_vmcnt<kLoadsPerStep>();
+          else wait_vmcnt<Lay::kVmPerStep>();
+          lds_barrier();  // every wave's loads of this step landed; slot (step+2)%3 is free
+          issue_next(step);
         }
 
         const uint8_t* tile;
@@ -633,9 +732,9 @@ k_decode(DecodeArgs a) {
         } else {
           tile = smem + Lay::kTileOff;
           dequant_half(smem + Lay::kTileOff, smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
-          __syncthreads();
+          lds_barrier();
         }
-        const int key0 = cj * kPage + h * kHalfRows;  // first key of this step
+        const int key0 = cjs * kPage + h * kHalfRows;  // first key of this step
         const bool any_key = SPARSE ? (key0 < a.topk) : (key0 < Lb);
         if (any_key) {
           // ---- lane-constant LDS offsets for this step (opaque bases; the
@@ -656,16 +755,31 @@ k_decode(DecodeArgs a) {
           const int voff0 = opaque(vlo + ((0 ^ half) << 6)), voff1 = opaque(vlo + ((1 ^ half) << 6));
 
           // ---- S^T for these 32 keys (rows = lanes), VGPR accumulator
+          // software pipelined: the LDS operands of k-step ks+kLa are read
+          // before the MFMA of k-step ks (order fixed by scheduling fences)
+          constexpr int kLa = 4;
+          auto read_k = [&](int ks) {
+            return *reinterpret_cast<const bf16x8*>(smem + koff[ks & 3] + (ks >> 2) * 128);
+          };
+          auto read_q = [&](int ks) {
+            return *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegSteps) & 3] +
+                                                    ((ks - kQRegSteps) >> 2) * 128);
+          };
           f32x16 sc;
+          bf16x8 kbuf[kLa], qbuf[kLa];
+#pragma unroll
+          for (int i = 0; i < kLa; ++i) kbuf[i] = read_k(i);
 #pragma unroll
           for (int ks = 0; ks < 36; ++ks) {
-            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(smem + koff[ks & 3] + (ks >> 2) * 128);
-            bf16x8 qb;
-            if (ks < kQRegSteps) qb = qf[ks];
-            else qb = *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegSteps) & 3] +
-                                                       ((ks - kQRegSteps) >> 2) * 128);
+            const bf16x8 ka = kbuf[ks % kLa];
+            const bf16x8 qb = ks < kQRegSteps ? qf[ks] : qbuf[ks % kLa];
+            if (ks + kLa < 36) {
+              kbuf[ks % kLa] = read_k(ks + kLa);
+              if (ks + kLa >= kQRegSteps) qbuf[ks % kLa] = read_q(ks + kLa);
+            }
             if (ks == 0) mfma_s_first(sc, ka, qb);
             else mfma_s_acc(sc, ka, qb);
+            __builtin_amdgcn_sched_barrier(0);
           }
           mfma_s_settle(sc);
 
@@ -696,30 +810,21 @@ k_decode(DecodeArgs a) {
           }
           mx = fmaxf(mx, wave_bcast_partner(mx));
           const bool need = mx > m_used + kRescaleThreshold;
-          if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-            const float alpha = need ? exp2f(m_used - mx) : 1.0f;  // exp2(-inf) = 0
-            if (need) m_used = mx;
-            // Scale the AGPR-resident O in place, one register at a time inside
-            // inline asm: written as plain C++ the compiler copies the whole
-            // 256-register accumulator through VGPRs for this rare path and
-            // spills the hot loop's working set to make room.
+          // Rare: the running max moved by more than the threshold; scale O.
+          const uint32_t any_need = uni((int)(__builtin_amdgcn_ballot_w64(need) != 0));
+          const float alpha = need ? exp2f(m_used - mx) : 1.0f;  // exp2(-inf) = 0
+          if (__builtin_expect(any_need != 0, 0)) {
+            o_settle(o);
 #pragma unroll
-            for (int mt = 0; mt < 16; ++mt)
+            for (int mt = 0; mt < 16; ++mt) {
 #pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                float t;
-                asm volatile(
-                    "v_accvgpr_read_b32 %1, %0\n\t"
-                    "s_nop 1\n\t"
-                    "v_mul_f32 %1, %1, %2\n\t"
-                    "v_accvgpr_write_b32 %0, %1"
-                    : "+a"(o[mt][i]), "=&v"(t)
-                    : "v"(alpha));
-              }
-            // accvgpr writes -> next MFMA reading them as accumulator
-            asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-            lsum *= alpha;
+              for (int i = 0; i < 16; ++i) o[mt][i] *= alpha;
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            o_settle(o);
           }
+          if (need) m_used = mx;
+          lsum *= alpha;
           const float mref = m_used == -INFINITY ? 0.f : m_used;
           bf16x8 pf[2];
           float ps = 0.f;
@@ -730,32 +835,41 @@ k_decode(DecodeArgs a) {
             pf[i >> 3][i & 7] = (__bf16)pv;
           }
           lsum += ps;
+          valu_to_mfma_settle(pf[0], pf[1]);
 
           // ---- O^T += V^T P^T over these 32 keys (2 k-steps x 16 d-tiles)
+          // 32 MFMAs, each fed by two transposed reads issued kVa MFMAs ahead
+          constexpr int kVa = 3;
+          auto read_v = [&](int i) {  // i = kq * 16 + mt
+            const int kq = i >> 4, mt = i & 15;
+            const uint8_t* p = smem + ((mt & 1) ? voff1 : voff0) + kq * 16 * kRowBytes + (mt >> 1) * 128;
+            const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(p));
+            const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(p + 8 * kRowBytes));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          };
+          bf16x8 vbuf[kVa];
 #pragma unroll
-          for (int kq = 0; kq < 2; ++kq) {
+          for (int i = 0; i < kVa; ++i) vbuf[i] = read_v(i);
 #pragma unroll
-            for (int mt = 0; mt < 16; ++mt) {
-              const uint8_t* p = smem + ((mt & 1) ? voff1 : voff0) + kq * 16 * kRowBytes + (mt >> 1) * 128;
-              const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) s16x4*)(p));
-              const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) s16x4*)(p + 8 * kRowBytes));
-              const s16x8 v8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-              o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pf[kq],
-                                                              o[mt], 0, 0, 0);
-            }
+          for (int i = 0; i < 32; ++i) {
+            const bf16x8 va = vbuf[i % kVa];
+            if (i + kVa < 32) vbuf[i % kVa] = read_v(i + kVa);
+            mfma_o(o[i & 15], va, pf[i >> 4]);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
     }
 
     // ======== finalize the piece: O / l and LSE; direct output or partial
+    o_settle(o);
     {
       const float lt = lsum + wave_bcast_partner(lsum);
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
       const float lse2 = lt > 0.f ? m_used + __builtin_amdgcn_logf(lt) : -INFINITY;
-      const int nsplit = uni(a.num_splits[cb + 1] - a.num_splits[cb]);
+      const int nsplit = uni(sload(a.num_splits, cb + 1) - sload(a.num_splits, cb));
       if (nsplit == 1) {
         const int64_t orow = (int64_t)cb * a.rows + row;
         if constexpr (!FUSED) {
@@ -826,7 +940,7 @@ k_decode(DecodeArgs a) {
       } else {
         // partial of split `split_k` of sequence cb, row group g, stored in
         // register order: [wave][d-tile][quad][lane][4]
-        const int64_t pidx = (int64_t)uni(a.num_splits[cb] + split_k) * a.groups + g;
+        const int64_t pidx = (int64_t)uni(sload(a.num_splits, cb) + split_k) * a.groups + g;
         float* po = a.part_o + pidx * kPartialOFloats + (size_t)wave * (16 * 4 * 64 * 4);
 #pragma unroll
         for (int mt = 0; mt < 16; ++mt)
