@@ -102,6 +102,9 @@ def main():
     ap.add_argument("--workload", default="dense_b64_h128_L1k-8k")
     ap.add_argument("--rotate", type=int, default=0, help="KV copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times) and exit: "
+                         "the known-size kernel that scales HBM counter readings")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -113,6 +116,15 @@ def main():
     from mla_paged_kv_05_amd import binding as B
 
     dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+        return
     t0 = time.time()
     p = make_workload(args.workload)
     nbytes, flops = algorithmic(p)
