@@ -339,38 +339,63 @@ k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
 
 // ---------------------------------------------------------------------------
 // KV staging.  The unit of work is a half block of 32 tokens.  A bf16 half
-// tile in LDS is [32][576] with token r's 16-byte chunk c at
-// r*1152 + ((c ^ (r & 7)) << 4): the 32 rows a wave reads at one column fall
-// on distinct LDS banks.  Half tiles rotate through a ring of 3 slots, so two
-// halves (72 KB) are in flight while the third is computed on.
+// tile in LDS has two parts:
+//   main  [32][1040 B]: token r's dims 0..511 at r*1040 (1024 B + 16 B pad);
+//   rope  [32][128 B] at kRopeOff: token r's dims 512..575, 16-byte chunk c
+//         at r*128 + ((c ^ ((r >> 1) & 7)) << 4).
+// The 16-byte pad turns every main row into a one-bank-group shift, and the
+// S^T rows are bound to keys in the order key_of_row() below, so the
+// 16-lane phases of the K reads (16 keys, one chunk) and the 32-lane phases
+// of the transposed V reads (keys b, b+4, b+8, b+12 x 4 chunks) both touch
+// 16 distinct 4-bank groups: no bank conflicts, and each read stream needs a
+// single per-lane base address plus immediates.  Half tiles rotate through a
+// ring of 3 slots, so two halves are in flight while the third is computed
+// on.
 // ---------------------------------------------------------------------------
 constexpr int kHalfRows = 32;
-constexpr int kHalfBytes = kHalfRows * kRowBytes;          // 36864
-constexpr int kHalfChunks = kHalfRows * kChunksPerRow;     // 2304 = 36 wave-loads
+constexpr int kMainStride = 1040;
+constexpr int kRopeOff = kHalfRows * kMainStride;               // 33280
+constexpr int kRopeStride = 128;
+constexpr int kHalfBytes = kRopeOff + kHalfRows * kRopeStride;  // 37376
+constexpr int kLoadsPerHalf = kHalfRows / kWaves + 1;           // 9 per wave: 8 rows + rope
 constexpr int kRing = 3;
+
+// The key held by row m (0..31) of an S^T tile (and by k-slot m of the
+// matching P^T / V^T operands): keys 4j+c of a 16-row block sit at rows
+// 4c+j, so 4 consecutive rows hold keys 4 apart.
+__host__ __device__ constexpr int key_of_row(int m) {
+  return 16 * (m >> 4) + 4 * (m & 3) + ((m >> 2) & 3);
+}
+__device__ __forceinline__ int rope_phys_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // All-zero source for rows that hold no token (masked sparse entries).
 __device__ __attribute__((aligned(16))) const uint8_t g_zero_row[kRowBytes] = {0};
 
+// global -> LDS with a wave-uniform 64-bit base and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma_glb16_s(uint32_t lds, int voff, const void* sbase) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
 // Dense bf16: half `h` of pool block `phys` whose first `valid` tokens are
 // real.  The buffer resource covers exactly those tokens, so the hardware
-// writes zeros for the others and never reads past the sequence.  Each wave
-// issues 9 LDS-DMA loads; load i fills slot bytes [i*1024, i*1024+1024).
+// writes zeros for the others and never reads past the sequence.  Wave w
+// stages main rows w, w+4, ..., w+28 (one 1 KB load each) and rope rows
+// 8w..8w+7 (one load).
 __device__ __forceinline__ void load_half_bf16_dense(uint8_t* slot, const uint8_t* kv, int64_t phys,
                                                      int valid, int h, int wave, int lane) {
-  lane = opaque(lane);
+  const int l16 = opaque(lane << 4);
   const uint8_t* page = kv + phys * (int64_t)kTileBytes;
   const i32x4 rs = make_rsrc(page, valid * kRowBytes);
   const uint32_t base = lds_off(slot);
 #pragma unroll
-  for (int ii = 0; ii < kHalfChunks / 64 / kWaves; ++ii) {
-    const int i = ii * kWaves + wave;
-    const int pos_all = i * 64 + lane;
-    const int r = pos_all / kChunksPerRow;
-    const int pos = pos_all - r * kChunksPerRow;
-    const int c = pos ^ (r & 7);
-    dma_buf16(base + i * 1024, (h * kHalfRows + r) * kRowBytes + c * 16, rs);
+  for (int k = 0; k < kHalfRows / kWaves; ++k) {
+    const int r = wave + kWaves * k;
+    dma_buf16(base + r * kMainStride, (h * kHalfRows + r) * kRowBytes + l16, rs);
   }
+  const int rr = 8 * wave + (l16 >> 7);
+  dma_buf16(base + kRopeOff + wave * 1024,
+            (h * kHalfRows + rr) * kRowBytes + 1024 + (rope_phys_chunk(rr, (l16 >> 4) & 7) << 4), rs);
 }
 
 // Sparse bf16: row r is flat pool token ids[r] when r < nvalid and
@@ -378,18 +403,20 @@ __device__ __forceinline__ void load_half_bf16_dense(uint8_t* slot, const uint8_
 __device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8_t* kv,
                                                       const int32_t* ids, int nvalid, int wave,
                                                       int lane) {
-  lane = opaque(lane);
+  const int l16 = opaque(lane << 4);
+  const uint32_t base = lds_off(slot);
 #pragma unroll
-  for (int ii = 0; ii < kHalfChunks / 64 / kWaves; ++ii) {
-    const int i = ii * kWaves + wave;
-    const int pos_all = i * 64 + lane;
-    const int r = pos_all / kChunksPerRow;
-    const int pos = pos_all - r * kChunksPerRow;
-    const int c = pos ^ (r & 7);
-    const int id = r < nvalid ? ids[r] : -1;
-    const uint8_t* g = id >= 0 ? kv + (int64_t)id * kRowBytes + c * 16 : g_zero_row + c * 16;
-    dma_glb16(lds_off(slot) + i * 1024, g);
+  for (int k = 0; k < kHalfRows / kWaves; ++k) {
+    const int r = wave + kWaves * k;
+    const int id = uni(r < nvalid ? ids[r] : -1);
+    const uint8_t* src = id >= 0 ? kv + (int64_t)id * kRowBytes : g_zero_row;
+    dma_glb16_s(base + r * kMainStride, l16, src);
   }
+  const int rr = 8 * wave + (l16 >> 7);
+  const int id = rr < nvalid ? ids[rr] : -1;
+  const int cc = rope_phys_chunk(rr, (l16 >> 4) & 7);
+  const uint8_t* g = id >= 0 ? kv + (int64_t)id * kRowBytes + 1024 + cc * 16 : g_zero_row + 1024 + cc * 16;
+  dma_glb16(base + kRopeOff + wave * 1024, g);
 }
 
 // FP8 V3.2 records of one half (32 x 656 B = 1312 chunks) are staged raw by
@@ -435,34 +462,32 @@ __device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t
 // dims 512..575 are copied.  An all-zero record gives a zero row.
 __device__ __forceinline__ void dequant_half(uint8_t* tile, const uint8_t* raw, int tid) {
 #pragma unroll
-  for (int kk = 0; kk < kHalfChunks / kThreads; ++kk) {
+  for (int kk = 0; kk < kHalfRows * 64 / kThreads; ++kk) {
     const int k = kk * kThreads + tid;
-    const int r = k / kChunksPerRow;
-    const int c = k - r * kChunksPerRow;
+    const int r = k >> 6, c = k & 63;
     const uint8_t* rec = raw + r * kFp8TokenBytes;
+    const uint2 code = *reinterpret_cast<const uint2*>(rec + c * 8);
+    const float sc = *reinterpret_cast<const float*>(rec + 512 + (c >> 4) * 4);
+    const uint32_t cw[2] = {code.x, code.y};
     uint32_t w[4];
-    if (c < 64) {
-      const uint2 code = *reinterpret_cast<const uint2*>(rec + c * 8);
-      const float sc = *reinterpret_cast<const float*>(rec + 512 + (c >> 4) * 4);
-      const uint32_t cw[2] = {code.x, code.y};
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        typedef __attribute__((ext_vector_type(2))) float f2;
-        f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], false);
-        f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], true);
-        __bf16 b0 = (__bf16)(lo[0] * sc), b1 = (__bf16)(lo[1] * sc);
-        __bf16 b2 = (__bf16)(hi[0] * sc), b3 = (__bf16)(hi[1] * sc);
-        w[2 * hh] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-                    ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        w[2 * hh + 1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-      }
-    } else {
-      const uint4 v = *reinterpret_cast<const uint4*>(rec + 528 + (c - 64) * 16);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    for (int hh = 0; hh < 2; ++hh) {
+      typedef __attribute__((ext_vector_type(2))) float f2;
+      f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], false);
+      f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], true);
+      __bf16 b0 = (__bf16)(lo[0] * sc), b1 = (__bf16)(lo[1] * sc);
+      __bf16 b2 = (__bf16)(hi[0] * sc), b3 = (__bf16)(hi[1] * sc);
+      w[2 * hh] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      w[2 * hh + 1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
     }
-    *reinterpret_cast<uint4*>(tile + r * kRowBytes + ((c ^ (r & 7)) << 4)) =
-        make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(tile + r * kMainStride + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  {
+    const int r = tid >> 3, c = tid & 7;
+    const uint4 v = *reinterpret_cast<const uint4*>(raw + r * kFp8TokenBytes + 528 + c * 16);
+    *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = v;
   }
 }
 
@@ -513,7 +538,7 @@ struct DecodeLayout {
   static constexpr int kSmem = kIdsOff + (SPARSE ? kIdsSlots * 256 : 0);
   // per-step VMEM instructions issued by every wave (loads + id fetch)
   static constexpr int kVmPerStep =
-      (KVF == kKvBf16 ? kHalfChunks / 64 / kWaves : kRawLoadsPerWave) + (SPARSE ? 1 : 0);
+      (KVF == kKvBf16 ? kLoadsPerHalf : kRawLoadsPerWave) + (SPARSE ? 1 : 0);
 };
 
 __device__ __forceinline__ int seq_items(const DecodeArgs& a, int b) {
@@ -634,7 +659,9 @@ k_decode(DecodeArgs a) {
   }
 
   uint8_t* qlds = smem + Lay::kQOff + wave * kQLdsWaveBytes;
-  const int x = lane & 7;
+  // Q rows are 384 B apart (an 8-group shift): chunk c of row r at
+  // c ^ ((r >> 1) & 7) puts the 16 rows of a read phase on distinct groups
+  const int x = (r32 >> 1) & 7;
   bf16x8 qf[kQRegSteps];
   f32x16 o[16];
 
@@ -743,23 +770,27 @@ k_decode(DecodeArgs a) {
           // 16*kk + 4*half + (lane&15)/4 (+8 for k-slots 4..7) and dims
           // 32*mt + 16*((lane>>4)&1) + 4*(lane&3).
           const int tb = (int)(tile - smem);
-          int koff[4], qoff[4];
+          const int mkey = key_of_row(r32);  // key of this lane's S^T row
+          const int koff = opaque(tb + mkey * kMainStride + 16 * half);
+          const int kroff = tb + kRopeOff + mkey * kRopeStride;
+          const int kfr = (mkey >> 1) & 7;
+          int qoff[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            koff[e] = opaque(tb + r32 * kRowBytes + ((((2 * e) | half) ^ x) << 4));
+          for (int e = 0; e < 4; ++e)
             qoff[e] = opaque((int)(qlds - smem) + r32 * kQLdsRowBytes + ((((2 * e) | half) ^ x) << 4));
-          }
-          const int kr = 4 * half + ((lane & 15) >> 2);
-          const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-          const int vlo = tb + ((cl ^ ((lane >> 2) & 3)) << 4) + 8 * (lane & 1) + kr * kRowBytes;
-          const int voff0 = opaque(vlo + ((0 ^ half) << 6)), voff1 = opaque(vlo + ((1 ^ half) << 6));
+          // V^T (transposed reads): this lane supplies key row
+          // key_of_row(16kq + 8hi + 4half + j) = 16kq + 4j + 2hi + half,
+          // j = (lane & 15) >> 2, and dims 32mt + 16*((lane >> 4) & 1) + 4*(lane & 3)
+          const int voff = opaque(tb + (4 * ((lane & 15) >> 2) + half) * kMainStride +
+                                  32 * ((lane >> 4) & 1) + 8 * (lane & 3));
 
           // ---- S^T for these 32 keys (rows = lanes), VGPR accumulator
           // software pipelined: the LDS operands of k-step ks+kLa are read
           // before the MFMA of k-step ks (order fixed by scheduling fences)
           constexpr int kLa = 4;
           auto read_k = [&](int ks) {
-            return *reinterpret_cast<const bf16x8*>(smem + koff[ks & 3] + (ks >> 2) * 128);
+            if (ks < 32) return *reinterpret_cast<const bf16x8*>(smem + koff + 32 * ks);
+            return *reinterpret_cast<const bf16x8*>(smem + kroff + ((((2 * (ks - 32)) | half) ^ kfr) << 4));
           };
           auto read_q = [&](int ks) {
             return *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegSteps) & 3] +
@@ -791,7 +822,7 @@ k_decode(DecodeArgs a) {
             const int nvalid = row_ok ? min(kHalfRows, a.topk - key0) : 0;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int k = 8 * (i >> 2) + 4 * half + (i & 3);
+              const int k = key_of_row(8 * (i >> 2) + (i & 3)) + half;
               float v = sc[i] * a.scale_log2;
               v = (k < nvalid && ids[k] >= 0) ? v : -INFINITY;
               sc[i] = v;
@@ -801,7 +832,7 @@ k_decode(DecodeArgs a) {
             const int lim = vis_end - key0;  // keys < lim visible in this step
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int k = 8 * (i >> 2) + 4 * half + (i & 3);
+              const int k = key_of_row(8 * (i >> 2) + (i & 3)) + half;
               float v = sc[i] * a.scale_log2;
               v = k < lim ? v : -INFINITY;
               sc[i] = v;
@@ -842,11 +873,11 @@ k_decode(DecodeArgs a) {
           constexpr int kVa = 3;
           auto read_v = [&](int i) {  // i = kq * 16 + mt
             const int kq = i >> 4, mt = i & 15;
-            const uint8_t* p = smem + ((mt & 1) ? voff1 : voff0) + kq * 16 * kRowBytes + (mt >> 1) * 128;
+            const uint8_t* p = smem + voff + kq * 16 * kMainStride + mt * 64;
             const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4*)(p));
             const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(p + 8 * kRowBytes));
+                (__attribute__((address_space(3))) s16x4*)(p + 2 * kMainStride));
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
           };
           bf16x8 vbuf[kVa];
@@ -1111,10 +1142,11 @@ __global__ void __launch_bounds__(kThreads) k_debug_gather(DecodeArgs a, int b, 
       dequant_half(tile, raw, tid);
       __syncthreads();
     }
-    for (int k = tid; k < kHalfChunks; k += kThreads) {
+    for (int k = tid; k < kHalfRows * kChunksPerRow; k += kThreads) {
       const int r = k / kChunksPerRow, c = k - r * kChunksPerRow;
-      const uint4 v = *reinterpret_cast<const uint4*>(tile + r * kRowBytes + ((c ^ (r & 7)) << 4));
-      *reinterpret_cast<uint4*>(dst + (h * kHalfRows + r) * kDqk + c * 8) = v;
+      const uint8_t* src = c < 64 ? tile + r * kMainStride + c * 16
+                                  : tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c - 64) << 4);
+      *reinterpret_cast<uint4*>(dst + (h * kHalfRows + r) * kDqk + c * 8) = *reinterpret_cast<const uint4*>(src);
     }
   }
 }
