@@ -167,16 +167,30 @@ def main():
     sh = ctypes.c_void_p(stream.cuda_stream)
     sl_p, meta_p, ns_p = ctypes.c_void_p(sl.data_ptr()), ctypes.c_void_p(meta.data_ptr()), ctypes.c_void_p(ns.data_ptr())
 
-    def step(i, ev=None):
+    # The decode kernel's own start/end timestamps (mla_decode_timed records
+    # the events at the kernel dispatch), on the launch stream.
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime already loaded by torch
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def hip_event():
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def step(i, ev=None, kev=None):
         pr = params[i % R]
         if ev is not None:
             ev[0].record(stream)
         st = lib.mla_get_metadata(sl_p, p.batch, rows, 1, topk, S, meta_p, ns_p, sh)
         if ev is not None:
             ev[1].record(stream)
-        st |= lib.mla_decode(ctypes.byref(pr), sh)
-        if ev is not None:
-            ev[2].record(stream)
+        if kev is not None:
+            st |= lib.mla_decode_timed(ctypes.byref(pr), sh, kev[0], kev[1])
+        else:
+            st |= lib.mla_decode(ctypes.byref(pr), sh)
         st |= lib.mla_combine(ctypes.byref(pr), sh)
         if st != 0:
             raise RuntimeError(lib.mla_last_error().decode())
@@ -184,19 +198,27 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    kevs = [(hip_event(), hip_event()) for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, evs[i], kevs[i])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
-    dec_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)]
+    dec_ms = []
+    for k0, k1 in kevs:
+        t = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(t), k0, k1) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        dec_ms.append(t.value)
+        hip.hipEventDestroy(k0)
+        hip.hipEventDestroy(k1)
     meta_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
     dec_avg = float(np.mean(dec_ms))
     log(f"step {ms * 1e3:.1f} us (wall {wall / args.steps * 1e6:.1f} us); decode kernel avg "

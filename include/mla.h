@@ -95,7 +95,8 @@ mla_status mla_get_metadata(const int32_t* cache_seqlens, int32_t batch,
                             int32_t num_slots, int32_t* sched_meta, int32_t* num_splits,
                             void* stream);
 
-/* [host] Workspace bytes a decode call needs (fp32 split partials). */
+/* [host] Workspace bytes a decode call needs: split partials, O in bf16
+ * (128 rows x 512 per row group) and LSE in fp32 (128 per row group). */
 size_t mla_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int32_t num_slots);
 
 typedef struct mla_decode_params {
@@ -134,13 +135,23 @@ typedef struct mla_decode_params {
 
 /* Paged MLA decode: O and LSE for every query row (see the file comment).
  * A row that sees no key gets O = 0 and LSE = -inf.  Sequences whose work
- * the schedule splits write fp32 partials to the workspace and a combine
+ * the schedule splits write partials (O in bf16, LSE in fp32) to the
+ * workspace and a combine
  * pass merges them by LSE; others write their output directly.
  * Supported: h_kv = 1, d_qk = 576, d_v = 512, page 64, s_q*h_q <= 65536;
  * sparse needs causal = 0 and (s_q == 1 or h_q % 128 == 0); FP8 KV needs
  * indices; fused needs s_q*h_q of whole heads as above.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP (launch failure). */
 mla_status mla_decode(const mla_decode_params* params, void* stream);
+
+/* Measurement hook: mla_decode whose decode-kernel launch also records
+ * `start_event` and `stop_event` (hipEvent_t created with timing enabled;
+ * either may be NULL) at the kernel's own start and end on the stream, so
+ * hipEventElapsedTime gives the kernel's execution time without the gaps
+ * that events recorded around the launch add.  Same arguments and errors as
+ * mla_decode. */
+mla_status mla_decode_timed(const mla_decode_params* params, void* stream, void* start_event,
+                            void* stop_event);
 
 /* The LSE merge of split partials ("FlashMLA" Ampere-adaptation README,
  * section "Usage": the decode returns (o, lse) over the whole KV length).

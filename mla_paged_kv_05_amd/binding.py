@@ -74,7 +74,7 @@ MLA_FLAG_DEFER_COMBINE = 1
 
 
 EXPORTED = ["mla_num_sched_slots", "mla_sched_meta_ints", "mla_num_splits_ints", "mla_get_metadata",
-            "mla_workspace_bytes", "mla_decode", "mla_combine", "mla_debug_gather",
+            "mla_workspace_bytes", "mla_decode", "mla_decode_timed", "mla_combine", "mla_debug_gather",
             "mla_status_string", "mla_last_error"]
 
 _lib = None
@@ -103,6 +103,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_workspace_bytes.argtypes = [c.c_int32, c.c_int32, c.c_int32, c.c_int32]
     lib.mla_decode.restype = c.c_int
     lib.mla_decode.argtypes = [c.POINTER(DecodeParams), c.c_void_p]
+    lib.mla_decode_timed.restype = c.c_int
+    lib.mla_decode_timed.argtypes = [c.POINTER(DecodeParams), c.c_void_p, c.c_void_p, c.c_void_p]
     lib.mla_combine.restype = c.c_int
     lib.mla_combine.argtypes = [c.POINTER(DecodeParams), c.c_void_p]
     lib.mla_debug_gather.restype = c.c_int

@@ -93,7 +93,7 @@ size_t mla_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int32_t num_
   if (batch < 0 || s_q < 1 || h_q < 1 || num_slots < 1) return 0;
   const size_t G = (size_t)mla::row_groups(s_q * h_q);
   const size_t P = partials_max(batch, num_slots) * G;
-  return P * (mla::kPartialOFloats + mla::kPartialLseFloats) * sizeof(float);
+  return P * (mla::kPartialOElems * sizeof(uint16_t) + mla::kPartialLseFloats * sizeof(float));
 }
 
 static mla_status build_args(const mla_decode_params* p, mla::DecodeArgs& a, bool& sparse) {
@@ -154,8 +154,8 @@ static mla_status build_args(const mla_decode_params* p, mla::DecodeArgs& a, boo
   a.indices = p->indices;
   a.meta = p->sched_meta;
   a.num_splits = p->num_splits;
-  a.part_o = static_cast<float*>(p->workspace);
-  a.part_lse = a.part_o + P * mla::kPartialOFloats;
+  a.part_o = static_cast<uint16_t*>(p->workspace);
+  a.part_lse = reinterpret_cast<float*>(a.part_o + P * mla::kPartialOElems);
   a.out = p->out;
   a.lse = p->lse;
   a.out_scale = p->out_scale;
@@ -176,19 +176,29 @@ static mla_status build_args(const mla_decode_params* p, mla::DecodeArgs& a, boo
   return MLA_OK;
 }
 
-mla_status mla_decode(const mla_decode_params* p, void* stream) {
+static mla_status decode_impl(const mla_decode_params* p, void* stream, hipEvent_t start,
+                              hipEvent_t stop) {
   mla::DecodeArgs a{};
   bool sparse = false;
   mla_status st = build_args(p, a, sparse);
   if (st != MLA_OK) return st;
   if (p->batch == 0) return MLA_OK;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = mla::launch_decode(a, p->kv_format, sparse, p->fused != 0, s);
+  hipError_t e = mla::launch_decode(a, p->kv_format, sparse, p->fused != 0, s, start, stop);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (p->flags & MLA_FLAG_DEFER_COMBINE) return MLA_OK;
   e = mla::launch_combine(a, p->fused != 0, s);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return MLA_OK;
+}
+
+mla_status mla_decode(const mla_decode_params* p, void* stream) {
+  return decode_impl(p, stream, nullptr, nullptr);
+}
+
+mla_status mla_decode_timed(const mla_decode_params* p, void* stream, void* start_event,
+                            void* stop_event) {
+  return decode_impl(p, stream, (hipEvent_t)start_event, (hipEvent_t)stop_event);
 }
 
 mla_status mla_combine(const mla_decode_params* p, void* stream) {

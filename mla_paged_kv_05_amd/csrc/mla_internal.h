@@ -29,7 +29,7 @@ inline int row_groups(int rows) { return (rows + kRowsPerWg - 1) / kRowsPerWg; }
 
 // Partial results of one (split, row group): 128 rows x 512 fp32 in the
 // decode kernel's register order plus 128 fp32 LSEs.
-constexpr size_t kPartialOFloats = (size_t)kRowsPerWg * kDv;
+constexpr size_t kPartialOElems = (size_t)kRowsPerWg * kDv;   // bf16 elements
 constexpr size_t kPartialLseFloats = kRowsPerWg;
 
 struct DecodeArgs {
@@ -40,7 +40,7 @@ struct DecodeArgs {
   const int32_t* indices;    // sparse only
   const int32_t* meta;       // [S][8]
   const int32_t* num_splits; // [batch+1]
-  float* part_o;             // [max_partials][G][128*512] (register order)
+  uint16_t* part_o;          // bf16 [max_partials][G][128*512] (register order)
   float* part_lse;           // [max_partials][G][128]
   void* out;                 // bf16 or e4m3 [batch][rows][512]
   float* lse;                // [batch][rows]
@@ -57,7 +57,7 @@ enum KvFormat { kKvBf16 = 0, kKvFp8V32 = 1 };
 hipError_t launch_sched(const int32_t* seqlens, int batch, int rows, int topk, int num_slots,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool fused,
-                         hipStream_t stream);
+                         hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t launch_combine(const DecodeArgs& a, bool fused, hipStream_t stream);
 hipError_t launch_debug_gather(const DecodeArgs& a, int kv_format, bool sparse, int b, int t,
                                int j, uint16_t* dst, hipStream_t stream);

@@ -30,6 +30,7 @@
 //    O accumulator is almost never rescaled ("skip scale", AI Wiki, section
 //    "The Ascend kernel deep-dive"); exact up to rounding.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <cstdint>
 #include <cmath>
 
@@ -191,9 +192,15 @@ __device__ __forceinline__ void rescale_tile(f32x16& o, float alpha, uint32_t co
       : "scc");
 }
 
-__device__ __forceinline__ float wave_bcast_partner(float v) {
-  // value held by lane l ^ 32 (the other half of the same row)
-  return __shfl_xor(v, 32, 64);
+// Max / sum over the lane pair (l, l ^ 32) that holds one query row:
+// v_permlane32_swap leaves {v[l], v[l ^ 32]} in the two results of every lane.
+__device__ __forceinline__ float row_max2(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row_sum2(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -606,20 +613,85 @@ k_decode(DecodeArgs a) {
     if constexpr (SPARSE)
       fetch_ids_dma(ids_slot(step), a.indices, ((int64_t)b * a.s_q + gtok) * a.topk, a.topk, j, h);
   };
-  // stage step `step` = (b, j, h) into its ring slot
-  auto issue_load = [&](int b, int j, int h, int step) {
+  // Load walker: (lb, lj, lh) is the next step to stage, lL and lend the
+  // length and item count of sequence lb, lphys the physical block of item
+  // (lb, lj).  On the bf16 dense path the block of a new item and the length
+  // of the next sequence are fetched by vector loads a step before they are
+  // needed and copied to scalars by land() right after the step-start
+  // vmcnt(0) wait.  (Scalar loads in flight would turn every LDS-operand wait
+  // of the MFMA loops into a full lgkmcnt(0) drain; a compiler-inserted wait
+  // on the vector loads elsewhere would also wait for the KV loads, which it
+  // cannot see.)  The FP8 path, whose waits keep a step of KV loads in
+  // flight, reads them with scalar loads when it needs them.
+  constexpr bool kVecWalk = KVF == kKvBf16 && !SPARSE;
+  int lb = b0, lj = j0, lh = 0;
+  int lL = SPARSE ? 0 : uni(sload(a.seqlens, b0));
+  int lend = item_end(b0);
+  int lphys = 0, lnL = 0;
+  const __amdgpu_buffer_rsrc_t bt_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(a.block_table), 0, kVecWalk ? (int)((int64_t)a.batch * a.max_blocks * 4) : 0,
+      (int)kBufferFlags);
+  const __amdgpu_buffer_rsrc_t sl_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(a.seqlens), 0, kVecWalk ? a.batch * 4 : 0, (int)kBufferFlags);
+  // Offsets go in the scalar soffset field (always in range): a VGPR
+  // address would make the compiler wait for the load, and with it for the
+  // KV loads issued before it, before that VGPR is reused.
+  int phys_v = 0, nL_v = 0;  // vector copies in flight
+  bool lany = false;
+  auto fetch_phys = [&]() {
+    const bool any = lb <= b1 && lj * kPage < lL;
+    if constexpr (kVecWalk) {
+      lany = any;
+      phys_v = __builtin_amdgcn_raw_buffer_load_b32(bt_rs, 0, any ? (lb * a.max_blocks + lj) * 4 : 0, 0);
+    } else if constexpr (!SPARSE) {
+      lphys = any ? uni(sload(a.block_table, (int64_t)lb * a.max_blocks + lj)) : 0;
+    }
+  };
+  auto fetch_next_len = [&]() {
+    if constexpr (kVecWalk) nL_v = __builtin_amdgcn_raw_buffer_load_b32(sl_rs, 0, min(lb + 1, b1) * 4, 0);
+  };
+  auto land = [&]() {
+    if constexpr (kVecWalk) {
+      lphys = lany ? uni(phys_v) : 0;
+      lnL = uni(nL_v);
+    }
+  };
+  auto advance_load = [&]() {
+    if (lh == 0) { lh = 1; return; }
+    lh = 0;
+    ++lj;
+    if (lj >= lend) {
+      ++lb;
+      lj = 0;
+      const int bq = min(lb, b1);  // nothing past the slot's last sequence is staged
+      if constexpr (kVecWalk) {
+        lL = lnL;
+        fetch_next_len();
+        lend = lb == b1 ? j1 : max((lL + kPage - 1) / kPage, 1);
+      } else {
+        if constexpr (!SPARSE) lL = uni(sload(a.seqlens, bq));
+        lend = item_end(bq);
+      }
+    }
+    lb = uni(lb);
+    lj = uni(lj);
+    fetch_phys();
+  };
+  fetch_phys();
+  fetch_next_len();
+  land();  // kernel start: nothing else is in flight yet
+  // stage the walker's step as step `step` into its ring slot
+  auto issue_load = [&](int step) {
     const int rs = step % kRing;
     if constexpr (!SPARSE) {
-      const int L = uni(sload(a.seqlens, b));
-      const bool any = j * kPage < L;
-      const int64_t phys = any ? uni(sload(a.block_table, (int64_t)b * a.max_blocks + j)) : 0;
-      const int valid = any ? min(kPage, L - j * kPage) : 0;
+      const bool any = lj * kPage < lL;
+      const int valid = any ? min(kPage, lL - lj * kPage) : 0;
       if constexpr (KVF == kKvBf16)
-        load_half_bf16_dense(smem + Lay::kTileOff + rs * kHalfBytes, a.kv, phys, valid, h, wave, lane);
+        load_half_bf16_dense(smem + Lay::kTileOff + rs * kHalfBytes, a.kv, lphys, valid, lh, wave, lane);
       else
-        load_half_fp8_dense(smem + Lay::kRawOff + rs * kRawSlotBytes, a.kv, phys, valid, h, wave, lane);
+        load_half_fp8_dense(smem + Lay::kRawOff + rs * kRawSlotBytes, a.kv, lphys, valid, lh, wave, lane);
     } else {
-      const int nvalid = min(kHalfRows, a.topk - j * kPage - h * kHalfRows);
+      const int nvalid = min(kHalfRows, a.topk - lj * kPage - lh * kHalfRows);
       if constexpr (KVF == kKvBf16)
         load_half_bf16_sparse(smem + Lay::kTileOff + rs * kHalfBytes, a.kv, ids_slot(step), nvalid,
                               wave, lane);
@@ -630,12 +702,11 @@ k_decode(DecodeArgs a) {
   };
 
   // loads of step+2 and (sparse) ids of step+4, issued at step `step`
-  int lb = b0, lj = j0, lh = 0;   // next step to load
   int fb = b0, fj = j0, fh = 0;   // next step whose ids to fetch
   auto issue_next = [&](int step) {
     if (step + 2 < nsteps) {
-      issue_load(lb, lj, lh, step + 2);
-      advance(lb, lj, lh);
+      issue_load(step + 2);
+      advance_load();
     }
     if constexpr (SPARSE) {
       if (step + 4 < nsteps) {
@@ -654,8 +725,8 @@ k_decode(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
   }
   for (int s = 0; s < min(2, nsteps); ++s) {
-    issue_load(lb, lj, lh, s);
-    advance(lb, lj, lh);
+    issue_load(s);
+    advance_load();
   }
 
   uint8_t* qlds = smem + Lay::kQOff + wave * kQLdsWaveBytes;
@@ -699,7 +770,7 @@ k_decode(DecodeArgs a) {
         for (int ks = 0; ks < 36; ++ks)
 #pragma unroll
           for (int e = 0; e < 8; ++e) { float v = (float)qraw[ks][e]; ss += v * v; }
-        ss += wave_bcast_partner(ss);
+        ss = row_sum2(ss);
         const float inv = 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
         const double pos = (double)Lb - (double)a.s_q + (double)tok;
 #pragma unroll
@@ -734,13 +805,198 @@ k_decode(DecodeArgs a) {
         }
       }
     }
-    issue_next(step);
 
-    for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
-      const int h = ps & 1;
-      const int cjs = cj + (ps >> 1);
-      {
-        // ======== one step: 32 keys
+    // ======== building blocks of one 32-key step
+    const int mkey = key_of_row(r32);  // key held by this lane's S^T row
+    const int kfr = (mkey >> 1) & 7;
+    auto tile_off = [&](int st) -> int {
+      if constexpr (KVF == kKvBf16) return Lay::kTileOff + (st % kRing) * kHalfBytes;
+      else return Lay::kTileOff;
+    };
+    // S^T (32 keys x 32 rows) of the tile at LDS offset tb into sc, with the
+    // LDS operands of k-step ks+kLa read before the MFMA of k-step ks (order
+    // fixed by scheduling fences); hook(ks) runs after that MFMA is issued.
+    auto qk = [&](int tb, f32x16& sc, auto&& hook) {
+      constexpr int kLa = 4;
+      const int koff = opaque(tb + mkey * kMainStride + 16 * half);
+      const int kroff = tb + kRopeOff + mkey * kRopeStride;
+      int qoff[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qoff[e] = opaque((int)(qlds - smem) + r32 * kQLdsRowBytes + ((((2 * e) | half) ^ x) << 4));
+      auto read_k = [&](int ks) {
+        if (ks < 32) return *reinterpret_cast<const bf16x8*>(smem + koff + 32 * ks);
+        return *reinterpret_cast<const bf16x8*>(smem + kroff + ((((2 * (ks - 32)) | half) ^ kfr) << 4));
+      };
+      auto read_q = [&](int ks) {
+        return *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegSteps) & 3] +
+                                                ((ks - kQRegSteps) >> 2) * 128);
+      };
+      bf16x8 kbuf[kLa], qbuf[kLa];
+#pragma unroll
+      for (int i = 0; i < kLa; ++i) kbuf[i] = read_k(i);
+#pragma unroll
+      for (int ks = 0; ks < 36; ++ks) {
+        const bf16x8 ka = kbuf[ks % kLa];
+        const bf16x8 qb = ks < kQRegSteps ? qf[ks] : qbuf[ks % kLa];
+        if (ks + kLa < 36) {
+          kbuf[ks % kLa] = read_k(ks + kLa);
+          if (ks + kLa >= kQRegSteps) qbuf[ks % kLa] = read_q(ks + kLa);
+        }
+        if (ks == 0) mfma_s_first(sc, ka, qb);
+        else mfma_s_acc(sc, ka, qb);
+        hook(ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma_s_settle(sc);
+    };
+    // O^T += V^T P^T over the tile at tb (2 k-steps x 16 d-tiles): 32 MFMAs,
+    // each fed by two transposed reads issued kVa MFMAs ahead.  This lane
+    // supplies key row key_of_row(16kq + 8hi + 4half + j) = 16kq + 4j + 2hi +
+    // half (j = (lane & 15) >> 2) and dims 32mt + 16*((lane >> 4) & 1) + 4*(lane & 3).
+    auto pv = [&](int tb, const bf16x8 (&pf)[2]) {
+      constexpr int kVa = 3;
+      const int voff = opaque(tb + (4 * ((lane & 15) >> 2) + half) * kMainStride +
+                              32 * ((lane >> 4) & 1) + 8 * (lane & 3));
+      auto read_v = [&](int i) {  // i = kq * 16 + mt
+        const int kq = i >> 4, mt = i & 15;
+        const uint8_t* p = smem + voff + kq * 16 * kMainStride + mt * 64;
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(p));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(p + 2 * kMainStride));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vbuf[kVa];
+#pragma unroll
+      for (int i = 0; i < kVa; ++i) vbuf[i] = read_v(i);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const bf16x8 va = vbuf[i % kVa];
+        if (i + kVa < 32) vbuf[i % kVa] = read_v(i + kVa);
+        mfma_o(o[i & 15], va, pf[i >> 4]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto key0_of = [&](int ps) { return (cj + (ps >> 1)) * kPage + (ps & 1) * kHalfRows; };
+    auto has_keys = [&](int ps) {
+      const int k0 = key0_of(ps);
+      return SPARSE ? (k0 < a.topk) : (k0 < Lb);
+    };
+    // Online softmax of one tile (log2 domain) in kSmSlices slices, so that
+    // it can be spread between the MFMAs of the next tile's S^T.  Register i
+    // of the S^T accumulator holds key key0 + key_of_row(8*(i/4) + i%4) + half.
+    //   0..3  scale, mask, max of registers 4k..4k+3
+    //   4     row max over the lane pair
+    //   5     lazy rescale decision
+    //   6..9  p = exp2(s - m), P^T fragments, row sum of registers 4(k-6)..
+    //   10    running sum
+    struct SmState {
+      float mx, alpha, mref, psum;
+      uint32_t any_need;
+      bf16x8 pf[2];
+    };
+    auto sm_slice = [&](int k, f32x16& sc, SmState& st, int key0, int st_step) {
+      if (k < 4) {
+        if (k == 0) st.mx = -INFINITY;
+        if constexpr (SPARSE) {
+          const int32_t* ids = ids_slot(st_step);
+          const int nvalid = row_ok ? min(kHalfRows, a.topk - key0) : 0;
+#pragma unroll
+          for (int i = 4 * k; i < 4 * k + 4; ++i) {
+            const int kk = key_of_row(8 * (i >> 2) + (i & 3)) + half;
+            float v = sc[i] * a.scale_log2;
+            v = (kk < nvalid && ids[kk] >= 0) ? v : -INFINITY;
+            sc[i] = v;
+            st.mx = fmaxf(st.mx, v);
+          }
+        } else {
+          const int lim = vis_end - key0;  // keys < lim are visible
+#pragma unroll
+          for (int i = 4 * k; i < 4 * k + 4; ++i) {
+            const int kk = key_of_row(8 * (i >> 2) + (i & 3)) + half;
+            float v = sc[i] * a.scale_log2;
+            v = kk < lim ? v : -INFINITY;
+            sc[i] = v;
+            st.mx = fmaxf(st.mx, v);
+          }
+        }
+      } else if (k == 4) {
+        st.mx = row_max2(st.mx);
+      } else if (k == 5) {
+        const bool need = st.mx > m_used + kRescaleThreshold;
+        st.any_need = uni((int)(__builtin_amdgcn_ballot_w64(need) != 0));
+        st.alpha = need ? exp2f(m_used - st.mx) : 1.0f;  // exp2(-inf) = 0
+        if (need) m_used = st.mx;
+        st.mref = m_used == -INFINITY ? 0.f : m_used;
+        st.psum = 0.f;
+      } else if (k < 10) {
+#pragma unroll
+        for (int i = 4 * (k - 6); i < 4 * (k - 6) + 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(sc[i] - st.mref);
+          st.psum += p;
+          st.pf[i >> 3][i & 7] = (__bf16)p;
+        }
+      } else {
+        lsum = lsum * st.alpha + st.psum;
+      }
+    };
+    constexpr int kSmSlices = 11;
+    // k-step of the next tile's S^T after whose MFMA slice k runs
+    auto slice_at = [](int k) { return k < 6 ? 2 * k : 12 + 3 * (k - 6); };
+    // Rare: the running max moved by more than the threshold; scale O.
+    auto rescale_o = [&](const SmState& st) {
+      if (__builtin_expect(st.any_need != 0, 0)) {
+        o_settle(o);
+#pragma unroll
+        for (int mt = 0; mt < 16; ++mt) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[mt][i] *= st.alpha;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        o_settle(o);
+      }
+    };
+
+    if constexpr (KVF == kKvBf16) {
+      // ---- bf16: step ps computes S^T of tile ps+1 with the softmax of tile
+      // ps woven between its MFMAs, then O += P V of tile ps.  Tiles ps and
+      // ps+1 are resident; tile ps+2 loads into the third ring slot.
+      const int n = 2 * (piece_end - cj);
+      f32x16 sc_cur, sc_nxt;
+      bool cur_has = has_keys(0);
+      if (cur_has) qk(tile_off(step), sc_cur, [](int) {});
+      for (int ps = 0; ps < n; ++ps, ++step) {
+        const bool has_next = ps + 1 < n;
+        const bool nxt_has = has_next && has_keys(ps + 1);
+        wait_vmcnt<0>();  // tile ps+1 (issued a step ago) and the walker's prefetch landed
+        land();
+        lds_barrier();    // ... for every wave; tile ps-1's slot is free
+        issue_next(step);
+        SmState st;
+        const int key0 = key0_of(ps);
+        if (nxt_has) {
+          qk(tile_off(step + 1), sc_nxt, [&](int ks) {
+#pragma unroll
+            for (int k = 0; k < kSmSlices; ++k)
+              if (ks == slice_at(k)) sm_slice(k, sc_cur, st, key0, step);
+          });
+        } else {
+#pragma unroll
+          for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc_cur, st, key0, step);
+        }
+        if (cur_has) {
+          rescale_o(st);
+          valu_to_mfma_settle(st.pf[0], st.pf[1]);
+          pv(tile_off(step), st.pf);
+        }
+        sc_cur = sc_nxt;
+        cur_has = nxt_has;
+      }
+    } else {
+      // ---- FP8: one bf16 tile, dequantised from the raw ring each step
+      issue_next(step);
+      for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
         if (ps > 0) {
           // This step's loads were issued two steps ago; the previous step
           // then issued the loads of step+1 (if any) and, sparse, the ids of
@@ -752,144 +1008,17 @@ k_decode(DecodeArgs a) {
           lds_barrier();  // every wave's loads of this step landed; slot (step+2)%3 is free
           issue_next(step);
         }
-
-        const uint8_t* tile;
-        if constexpr (KVF == kKvBf16) {
-          tile = smem + Lay::kTileOff + (step % kRing) * kHalfBytes;
-        } else {
-          tile = smem + Lay::kTileOff;
-          dequant_half(smem + Lay::kTileOff, smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
-          lds_barrier();
-        }
-        const int key0 = cjs * kPage + h * kHalfRows;  // first key of this step
-        const bool any_key = SPARSE ? (key0 < a.topk) : (key0 < Lb);
-        if (any_key) {
-          // ---- lane-constant LDS offsets for this step (opaque bases; the
-          // rest are DS immediates).  K rows = keys (A operand of S^T = K Q^T),
-          // chunk 2*ks + half; V^T via transposed reads: lane supplies key
-          // 16*kk + 4*half + (lane&15)/4 (+8 for k-slots 4..7) and dims
-          // 32*mt + 16*((lane>>4)&1) + 4*(lane&3).
-          const int tb = (int)(tile - smem);
-          const int mkey = key_of_row(r32);  // key of this lane's S^T row
-          const int koff = opaque(tb + mkey * kMainStride + 16 * half);
-          const int kroff = tb + kRopeOff + mkey * kRopeStride;
-          const int kfr = (mkey >> 1) & 7;
-          int qoff[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            qoff[e] = opaque((int)(qlds - smem) + r32 * kQLdsRowBytes + ((((2 * e) | half) ^ x) << 4));
-          // V^T (transposed reads): this lane supplies key row
-          // key_of_row(16kq + 8hi + 4half + j) = 16kq + 4j + 2hi + half,
-          // j = (lane & 15) >> 2, and dims 32mt + 16*((lane >> 4) & 1) + 4*(lane & 3)
-          const int voff = opaque(tb + (4 * ((lane & 15) >> 2) + half) * kMainStride +
-                                  32 * ((lane >> 4) & 1) + 8 * (lane & 3));
-
-          // ---- S^T for these 32 keys (rows = lanes), VGPR accumulator
-          // software pipelined: the LDS operands of k-step ks+kLa are read
-          // before the MFMA of k-step ks (order fixed by scheduling fences)
-          constexpr int kLa = 4;
-          auto read_k = [&](int ks) {
-            if (ks < 32) return *reinterpret_cast<const bf16x8*>(smem + koff + 32 * ks);
-            return *reinterpret_cast<const bf16x8*>(smem + kroff + ((((2 * (ks - 32)) | half) ^ kfr) << 4));
-          };
-          auto read_q = [&](int ks) {
-            return *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegSteps) & 3] +
-                                                    ((ks - kQRegSteps) >> 2) * 128);
-          };
+        dequant_half(smem + Lay::kTileOff, smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
+        lds_barrier();
+        if (has_keys(ps)) {
           f32x16 sc;
-          bf16x8 kbuf[kLa], qbuf[kLa];
+          SmState st;
+          qk(tile_off(step), sc, [](int) {});
 #pragma unroll
-          for (int i = 0; i < kLa; ++i) kbuf[i] = read_k(i);
-#pragma unroll
-          for (int ks = 0; ks < 36; ++ks) {
-            const bf16x8 ka = kbuf[ks % kLa];
-            const bf16x8 qb = ks < kQRegSteps ? qf[ks] : qbuf[ks % kLa];
-            if (ks + kLa < 36) {
-              kbuf[ks % kLa] = read_k(ks + kLa);
-              if (ks + kLa >= kQRegSteps) qbuf[ks % kLa] = read_q(ks + kLa);
-            }
-            if (ks == 0) mfma_s_first(sc, ka, qb);
-            else mfma_s_acc(sc, ka, qb);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          mfma_s_settle(sc);
-
-          // ---- mask + online softmax (log2 domain); register i holds key
-          // key0 + 8*(i/4) + 4*half + i%4
-          float mx = -INFINITY;
-          if constexpr (SPARSE) {
-            const int32_t* ids = ids_slot(step);
-            const int nvalid = row_ok ? min(kHalfRows, a.topk - key0) : 0;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int k = key_of_row(8 * (i >> 2) + (i & 3)) + half;
-              float v = sc[i] * a.scale_log2;
-              v = (k < nvalid && ids[k] >= 0) ? v : -INFINITY;
-              sc[i] = v;
-              mx = fmaxf(mx, v);
-            }
-          } else {
-            const int lim = vis_end - key0;  // keys < lim visible in this step
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int k = key_of_row(8 * (i >> 2) + (i & 3)) + half;
-              float v = sc[i] * a.scale_log2;
-              v = k < lim ? v : -INFINITY;
-              sc[i] = v;
-              mx = fmaxf(mx, v);
-            }
-          }
-          mx = fmaxf(mx, wave_bcast_partner(mx));
-          const bool need = mx > m_used + kRescaleThreshold;
-          // Rare: the running max moved by more than the threshold; scale O.
-          const uint32_t any_need = uni((int)(__builtin_amdgcn_ballot_w64(need) != 0));
-          const float alpha = need ? exp2f(m_used - mx) : 1.0f;  // exp2(-inf) = 0
-          if (__builtin_expect(any_need != 0, 0)) {
-            o_settle(o);
-#pragma unroll
-            for (int mt = 0; mt < 16; ++mt) {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) o[mt][i] *= alpha;
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            o_settle(o);
-          }
-          if (need) m_used = mx;
-          lsum *= alpha;
-          const float mref = m_used == -INFINITY ? 0.f : m_used;
-          bf16x8 pf[2];
-          float ps = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(sc[i] - mref);
-            ps += pv;
-            pf[i >> 3][i & 7] = (__bf16)pv;
-          }
-          lsum += ps;
-          valu_to_mfma_settle(pf[0], pf[1]);
-
-          // ---- O^T += V^T P^T over these 32 keys (2 k-steps x 16 d-tiles)
-          // 32 MFMAs, each fed by two transposed reads issued kVa MFMAs ahead
-          constexpr int kVa = 3;
-          auto read_v = [&](int i) {  // i = kq * 16 + mt
-            const int kq = i >> 4, mt = i & 15;
-            const uint8_t* p = smem + voff + kq * 16 * kMainStride + mt * 64;
-            const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(p));
-            const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(p + 2 * kMainStride));
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          };
-          bf16x8 vbuf[kVa];
-#pragma unroll
-          for (int i = 0; i < kVa; ++i) vbuf[i] = read_v(i);
-#pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            const bf16x8 va = vbuf[i % kVa];
-            if (i + kVa < 32) vbuf[i % kVa] = read_v(i + kVa);
-            mfma_o(o[i & 15], va, pf[i >> 4]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc, st, key0_of(ps), step);
+          rescale_o(st);
+          valu_to_mfma_settle(st.pf[0], st.pf[1]);
+          pv(tile_off(step), st.pf);
         }
       }
     }
@@ -897,7 +1026,7 @@ k_decode(DecodeArgs a) {
     // ======== finalize the piece: O / l and LSE; direct output or partial
     o_settle(o);
     {
-      const float lt = lsum + wave_bcast_partner(lsum);
+      const float lt = row_sum2(lsum);
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
       const float lse2 = lt > 0.f ? m_used + __builtin_amdgcn_logf(lt) : -INFINITY;
       const int nsplit = uni(sload(a.num_splits, cb + 1) - sload(a.num_splits, cb));
@@ -945,7 +1074,7 @@ k_decode(DecodeArgs a) {
           for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[mt][i]));
-          amax = fmaxf(amax, wave_bcast_partner(amax));
+          amax = row_max2(amax);
           const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
           const float rs = amax > 0.f ? 448.0f / amax : 1.0f;
           if (row_ok) {
@@ -969,17 +1098,21 @@ k_decode(DecodeArgs a) {
           }
         }
       } else {
-        // partial of split `split_k` of sequence cb, row group g, stored in
-        // register order: [wave][d-tile][quad][lane][4]
+        // partial of split `split_k` of sequence cb, row group g: O/l rounded
+        // to bf16, stored in register order [wave][d-tile][quad pair][lane][8]
         const int64_t pidx = (int64_t)uni(sload(a.num_splits, cb) + split_k) * a.groups + g;
-        float* po = a.part_o + pidx * kPartialOFloats + (size_t)wave * (16 * 4 * 64 * 4);
+        uint16_t* po = a.part_o + pidx * kPartialOElems + (size_t)wave * (16 * 2 * 64 * 8);
 #pragma unroll
         for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const f32x4 v = {o[mt][4 * qd] * inv, o[mt][4 * qd + 1] * inv, o[mt][4 * qd + 2] * inv,
-                             o[mt][4 * qd + 3] * inv};
-            *reinterpret_cast<f32x4*>(po + ((mt * 4 + qd) * 64 + lane) * 4) = v;
+          for (int q2 = 0; q2 < 2; ++q2) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const __bf16 lo = (__bf16)(o[mt][8 * q2 + 2 * e] * inv), hi = (__bf16)(o[mt][8 * q2 + 2 * e + 1] * inv);
+              w[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            }
+            *reinterpret_cast<uint4*>(po + ((mt * 2 + q2) * 64 + lane) * 8) = make_uint4(w[0], w[1], w[2], w[3]);
           }
         if (half == 0) a.part_lse[pidx * kPartialLseFloats + wave * 32 + r32] = lse2 * kLn2;
       }
@@ -1020,6 +1153,8 @@ __global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
       tot += l == -INFINITY ? 0.f : expf(l - m);
     }
   const float lse = m == -INFINITY ? -INFINITY : m + logf(tot);
+  // thread (sub, lane) owns d-tiles 4*sub .. 4*sub+3 of its row: acc[4*i + qd]
+  // holds quad qd of d-tile 4*sub + i (8 stored quad pairs)
   f32x4 acc[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) acc[k] = f32x4{};
@@ -1029,12 +1164,21 @@ __global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
       const float l = a.part_lse[pidx * kPartialLseFloats + wt * 32 + r32];
       if (l == -INFINITY) continue;  // lane-divergent skip is fine: loads below are per lane
       const float w = expf(l - lse);
-      const float* po = a.part_o + pidx * kPartialOFloats + (size_t)wt * (16 * 4 * 64 * 4);
+      const uint16_t* po = a.part_o + pidx * kPartialOElems + (size_t)wt * (16 * 2 * 64 * 8);
+      uint4 v[8];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int e = sub * 16 + k;  // (mt, qd) = (e / 4, e % 4)
-        f32x4 v = *reinterpret_cast<const f32x4*>(po + (e * 64 + lane) * 4);
-        acc[k] += w * v;
+      for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const uint4*>(po + ((sub * 8 + k) * 64 + lane) * 8);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t u[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        // load k = (d-tile 4*sub + k/2, quad pair k%2); u[e] holds elements
+        // 2e, 2e+1 of the pair, i.e. quad 2*(k%2) + e/2, lanes (2e)%4, (2e+1)%4
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f32x4& t = acc[4 * (k >> 1) + 2 * (k & 1) + (e >> 1)];
+          t[(2 * e) & 3] += w * __uint_as_float(u[e] << 16);
+          t[(2 * e + 1) & 3] += w * __uint_as_float(u[e] & 0xffff0000u);
+        }
       }
     }
   }
@@ -1079,7 +1223,7 @@ __global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
     for (int k = 0; k < 16; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(acc[k][e]));
-    amax = fmaxf(amax, wave_bcast_partner(amax));
+    amax = row_max2(amax);
     amax_s[sub][lane] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(amax_s[0][lane], amax_s[1][lane]), fmaxf(amax_s[2][lane], amax_s[3][lane]));
@@ -1162,24 +1306,29 @@ hipError_t launch_sched(const int32_t* seqlens, int batch, int rows, int topk, i
 }
 
 template <int KVF, bool SPARSE, bool FUSED>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
+                                  hipEvent_t stop) {
   const int grid = a.num_slots * a.groups;
-  hipLaunchKernelGGL((k_decode<KVF, SPARSE, FUSED>), dim3(grid), dim3(kThreads), 0, stream, a);
+  if (start || stop)
+    hipExtLaunchKernelGGL((k_decode<KVF, SPARSE, FUSED>), dim3(grid), dim3(kThreads), 0, stream, start,
+                          stop, 0, a);
+  else
+    hipLaunchKernelGGL((k_decode<KVF, SPARSE, FUSED>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool fused,
-                         hipStream_t stream) {
+                         hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (kv_format == kKvBf16) {
-    if (!sparse) return fused ? launch_decode_t<kKvBf16, false, true>(a, stream)
-                              : launch_decode_t<kKvBf16, false, false>(a, stream);
-    return fused ? launch_decode_t<kKvBf16, true, true>(a, stream)
-                 : launch_decode_t<kKvBf16, true, false>(a, stream);
+    if (!sparse) return fused ? launch_decode_t<kKvBf16, false, true>(a, stream, start, stop)
+                              : launch_decode_t<kKvBf16, false, false>(a, stream, start, stop);
+    return fused ? launch_decode_t<kKvBf16, true, true>(a, stream, start, stop)
+                 : launch_decode_t<kKvBf16, true, false>(a, stream, start, stop);
   }
-  if (!sparse) return fused ? launch_decode_t<kKvFp8V32, false, true>(a, stream)
-                            : launch_decode_t<kKvFp8V32, false, false>(a, stream);
-  return fused ? launch_decode_t<kKvFp8V32, true, true>(a, stream)
-               : launch_decode_t<kKvFp8V32, true, false>(a, stream);
+  if (!sparse) return fused ? launch_decode_t<kKvFp8V32, false, true>(a, stream, start, stop)
+                            : launch_decode_t<kKvFp8V32, false, false>(a, stream, start, stop);
+  return fused ? launch_decode_t<kKvFp8V32, true, true>(a, stream, start, stop)
+               : launch_decode_t<kKvFp8V32, true, false>(a, stream, start, stop);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, bool fused, hipStream_t stream) {

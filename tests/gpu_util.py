@@ -80,6 +80,9 @@ def check_o_lse(o, lse, ref_o, ref_lse, what=""):
         assert le <= LSE_MAX_ABS, f"{what}: LSE max-abs {le:.3e}"
     if empty.any():
         assert np.all(o[empty] == 0), f"{what}: empty rows must be exactly 0"
+    le = float(np.abs(lse[~empty] - ref_lse[~empty]).max()) if (~empty).any() else 0.0
+    say(f"{what}: O max-abs {max_abs:.2e} (bar {O_MAX_ABS:.0e}), rel-RMS {rel:.2e} (bar {O_REL_RMS:.0e}), "
+        f"LSE max-abs {le:.2e} (bar {LSE_MAX_ABS:.0e})")
     return max_abs, rel
 
 
@@ -118,4 +121,5 @@ def check_fp8(codes, scale, ref_o, ref_scale, what=""):
     nz = ref_scale > 0
     top = (np.asarray(codes) & 0x7F).max(axis=-1)
     assert np.all(top[np.abs(ref_o).max(axis=-1) > 0] == 0x7E), f"{what}: row max does not encode as 448"
+    say(f"{what}: FP8 distance max {max_e:.2e} (bar {O_MAX_ABS:.0e}), rel-RMS {rel:.2e} (bar {O_REL_RMS:.0e})")
     return max_e, rel

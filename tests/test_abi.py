@@ -31,8 +31,8 @@ def test_size_queries():
     assert lib.mla_sched_meta_ints(256) == 2048
     assert lib.mla_num_splits_ints(64) == 65
     # (batch + slots) partials x row groups x (128*512 + 128) fp32
-    assert lib.mla_workspace_bytes(64, 1, 128, 256) == 320 * (128 * 512 + 128) * 4
-    assert lib.mla_workspace_bytes(128, 2, 128, 128) == 256 * 2 * (128 * 512 + 128) * 4
+    assert lib.mla_workspace_bytes(64, 1, 128, 256) == 320 * (128 * 512 * 2 + 128 * 4)
+    assert lib.mla_workspace_bytes(128, 2, 128, 128) == 256 * 2 * (128 * 512 * 2 + 128 * 4)
     assert lib.mla_workspace_bytes(-1, 1, 128, 256) == 0
     assert lib.mla_status_string(3) == b"MLA_ERR_WORKSPACE"
 

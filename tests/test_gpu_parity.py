@@ -218,3 +218,46 @@ def test_full_config4_sampled():
     pad = [int(b) for b in range(p.batch) if (p.indices[b, 0] < 0).any()][:3]
     rows += [(b, 0, 5) for b in pad]
     _sampled(p, rows, "config4")
+
+
+@gpu
+def test_decode_timed_matches_decode():
+    """mla_decode_timed writes what mla_decode writes and records the
+    decode kernel's start/end events."""
+    torch = _torch_cuda()
+    import ctypes
+    from mla_paged_kv_05_amd import binding as B
+
+    p = W.make_dense("timed", [300, 1000, 64, 5], s_q=1, h_q=128, seed=21)
+    t = upload(p)
+    lib = B.load_library()
+    S = 16
+    meta = torch.empty((S, 8), dtype=torch.int32, device="cuda:0")
+    ns = torch.empty(p.batch + 1, dtype=torch.int32, device="cuda:0")
+    sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.mla_get_metadata(ctypes.c_void_p(t["seqlens"].data_ptr()), p.batch, 128, 1, 0, S,
+                                ctypes.c_void_p(meta.data_ptr()), ctypes.c_void_p(ns.data_ptr()), sh) == 0
+    ws = torch.empty(B.workspace_bytes(p.batch, 1, 128, S), dtype=torch.uint8, device="cuda:0")
+    outs = []
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
+    assert hip.hipEventCreate(ctypes.byref(e0)) == 0 and hip.hipEventCreate(ctypes.byref(e1)) == 0
+    for timed in (False, True):
+        out = torch.empty((p.batch, 1, 128, 512), dtype=torch.bfloat16, device="cuda:0")
+        lse = torch.empty((p.batch, 1, 128), dtype=torch.float32, device="cuda:0")
+        pr = B._params(t["q"], t["kv"], t["block_table"], t["seqlens"], meta, ns, False, None, p.scale,
+                       "bf16", ws, out, lse, None)
+        say(f"decode_timed timed={timed}")
+        st = lib.mla_decode_timed(ctypes.byref(pr), sh, e0, e1) if timed else lib.mla_decode(ctypes.byref(pr), sh)
+        assert st == 0, lib.mla_last_error()
+        torch.cuda.synchronize()
+        outs.append((out.view(torch.int16).cpu().numpy(), lse.cpu().numpy()))
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1) == 0
+    hip.hipEventDestroy(e0)
+    hip.hipEventDestroy(e1)
+    assert 0.0 < ms.value < 1000.0
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
