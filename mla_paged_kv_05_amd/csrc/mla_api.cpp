@@ -8,6 +8,7 @@
 
 #include <cstdarg>
 #include <cstdint>
+#include <cmath>
 #include <cstdio>
 #include <mutex>
 #include <string>
@@ -173,6 +174,8 @@ static mla_status build_args(const mla_decode_params* p, mla::DecodeArgs& a, boo
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   a.norm_eps = p->norm_eps;
   a.rope_base = p->rope_base;
+  if (p->fused)
+    for (int i = 0; i < 32; ++i) a.rope_inv_freq[i] = std::pow((double)p->rope_base, -2.0 * i / 64.0);
   return MLA_OK;
 }
 

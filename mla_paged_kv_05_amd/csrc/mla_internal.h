@@ -50,6 +50,7 @@ struct DecodeArgs {
   int batch, s_q, h_q, rows, groups, max_blocks, topk, causal, num_slots;
   float scale_log2;          // softmax_scale * log2(e)
   float norm_eps, rope_base;
+  double rope_inv_freq[32];  // fused only: rope_base^(-2i/64), computed on the host in fp64
 };
 
 enum KvFormat { kKvBf16 = 0, kKvFp8V32 = 1 };

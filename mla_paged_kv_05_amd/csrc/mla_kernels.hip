@@ -117,6 +117,13 @@ __device__ __forceinline__ int opaque(int v) {
   asm volatile("" : "+v"(v));
   return v;
 }
+// This lane's index, recomputed (mbcnt) where it is used, so per-lane LDS
+// address bases live only inside a step, never across the KV loop: there the
+// allocator may spill them, and each reload of a spill would cost a full
+// vmcnt wait in a loop that keeps KV loads in flight.
+__device__ __forceinline__ int fresh_lane() {
+  return opaque(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+}
 
 // S^T = K Q^T step on v_mfma_f32_32x32x16_bf16 with the accumulator held in
 // VGPRs.  Written as inline asm because the builtin lets the compiler move
@@ -391,7 +398,7 @@ __device__ __forceinline__ void dma_glb16_s(uint32_t lds, int voff, const void* 
 // 8w..8w+7 (one load).
 __device__ __forceinline__ void load_half_bf16_dense(uint8_t* slot, const uint8_t* kv, int64_t phys,
                                                      int valid, int h, int wave, int lane) {
-  const int l16 = opaque(lane << 4);
+  const int l16 = fresh_lane() << 4;
   const uint8_t* page = kv + phys * (int64_t)kTileBytes;
   const i32x4 rs = make_rsrc(page, valid * kRowBytes);
   const uint32_t base = lds_off(slot);
@@ -410,7 +417,7 @@ __device__ __forceinline__ void load_half_bf16_dense(uint8_t* slot, const uint8_
 __device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8_t* kv,
                                                       const int32_t* ids, int nvalid, int wave,
                                                       int lane) {
-  const int l16 = opaque(lane << 4);
+  const int l16 = fresh_lane() << 4;
   const uint32_t base = lds_off(slot);
 #pragma unroll
   for (int k = 0; k < kHalfRows / kWaves; ++k) {
@@ -510,15 +517,31 @@ __device__ __forceinline__ void fetch_ids_dma(int32_t* ids_lds, const int32_t* i
 }
 
 // ---------------------------------------------------------------------------
-// Fused prologue / epilogue helpers.  RoPE angles are formed and reduced in
-// fp64 (positions reach 10^4 radians) before an fp32 sincos.
+// Fused prologue / epilogue helpers.  The RoPE angle of pair i at position
+// pos is theta = pos * base^(-2i/64) (the inverse frequencies come from the
+// host in fp64); it is formed and reduced to [-pi, pi] in fp64, since
+// positions reach 10^4 radians, then sin and cos come from Taylor series in
+// fp64 on the quarter-turn-reduced angle |r| <= pi/4 (truncation below 3e-14)
+// and are rounded once to fp32.  Light on registers, unlike a general
+// sincosf with its large-argument path.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void rope_cs(double pos, int pair, float base, float sign, float& c,
-                                        float& s) {
-  // theta = pos * base^(-2*pair/64)
-  double th = sign * pos * exp2(-(double)(2 * pair) / 64.0 * log2((double)base));
-  double red = th - 6.283185307179586 * rint(th / 6.283185307179586);
-  sincosf((float)red, &s, &c);
+__device__ __forceinline__ void sincos_reduced(double x, float& s, float& c) {
+  const double q = rint(x * 0.63661977236758138);                          // x / (pi/2)
+  const double r = (x - q * 1.5707963267948966) - q * 6.123233995736766e-17;  // pi/2 as hi + lo
+  const double r2 = r * r;
+  const double sp = r * (1.0 + r2 * (-1.0 / 6 + r2 * (1.0 / 120 + r2 * (-1.0 / 5040 + r2 * (1.0 / 362880 +
+                    r2 * (-1.0 / 39916800 + r2 * (1.0 / 6227020800.0)))))));
+  const double cp = 1.0 + r2 * (-0.5 + r2 * (1.0 / 24 + r2 * (-1.0 / 720 + r2 * (1.0 / 40320 +
+                    r2 * (-1.0 / 3628800 + r2 * (1.0 / 479001600.0 + r2 * (-1.0 / 87178291200.0)))))));
+  const int qi = (int)q & 3;  // x = r + qi * pi/2 (mod 2 pi)
+  const double ss = qi == 0 ? sp : qi == 1 ? cp : qi == 2 ? -sp : -cp;
+  const double cc = qi == 0 ? cp : qi == 1 ? -sp : qi == 2 ? -cp : sp;
+  s = (float)ss;
+  c = (float)cc;
+}
+__device__ __forceinline__ void rope_cs(double pos, double inv_freq, float sign, float& c, float& s) {
+  const double th = (double)sign * pos * inv_freq;
+  sincos_reduced(th - 6.283185307179586 * rint(th * 0.15915494309189535), s, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -542,7 +565,8 @@ struct DecodeLayout {
   static constexpr int kRawOff = kTiles * kHalfBytes;                  // fp8 raw slots
   static constexpr int kQOff = kRawOff + (KVF == kKvBf16 ? 0 : kRing * kRawSlotBytes);
   static constexpr int kIdsOff = kQOff + kWaves * kQLdsWaveBytes;
-  static constexpr int kSmem = kIdsOff + (SPARSE ? kIdsSlots * 256 : 0);
+  static constexpr int kWalkOff = kIdsOff + (SPARSE ? kIdsSlots * 256 : 0);  // 2 words per wave
+  static constexpr int kSmem = kWalkOff + (KVF == kKvBf16 && !SPARSE ? kWaves * 8 : 0);
   // per-step VMEM instructions issued by every wave (loads + id fetch)
   static constexpr int kVmPerStep =
       (KVF == kKvBf16 ? kLoadsPerHalf : kRawLoadsPerWave) + (SPARSE ? 1 : 0);
@@ -616,44 +640,42 @@ k_decode(DecodeArgs a) {
   // Load walker: (lb, lj, lh) is the next step to stage, lL and lend the
   // length and item count of sequence lb, lphys the physical block of item
   // (lb, lj).  On the bf16 dense path the block of a new item and the length
-  // of the next sequence are fetched by vector loads a step before they are
-  // needed and copied to scalars by land() right after the step-start
-  // vmcnt(0) wait.  (Scalar loads in flight would turn every LDS-operand wait
-  // of the MFMA loops into a full lgkmcnt(0) drain; a compiler-inserted wait
-  // on the vector loads elsewhere would also wait for the KV loads, which it
-  // cannot see.)  The FP8 path, whose waits keep a step of KV loads in
-  // flight, reads them with scalar loads when it needs them.
+  // of the next sequence are fetched a step before they are needed, by
+  // one-lane LDS-DMA loads into two words of the wave's own, and read back by
+  // land() after the step-start vmcnt(0) wait and barrier.  Neither scalar
+  // loads (an SMEM load in flight turns every LDS-operand wait of the MFMA
+  // loops into a full lgkmcnt(0) drain) nor vector loads into VGPRs (a
+  // compiler wait on them, or on a spill of their register, also waits for
+  // the KV loads it cannot see) would do.  The FP8 path, whose waits keep a
+  // step of KV loads in flight, uses scalar loads when it needs the values.
   constexpr bool kVecWalk = KVF == kKvBf16 && !SPARSE;
   int lb = b0, lj = j0, lh = 0;
   int lL = SPARSE ? 0 : uni(sload(a.seqlens, b0));
   int lend = item_end(b0);
   int lphys = 0, lnL = 0;
-  const __amdgpu_buffer_rsrc_t bt_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t*>(a.block_table), 0, kVecWalk ? (int)((int64_t)a.batch * a.max_blocks * 4) : 0,
-      (int)kBufferFlags);
-  const __amdgpu_buffer_rsrc_t sl_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t*>(a.seqlens), 0, kVecWalk ? a.batch * 4 : 0, (int)kBufferFlags);
-  // Offsets go in the scalar soffset field (always in range): a VGPR
-  // address would make the compiler wait for the load, and with it for the
-  // KV loads issued before it, before that VGPR is reused.
-  int phys_v = 0, nL_v = 0;  // vector copies in flight
   bool lany = false;
+  const int32_t* walk = reinterpret_cast<const int32_t*>(smem + Lay::kWalkOff) + 2 * wave;
+  const i32x4 bt_rs = make_rsrc(a.block_table, kVecWalk ? (uint32_t)((int64_t)a.batch * a.max_blocks * 4) : 0u);
+  const i32x4 sl_rs = make_rsrc(a.seqlens, kVecWalk ? (uint32_t)(a.batch * 4) : 0u);
+  auto fetch_word = [&](int w, const i32x4& rs, int byte_off) {
+    if (lane == 0) dma_buf4(lds_off(walk + w), byte_off, rs);
+  };
   auto fetch_phys = [&]() {
     const bool any = lb <= b1 && lj * kPage < lL;
     if constexpr (kVecWalk) {
       lany = any;
-      phys_v = __builtin_amdgcn_raw_buffer_load_b32(bt_rs, 0, any ? (lb * a.max_blocks + lj) * 4 : 0, 0);
+      if (any) fetch_word(0, bt_rs, (lb * a.max_blocks + lj) * 4);
     } else if constexpr (!SPARSE) {
       lphys = any ? uni(sload(a.block_table, (int64_t)lb * a.max_blocks + lj)) : 0;
     }
   };
   auto fetch_next_len = [&]() {
-    if constexpr (kVecWalk) nL_v = __builtin_amdgcn_raw_buffer_load_b32(sl_rs, 0, min(lb + 1, b1) * 4, 0);
+    if constexpr (kVecWalk) fetch_word(1, sl_rs, min(lb + 1, b1) * 4);
   };
   auto land = [&]() {
     if constexpr (kVecWalk) {
-      lphys = lany ? uni(phys_v) : 0;
-      lnL = uni(nL_v);
+      lphys = lany ? uni(walk[0]) : 0;
+      lnL = uni(walk[1]);
     }
   };
   auto advance_load = [&]() {
@@ -679,7 +701,11 @@ k_decode(DecodeArgs a) {
   };
   fetch_phys();
   fetch_next_len();
-  land();  // kernel start: nothing else is in flight yet
+  if constexpr (kVecWalk) {
+    __builtin_amdgcn_s_waitcnt(0);  // kernel start: nothing else is in flight yet
+    lds_barrier();
+  }
+  land();
   // stage the walker's step as step `step` into its ring slot
   auto issue_load = [&](int step) {
     const int rs = step % kRing;
@@ -756,47 +782,44 @@ k_decode(DecodeArgs a) {
     // for them does not wait for those
     wait_vmcnt<0>();
     lds_barrier();  // every wave's loads of the first step landed
+    // Query fragments of this piece.  Fused: q^ = inv * RoPE(q (.) w) with
+    // inv = 1 / sqrt(mean(q^2) + eps) (RMSNorm over the row's 576 dims, then
+    // RoPE on dims 512..575 at position len - s_q + t; RoPE is linear, so the
+    // row factor commutes with it).  The fragments hold bf16(RoPE(q (.) w))
+    // chunk by chunk and inv joins the row's softmax scale, applied to S in
+    // fp32; no chunk has to wait for the whole row's statistic.
+    float srow = a.scale_log2;  // log2(e) * softmax scale (* inv when fused)
     {
-          const uint16_t* qrow = a.q + ((int64_t)cb * a.rows + (row_ok ? row : 0)) * kDqk;
-      bf16x8 qraw[36];
+      const uint16_t* qrow = a.q + ((int64_t)cb * a.rows + (row_ok ? row : 0)) * kDqk;
+      float ss = 0.f;
+      const double pos = (double)Lb - (double)a.s_q + (double)tok;
 #pragma unroll
-      for (int ks = 0; ks < 36; ++ks)
-        qraw[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
-      if constexpr (FUSED) {
-        // RMSNorm over the row's 576 dims (lanes l and l^32 hold it), then
-        // RoPE on dims 512..575 at position len - s_q + t.
-        float ss = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) { float v = (float)qraw[ks][e]; ss += v * v; }
-        ss = row_sum2(ss);
-        const float inv = 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
-        const double pos = (double)Lb - (double)a.s_q + (double)tok;
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks) {
-          const int c = 2 * ks + half;
-          const bf16x8 wv = *reinterpret_cast<const bf16x8*>(a.norm_w + c * 8);
+      for (int ks = 0; ks < 36; ++ks) {
+        bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
+        if constexpr (FUSED) {
+          const bf16x8 wv = *reinterpret_cast<const bf16x8*>(a.norm_w + (2 * ks + half) * 8);
           float y[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = (float)qraw[ks][e] * (float)wv[e] * inv;
+          for (int e = 0; e < 8; ++e) {
+            const float qv = (float)v[e];
+            ss += qv * qv;
+            y[e] = qv * (float)wv[e];
+          }
           if (ks >= 32) {
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
               float cs, sn;
-              rope_cs(pos, (c * 8 - 512) / 2 + pp, a.rope_base, 1.0f, cs, sn);
+              rope_cs(pos, half ? a.rope_inv_freq[8 * (ks - 32) + 4 + pp] : a.rope_inv_freq[8 * (ks - 32) + pp],
+                      1.0f, cs, sn);
               const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
               y[2 * pp] = x0 * cs - x1 * sn;
               y[2 * pp + 1] = x0 * sn + x1 * cs;
             }
           }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qraw[ks][e] = (__bf16)y[e];
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)y[e];
         }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
-        const bf16x8 v = row_ok ? qraw[ks] : bf16x8{};
+        if (!row_ok) v = bf16x8{};
         if (ks < kQRegSteps) {
           qf[ks] = v;
         } else {
@@ -804,11 +827,13 @@ k_decode(DecodeArgs a) {
           *reinterpret_cast<bf16x8*>(qlds + r32 * kQLdsRowBytes + ((cq ^ x) << 4)) = v;
         }
       }
+      if constexpr (FUSED) {
+        ss = row_sum2(ss);
+        srow *= 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
+      }
     }
 
     // ======== building blocks of one 32-key step
-    const int mkey = key_of_row(r32);  // key held by this lane's S^T row
-    const int kfr = (mkey >> 1) & 7;
     auto tile_off = [&](int st) -> int {
       if constexpr (KVF == kKvBf16) return Lay::kTileOff + (st % kRing) * kHalfBytes;
       else return Lay::kTileOff;
@@ -817,16 +842,18 @@ k_decode(DecodeArgs a) {
     // LDS operands of k-step ks+kLa read before the MFMA of k-step ks (order
     // fixed by scheduling fences); hook(ks) runs after that MFMA is issued.
     auto qk = [&](int tb, f32x16& sc, auto&& hook) {
-      constexpr int kLa = 4;
-      const int koff = opaque(tb + mkey * kMainStride + 16 * half);
-      const int kroff = tb + kRopeOff + mkey * kRopeStride;
+      constexpr int kLa = FUSED ? 3 : 4;
+      const int ln = fresh_lane(), lr = ln & 31, lh = ln >> 5;
+      const int lkey = key_of_row(lr), lfr = (lkey >> 1) & 7, lx = (lr >> 1) & 7;
+      const int koff = tb + lkey * kMainStride + 16 * lh;
+      const int kroff = tb + kRopeOff + lkey * kRopeStride;
+      const int qb = Lay::kQOff + wave * kQLdsWaveBytes + lr * kQLdsRowBytes;
       int qoff[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qoff[e] = opaque((int)(qlds - smem) + r32 * kQLdsRowBytes + ((((2 * e) | half) ^ x) << 4));
+      for (int e = 0; e < 4; ++e) qoff[e] = qb + ((((2 * e) | lh) ^ lx) << 4);
       auto read_k = [&](int ks) {
         if (ks < 32) return *reinterpret_cast<const bf16x8*>(smem + koff + 32 * ks);
-        return *reinterpret_cast<const bf16x8*>(smem + kroff + ((((2 * (ks - 32)) | half) ^ kfr) << 4));
+        return *reinterpret_cast<const bf16x8*>(smem + kroff + ((((2 * (ks - 32)) | lh) ^ lfr) << 4));
       };
       auto read_q = [&](int ks) {
         return *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegSteps) & 3] +
@@ -856,8 +883,8 @@ k_decode(DecodeArgs a) {
     // half (j = (lane & 15) >> 2) and dims 32mt + 16*((lane >> 4) & 1) + 4*(lane & 3).
     auto pv = [&](int tb, const bf16x8 (&pf)[2]) {
       constexpr int kVa = 3;
-      const int voff = opaque(tb + (4 * ((lane & 15) >> 2) + half) * kMainStride +
-                              32 * ((lane >> 4) & 1) + 8 * (lane & 3));
+      const int ln = fresh_lane();
+      const int voff = tb + (4 * ((ln & 15) >> 2) + (ln >> 5)) * kMainStride + 32 * ((ln >> 4) & 1) + 8 * (ln & 3);
       auto read_v = [&](int i) {  // i = kq * 16 + mt
         const int kq = i >> 4, mt = i & 15;
         const uint8_t* p = smem + voff + kq * 16 * kMainStride + mt * 64;
@@ -899,24 +926,26 @@ k_decode(DecodeArgs a) {
     auto sm_slice = [&](int k, f32x16& sc, SmState& st, int key0, int st_step) {
       if (k < 4) {
         if (k == 0) st.mx = -INFINITY;
+        // the key of register i is kc + half with kc a compile-time constant,
+        // so the lane's half is folded into the limits, not into 16 keys
         if constexpr (SPARSE) {
-          const int32_t* ids = ids_slot(st_step);
-          const int nvalid = row_ok ? min(kHalfRows, a.topk - key0) : 0;
+          const int32_t* ids_h = ids_slot(st_step) + half;
+          const int nvalid_h = (row_ok ? min(kHalfRows, a.topk - key0) : 0) - half;
 #pragma unroll
           for (int i = 4 * k; i < 4 * k + 4; ++i) {
-            const int kk = key_of_row(8 * (i >> 2) + (i & 3)) + half;
-            float v = sc[i] * a.scale_log2;
-            v = (kk < nvalid && ids[kk] >= 0) ? v : -INFINITY;
+            const int kc = key_of_row(8 * (i >> 2) + (i & 3));
+            float v = sc[i] * srow;
+            v = (kc < nvalid_h && ids_h[kc] >= 0) ? v : -INFINITY;
             sc[i] = v;
             st.mx = fmaxf(st.mx, v);
           }
         } else {
-          const int lim = vis_end - key0;  // keys < lim are visible
+          const int lim_h = vis_end - key0 - half;  // register i visible iff kc < lim_h
 #pragma unroll
           for (int i = 4 * k; i < 4 * k + 4; ++i) {
-            const int kk = key_of_row(8 * (i >> 2) + (i & 3)) + half;
-            float v = sc[i] * a.scale_log2;
-            v = kk < lim ? v : -INFINITY;
+            const int kc = key_of_row(8 * (i >> 2) + (i & 3));
+            float v = sc[i] * srow;
+            v = kc < lim_h ? v : -INFINITY;
             sc[i] = v;
             st.mx = fmaxf(st.mx, v);
           }
@@ -925,7 +954,8 @@ k_decode(DecodeArgs a) {
         st.mx = row_max2(st.mx);
       } else if (k == 5) {
         const bool need = st.mx > m_used + kRescaleThreshold;
-        st.any_need = uni((int)(__builtin_amdgcn_ballot_w64(need) != 0));
+        // O is still zero while m_used is -inf: nothing to scale
+        st.any_need = uni((int)(__builtin_amdgcn_ballot_w64(need && m_used != -INFINITY) != 0));
         st.alpha = need ? exp2f(m_used - st.mx) : 1.0f;  // exp2(-inf) = 0
         if (need) m_used = st.mx;
         st.mref = m_used == -INFINITY ? 0.f : m_used;
@@ -945,6 +975,11 @@ k_decode(DecodeArgs a) {
     // k-step of the next tile's S^T after whose MFMA slice k runs
     auto slice_at = [](int k) { return k < 6 ? 2 * k : 12 + 3 * (k - 6); };
     // Rare: the running max moved by more than the threshold; scale O.
+    // Rare: some row's running max moved by more than the threshold while O
+    // already held keys; scale O by alpha.  The branch ends with a full vmcnt
+    // wait of its own: the compiler may spill around the bulk AGPR traffic
+    // here, and without that wait the reloads would leave pending loads at
+    // the join that it then guards with full waits on the common path.
     auto rescale_o = [&](const SmState& st) {
       if (__builtin_expect(st.any_need != 0, 0)) {
         o_settle(o);
@@ -955,6 +990,7 @@ k_decode(DecodeArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
         o_settle(o);
+        wait_vmcnt<0>();
       }
     };
 
@@ -970,8 +1006,8 @@ k_decode(DecodeArgs a) {
         const bool has_next = ps + 1 < n;
         const bool nxt_has = has_next && has_keys(ps + 1);
         wait_vmcnt<0>();  // tile ps+1 (issued a step ago) and the walker's prefetch landed
-        land();
         lds_barrier();    // ... for every wave; tile ps-1's slot is free
+        land();
         issue_next(step);
         SmState st;
         const int key0 = key0_of(ps);
@@ -1050,47 +1086,62 @@ k_decode(DecodeArgs a) {
             if (half == 0) a.lse[orow] = lse2 * kLn2;
           }
         } else {
-          // conjugate RoPE on dims 448..511, amax over the row, e4m3 cast
+          // conjugate RoPE on dims 448..511 (d-tiles 14, 15), amax over the
+          // row, e4m3 cast.  Tile by tile from the accumulators: only the 32
+          // rotated values are held in VGPRs (scaling all of O at once would
+          // move the 256 accumulators into VGPRs).  amax(O/l) = amax(O)/l
+          // exactly, since scaling by a positive constant keeps the order.
           const double pos = (double)Lb - (double)a.s_q + (double)tok;
+          float rot[2][16];
 #pragma unroll
-          for (int mt = 0; mt < 16; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[mt][i] *= inv;
-#pragma unroll
-          for (int mt = 14; mt < 16; ++mt)
+          for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
               for (int pp = 0; pp < 2; ++pp) {
-                const int d = 32 * mt + 8 * qd + 4 * half + 2 * pp;
+                const int k0 = 16 * t + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * half
                 float cs, sn;
-                rope_cs(pos, (d - 448) / 2, a.rope_base, -1.0f, cs, sn);
-                const float x0 = o[mt][4 * qd + 2 * pp], x1 = o[mt][4 * qd + 2 * pp + 1];
-                o[mt][4 * qd + 2 * pp] = x0 * cs - x1 * sn;
-                o[mt][4 * qd + 2 * pp + 1] = x0 * sn + x1 * cs;
+                rope_cs(pos, half ? a.rope_inv_freq[k0 + 2] : a.rope_inv_freq[k0], -1.0f, cs, sn);
+                const float x0 = o[14 + t][4 * qd + 2 * pp] * inv, x1 = o[14 + t][4 * qd + 2 * pp + 1] * inv;
+                rot[t][4 * qd + 2 * pp] = x0 * cs - x1 * sn;
+                rot[t][4 * qd + 2 * pp + 1] = x0 * sn + x1 * cs;
               }
-          float amax = 0.f;
+          float am = 0.f;
 #pragma unroll
-          for (int mt = 0; mt < 16; ++mt)
+          for (int mt = 0; mt < 14; ++mt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[mt][i]));
+            for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(o[mt][i]));
+          float amax = am * inv;
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(rot[t][i]));
           amax = row_max2(amax);
           const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
           const float rs = amax > 0.f ? 448.0f / amax : 1.0f;
           if (row_ok) {
             uint8_t* op = reinterpret_cast<uint8_t*>(a.out) + orow * kDv;
+            auto put = [&](int mt, int qd, float v0, float v1, float v2, float v3) {
+              const int d = 32 * mt + 8 * qd + 4 * half;
+              v0 = fminf(fmaxf(v0 * rs, -448.f), 448.f);
+              v1 = fminf(fmaxf(v1 * rs, -448.f), 448.f);
+              v2 = fminf(fmaxf(v2 * rs, -448.f), 448.f);
+              v3 = fminf(fmaxf(v3 * rs, -448.f), 448.f);
+              int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+              pk = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, pk, true);
+              *reinterpret_cast<int*>(op + d) = pk;
+            };
 #pragma unroll
-            for (int mt = 0; mt < 16; ++mt)
+            for (int mt = 0; mt < 14; ++mt)
 #pragma unroll
-              for (int qd = 0; qd < 4; ++qd) {
-                const int d = 32 * mt + 8 * qd + 4 * half;
-                float v[4];
+              for (int qd = 0; qd < 4; ++qd)
+                put(mt, qd, o[mt][4 * qd] * inv, o[mt][4 * qd + 1] * inv, o[mt][4 * qd + 2] * inv,
+                    o[mt][4 * qd + 3] * inv);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(o[mt][4 * qd + e] * rs, -448.f), 448.f);
-                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-                pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], pk, true);
-                *reinterpret_cast<int*>(op + d) = pk;
-              }
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int qd = 0; qd < 4; ++qd)
+                put(14 + t, qd, rot[t][4 * qd], rot[t][4 * qd + 1], rot[t][4 * qd + 2], rot[t][4 * qd + 3]);
             if (half == 0) {
               a.lse[orow] = lse2 * kLn2;
               a.out_scale[orow] = sc;
@@ -1210,9 +1261,9 @@ __global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
       if (mt < 14) continue;
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
-        const int d = 32 * mt + 8 * qd + 4 * half + 2 * pp;
+        const int k0 = 16 * (mt - 14) + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * half
         float cs, sn;
-        rope_cs(pos, (d - 448) / 2, a.rope_base, -1.0f, cs, sn);
+        rope_cs(pos, half ? a.rope_inv_freq[k0 + 2] : a.rope_inv_freq[k0], -1.0f, cs, sn);
         const float x0 = acc[k][2 * pp], x1 = acc[k][2 * pp + 1];
         acc[k][2 * pp] = x0 * cs - x1 * sn;
         acc[k][2 * pp + 1] = x0 * sn + x1 * cs;
