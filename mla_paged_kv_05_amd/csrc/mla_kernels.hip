@@ -393,44 +393,53 @@ __device__ __forceinline__ void dma_glb16_s(uint32_t lds, int voff, const void* 
 
 // Dense bf16: half `h` of pool block `phys` whose first `valid` tokens are
 // real.  The buffer resource covers exactly those tokens, so the hardware
-// writes zeros for the others and never reads past the sequence.  Wave w
-// stages main rows w, w+4, ..., w+28 (one 1 KB load each) and rope rows
-// 8w..8w+7 (one load).
-__device__ __forceinline__ void load_half_bf16_dense(uint8_t* slot, const uint8_t* kv, int64_t phys,
-                                                     int valid, int h, int wave, int lane) {
+// writes zeros for the others and never reads past the sequence (valid = 0
+// writes a zero half).  A wave's 9 loads: k < 8 stages main row wave + 4k
+// (1 KB), k = 8 the rope rows 8*wave .. 8*wave+7.
+__device__ __forceinline__ void load_row_bf16_dense(uint8_t* slot, const uint8_t* kv, int64_t phys,
+                                                    int valid, int h, int wave, int k) {
   const int l16 = fresh_lane() << 4;
-  const uint8_t* page = kv + phys * (int64_t)kTileBytes;
-  const i32x4 rs = make_rsrc(page, valid * kRowBytes);
+  const i32x4 rs = make_rsrc(kv + phys * (int64_t)kTileBytes, valid * kRowBytes);
   const uint32_t base = lds_off(slot);
-#pragma unroll
-  for (int k = 0; k < kHalfRows / kWaves; ++k) {
+  if (k < kHalfRows / kWaves) {
     const int r = wave + kWaves * k;
     dma_buf16(base + r * kMainStride, (h * kHalfRows + r) * kRowBytes + l16, rs);
+  } else {
+    const int rr = 8 * wave + (l16 >> 7);
+    dma_buf16(base + kRopeOff + wave * 1024,
+              (h * kHalfRows + rr) * kRowBytes + 1024 + (rope_phys_chunk(rr, (l16 >> 4) & 7) << 4), rs);
   }
-  const int rr = 8 * wave + (l16 >> 7);
-  dma_buf16(base + kRopeOff + wave * 1024,
-            (h * kHalfRows + rr) * kRowBytes + 1024 + (rope_phys_chunk(rr, (l16 >> 4) & 7) << 4), rs);
+}
+__device__ __forceinline__ void load_half_bf16_dense(uint8_t* slot, const uint8_t* kv, int64_t phys,
+                                                     int valid, int h, int wave, int /*lane*/) {
+#pragma unroll
+  for (int k = 0; k < kLoadsPerHalf; ++k) load_row_bf16_dense(slot, kv, phys, valid, h, wave, k);
 }
 
 // Sparse bf16: row r is flat pool token ids[r] when r < nvalid and
-// ids[r] >= 0, else zeros.
-__device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8_t* kv,
-                                                      const int32_t* ids, int nvalid, int wave,
-                                                      int lane) {
+// ids[r] >= 0, else zeros.  Same 9 loads per wave as the dense loader.
+__device__ __forceinline__ void load_row_bf16_sparse(uint8_t* slot, const uint8_t* kv,
+                                                     const int32_t* ids, int nvalid, int wave, int k) {
   const int l16 = fresh_lane() << 4;
   const uint32_t base = lds_off(slot);
-#pragma unroll
-  for (int k = 0; k < kHalfRows / kWaves; ++k) {
+  if (k < kHalfRows / kWaves) {
     const int r = wave + kWaves * k;
     const int id = uni(r < nvalid ? ids[r] : -1);
     const uint8_t* src = id >= 0 ? kv + (int64_t)id * kRowBytes : g_zero_row;
     dma_glb16_s(base + r * kMainStride, l16, src);
+  } else {
+    const int rr = 8 * wave + (l16 >> 7);
+    const int id = rr < nvalid ? ids[rr] : -1;
+    const int cc = rope_phys_chunk(rr, (l16 >> 4) & 7);
+    const uint8_t* g = id >= 0 ? kv + (int64_t)id * kRowBytes + 1024 + cc * 16 : g_zero_row + 1024 + cc * 16;
+    dma_glb16(base + kRopeOff + wave * 1024, g);
   }
-  const int rr = 8 * wave + (l16 >> 7);
-  const int id = rr < nvalid ? ids[rr] : -1;
-  const int cc = rope_phys_chunk(rr, (l16 >> 4) & 7);
-  const uint8_t* g = id >= 0 ? kv + (int64_t)id * kRowBytes + 1024 + cc * 16 : g_zero_row + 1024 + cc * 16;
-  dma_glb16(base + kRopeOff + wave * 1024, g);
+}
+__device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8_t* kv,
+                                                      const int32_t* ids, int nvalid, int wave,
+                                                      int /*lane*/) {
+#pragma unroll
+  for (int k = 0; k < kLoadsPerHalf; ++k) load_row_bf16_sparse(slot, kv, ids, nvalid, wave, k);
 }
 
 // FP8 V3.2 records of one half (32 x 656 B = 1312 chunks) are staged raw by
@@ -594,17 +603,23 @@ k_decode(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int half = lane >> 5, r32 = lane & 31;
 
-  // blockIdx -> (slot, row group); the G row groups of one slot are
-  // dispatched back to back onto the same XCD (ids s, s+8, ...) so their
-  // shared KV reads meet in that XCD's L2.
+  // blockIdx -> (slot, row group).  Workgroup w runs on XCD w % 8; XCD x
+  // gets the consecutive slots x*S/8 .. (x+1)*S/8 - 1, and the G row groups
+  // of one slot are dispatched back to back onto it.  Consecutive slots
+  // mostly hold the middle splits of one sequence, which start together and
+  // read the same query rows, and the row groups of a slot read the same KV:
+  // both meet in that XCD's L2.  (S % 8 == 0 is required when G > 1; with
+  // G == 1 and other S the slots are taken in workgroup order.)
   int slot, g;
   {
-    const int G = a.groups, wg = blockIdx.x;
-    if (G == 1) { slot = wg; g = 0; }
-    else {
-      const int xcd = wg & 7, k = wg >> 3;
+    const int G = a.groups, wg = blockIdx.x, S = a.num_slots;
+    const int xcd = wg & 7, k = wg >> 3;
+    if (G == 1) {
+      g = 0;
+      slot = (S & 7) ? wg : xcd * (S >> 3) + k;
+    } else {
       g = k % G;
-      slot = (k / G) * 8 + xcd;
+      slot = xcd * (S >> 3) + k / G;
     }
   }
   const int32_t* ms = a.meta + 8 * slot;
@@ -727,8 +742,42 @@ k_decode(DecodeArgs a) {
     }
   };
 
+  // bf16 path: the loads of step+2 are captured by prepare_load() at the
+  // start of step `step` and issued by emit_load(k), k < kLoadsPerHalf.
+  // Past the slot's last step the same instructions stage zeros into the
+  // free slot.  (Spreading the nine instructions between the MFMAs was
+  // measured: no gain, the address unit's queue blocks the wave either way.)
+  int pl_step = 0, pl_valid = 0, pl_h = 0, pl_nvalid = 0;
+  int64_t pl_phys = 0;
+  auto prepare_load = [&](int st) {
+    const bool do_load = st < nsteps;
+    pl_step = st;
+    pl_h = lh;
+    if constexpr (!SPARSE) {
+      const bool any = do_load && lj * kPage < lL;
+      pl_valid = any ? min(kPage, lL - lj * kPage) : 0;
+      pl_phys = any ? lphys : 0;
+    } else {
+      pl_nvalid = do_load ? min(kHalfRows, a.topk - lj * kPage - lh * kHalfRows) : 0;
+    }
+    if (do_load) advance_load();
+  };
+  auto emit_load = [&](int k) {
+    uint8_t* slot = smem + Lay::kTileOff + (pl_step % kRing) * kHalfBytes;
+    if constexpr (!SPARSE) load_row_bf16_dense(slot, a.kv, pl_phys, pl_valid, pl_h, wave, k);
+    else load_row_bf16_sparse(slot, a.kv, ids_slot(pl_step), pl_nvalid, wave, k);
+  };
+
   // loads of step+2 and (sparse) ids of step+4, issued at step `step`
   int fb = b0, fj = j0, fh = 0;   // next step whose ids to fetch
+  auto fetch_next_ids = [&](int step) {
+    if constexpr (SPARSE) {
+      if (step + 4 < nsteps) {
+        fetch_ids(fb, fj, fh, step + 4);
+        advance(fb, fj, fh);
+      }
+    }
+  };
   auto issue_next = [&](int step) {
     if (step + 2 < nsteps) {
       issue_load(step + 2);
@@ -1008,7 +1057,10 @@ k_decode(DecodeArgs a) {
         wait_vmcnt<0>();  // tile ps+1 (issued a step ago) and the walker's prefetch landed
         lds_barrier();    // ... for every wave; tile ps-1's slot is free
         land();
-        issue_next(step);
+        prepare_load(step + 2);
+        fetch_next_ids(step);
+#pragma unroll
+        for (int k = 0; k < kLoadsPerHalf; ++k) emit_load(k);
         SmState st;
         const int key0 = key0_of(ps);
         if (nxt_has) {
