@@ -452,7 +452,7 @@ constexpr int kRawLoadsPerWave = kRawSlotBytes / 1024 / kWaves;  // 6
 
 __device__ __forceinline__ void load_half_fp8_dense(uint8_t* raw, const uint8_t* kv, int64_t phys,
                                                     int valid, int h, int wave, int lane) {
-  lane = opaque(lane);
+  lane = fresh_lane();
   const uint8_t* page = kv + phys * (int64_t)(kPage * kFp8TokenBytes);
   const i32x4 rs = make_rsrc(page, valid * kFp8TokenBytes);
   const uint32_t base = lds_off(raw);
@@ -466,7 +466,7 @@ __device__ __forceinline__ void load_half_fp8_dense(uint8_t* raw, const uint8_t*
 __device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t* kv,
                                                      const int32_t* ids, int nvalid, int wave,
                                                      int lane) {
-  lane = opaque(lane);
+  lane = fresh_lane();
 #pragma unroll
   for (int ii = 0; ii < kRawLoadsPerWave; ++ii) {
     const int i = ii * kWaves + wave;
@@ -480,10 +480,60 @@ __device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t
   }
 }
 
+// Scales of an FP8 half tile in LDS, in the register order of the S^T
+// accumulator: [tile t][lane half h][i] holds the scale of dims 128t.. of
+// key key_of_row(8*(i/4) + i%4) + h.
+constexpr int kScaleBytes = 4 * 2 * 16 * 4;
+__device__ __forceinline__ int scale_slot(int key) {  // key -> h*16 + i
+  const int h = key & 1, kc = key - h, rem = kc & 15;
+  return h * 16 + 8 * (kc >> 4) + 4 * ((rem >> 1) & 1) + (rem >> 2);
+}
+
+// 32 raw records -> the bf16 half tile with the e4m3 codes of dims < 512
+// converted exactly (every e4m3 value is a bf16 value), dims 512..575
+// copied, and the fp32 tile scales moved to `scl`.  The decode applies the
+// scales in fp32: to each tile's partial scores in QK^T and to P in P.V, so
+// no product code*scale is ever rounded to bf16.  An all-zero record gives a
+// zero row with zero scales.
+__device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const uint8_t* raw, int tid) {
+  tid = (tid & ~63) | fresh_lane();  // keep the per-thread addresses out of the loop's live set
+#pragma unroll
+  for (int kk = 0; kk < kHalfRows * 64 / kThreads; ++kk) {
+    const int k = kk * kThreads + tid;
+    const int r = k >> 6, c = k & 63;
+    const uint2 code = *reinterpret_cast<const uint2*>(raw + r * kFp8TokenBytes + c * 8);
+    const uint32_t cw[2] = {code.x, code.y};
+    uint32_t w[4];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      typedef __attribute__((ext_vector_type(2))) float f2;
+      f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], false);
+      f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], true);
+      __bf16 b0 = (__bf16)lo[0], b1 = (__bf16)lo[1], b2 = (__bf16)hi[0], b3 = (__bf16)hi[1];
+      w[2 * hh] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      w[2 * hh + 1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+    }
+    *reinterpret_cast<uint4*>(tile + r * kMainStride + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  {
+    const int r = tid >> 3, c = tid & 7;
+    const uint4 v = *reinterpret_cast<const uint4*>(raw + r * kFp8TokenBytes + 528 + c * 16);
+    *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = v;
+  }
+  if (tid < 4 * kHalfRows) {
+    const int r = tid >> 2, t = tid & 3;
+    scl[t * 32 + scale_slot(r)] = *reinterpret_cast<const float*>(raw + r * kFp8TokenBytes + 512 + 4 * t);
+  }
+}
+
 // Dequantise 32 raw records into the bf16 half tile: dims < 512 are
 // e4m3 * fp32 tile scale computed in fp32 and rounded once to bf16 (RNE);
-// dims 512..575 are copied.  An all-zero record gives a zero row.
-__device__ __forceinline__ void dequant_half(uint8_t* tile, const uint8_t* raw, int tid) {
+// dims 512..575 are copied.  An all-zero record gives a zero row.  (The
+// staged rows as the cache defines them; the decode itself keeps the codes
+// and the scales apart, see dequant_codes.)
+__device__ __forceinline__ void dequant_half_scaled(uint8_t* tile, const uint8_t* raw, int tid) {
 #pragma unroll
   for (int kk = 0; kk < kHalfRows * 64 / kThreads; ++kk) {
     const int k = kk * kThreads + tid;
@@ -575,7 +625,8 @@ struct DecodeLayout {
   static constexpr int kQOff = kRawOff + (KVF == kKvBf16 ? 0 : kRing * kRawSlotBytes);
   static constexpr int kIdsOff = kQOff + kWaves * kQLdsWaveBytes;
   static constexpr int kWalkOff = kIdsOff + (SPARSE ? kIdsSlots * 256 : 0);  // 2 words per wave
-  static constexpr int kSmem = kWalkOff + (KVF == kKvBf16 && !SPARSE ? kWaves * 8 : 0);
+  static constexpr int kSclOff = kWalkOff + (KVF == kKvBf16 && !SPARSE ? kWaves * 8 : 0);
+  static constexpr int kSmem = kSclOff + (KVF == kKvBf16 ? 0 : kScaleBytes);
   // per-step VMEM instructions issued by every wave (loads + id fetch)
   static constexpr int kVmPerStep =
       (KVF == kKvBf16 ? kLoadsPerHalf : kRawLoadsPerWave) + (SPARSE ? 1 : 0);
@@ -954,6 +1005,105 @@ k_decode(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
+    // FP8: S^T from the exact codes, one 128-dim tile at a time, each tile's
+    // partial scores scaled by its per-key fp32 scale before they are summed;
+    // the RoPE block (bf16 in the cache) adds unscaled.
+    const float* scl = reinterpret_cast<const float*>(smem + Lay::kSclOff);
+    auto qk_fp8 = [&](int tb, f32x16& sc) {
+      constexpr int kLa = 3;
+      const int ln = fresh_lane(), lr = ln & 31, lh = ln >> 5;
+      const int lkey = key_of_row(lr), lfr = (lkey >> 1) & 7, lx = (lr >> 1) & 7;
+      const int koff = tb + lkey * kMainStride + 16 * lh;
+      const int kroff = tb + kRopeOff + lkey * kRopeStride;
+      const int qb = Lay::kQOff + wave * kQLdsWaveBytes + lr * kQLdsRowBytes;
+      int qoff[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qoff[e] = qb + ((((2 * e) | lh) ^ lx) << 4);
+      auto read_k = [&](int ks) {
+        if (ks < 32) return *reinterpret_cast<const bf16x8*>(smem + koff + 32 * ks);
+        return *reinterpret_cast<const bf16x8*>(smem + kroff + ((((2 * (ks - 32)) | lh) ^ lfr) << 4));
+      };
+      auto read_q = [&](int ks) {
+        return *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegSteps) & 3] +
+                                                ((ks - kQRegSteps) >> 2) * 128);
+      };
+      const f32x4* sv = reinterpret_cast<const f32x4*>(scl + lh * 16);
+      bf16x8 kbuf[kLa], qbuf[kLa];
+      f32x16 part;
+#pragma unroll
+      for (int i = 0; i < kLa; ++i) kbuf[i] = read_k(i);
+#pragma unroll
+      for (int ks = 0; ks < 36; ++ks) {
+        const bf16x8 ka = kbuf[ks % kLa];
+        const bf16x8 qb = ks < kQRegSteps ? qf[ks] : qbuf[ks % kLa];
+        if (ks + kLa < 36) {
+          kbuf[ks % kLa] = read_k(ks + kLa);
+          if (ks + kLa >= kQRegSteps) qbuf[ks % kLa] = read_q(ks + kLa);
+        }
+        if (ks % 8 == 0 && ks <= 32) mfma_s_first(part, ka, qb);
+        else mfma_s_acc(part, ka, qb);
+        if (ks % 8 == 7 || ks == 35) {
+          mfma_s_settle(part);
+          const int t = ks >> 3;
+          if (t < 4) {
+            // compiler-only fence: each fold reads its tile's scales here,
+            // not hoisted with the other tiles' into registers up front
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 s4 = sv[t * 8 + q];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                sc[4 * q + e] = (t == 0 ? 0.f : sc[4 * q + e]) + part[4 * q + e] * s4[e];
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[i] += part[i];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // FP8: O^T += V^T P_t^T where V holds the exact codes and P_t = p * the
+    // keys' scale of tile t (d-tiles 4t..4t+3), rounded once to bf16.
+    auto pv_fp8 = [&](int tb, const f32x16& p) {
+      const int ln = fresh_lane(), lh = ln >> 5;
+      const f32x4* sv = reinterpret_cast<const f32x4*>(scl + lh * 16);
+      constexpr int kVa = 3;
+      const int voff = tb + (4 * ((ln & 15) >> 2) + lh) * kMainStride + 32 * ((ln >> 4) & 1) + 8 * (ln & 3);
+      auto read_v = [&](int i) {  // i = kq * 16 + mt
+        const int kq = i >> 4, mt = i & 15;
+        const uint8_t* pp = smem + voff + kq * 16 * kMainStride + mt * 64;
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(pp));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(pp + 2 * kMainStride));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      // mt order: the four d-tiles of one scale tile, both key halves
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bf16x8 pt[2];
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 s4 = sv[t * 8 + q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pt[q >> 1][4 * (q & 1) + e] = (__bf16)(p[4 * q + e] * s4[e]);
+        }
+        valu_to_mfma_settle(pt[0], pt[1]);
+        bf16x8 vbuf[kVa];
+#pragma unroll
+        for (int i = 0; i < kVa; ++i) vbuf[i] = read_v((i >> 2) * 16 + 4 * t + (i & 3));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {  // i = kq * 4 + (mt - 4t)
+          const bf16x8 va = vbuf[i % kVa];
+          if (i + kVa < 8) vbuf[i % kVa] = read_v(((i + kVa) >> 2) * 16 + 4 * t + ((i + kVa) & 3));
+          mfma_o(o[4 * t + (i & 3)], va, pt[i >> 2]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
     auto key0_of = [&](int ps) { return (cj + (ps >> 1)) * kPage + (ps & 1) * kHalfRows; };
     auto has_keys = [&](int ps) {
       const int k0 = key0_of(ps);
@@ -1015,6 +1165,7 @@ k_decode(DecodeArgs a) {
           const float p = __builtin_amdgcn_exp2f(sc[i] - st.mref);
           st.psum += p;
           st.pf[i >> 3][i & 7] = (__bf16)p;
+          if constexpr (KVF != kKvBf16) sc[i] = p;
         }
       } else {
         lsum = lsum * st.alpha + st.psum;
@@ -1096,17 +1247,17 @@ k_decode(DecodeArgs a) {
           lds_barrier();  // every wave's loads of this step landed; slot (step+2)%3 is free
           issue_next(step);
         }
-        dequant_half(smem + Lay::kTileOff, smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
+        dequant_codes(smem + Lay::kTileOff, reinterpret_cast<float*>(smem + Lay::kSclOff),
+                      smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
         lds_barrier();
         if (has_keys(ps)) {
           f32x16 sc;
           SmState st;
-          qk(tile_off(step), sc, [](int) {});
+          qk_fp8(tile_off(step), sc);
 #pragma unroll
           for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc, st, key0_of(ps), step);
           rescale_o(st);
-          valu_to_mfma_settle(st.pf[0], st.pf[1]);
-          pv(tile_off(step), st.pf);
+          pv_fp8(tile_off(step), sc);
         }
       }
     }
@@ -1386,7 +1537,7 @@ __global__ void __launch_bounds__(kThreads) k_debug_gather(DecodeArgs a, int b, 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if constexpr (KVF != kKvBf16) {
-      dequant_half(tile, raw, tid);
+      dequant_half_scaled(tile, raw, tid);
       __syncthreads();
     }
     for (int k = tid; k < kHalfRows * kChunksPerRow; k += kThreads) {
