@@ -1010,7 +1010,7 @@ k_decode(DecodeArgs a) {
     // the RoPE block (bf16 in the cache) adds unscaled.
     const float* scl = reinterpret_cast<const float*>(smem + Lay::kSclOff);
     auto qk_fp8 = [&](int tb, f32x16& sc) {
-      constexpr int kLa = 3;
+      constexpr int kLa = 2;  // the tile accumulator costs 16 VGPRs: shorter lookahead
       const int ln = fresh_lane(), lr = ln & 31, lh = ln >> 5;
       const int lkey = key_of_row(lr), lfr = (lkey >> 1) & 7, lx = (lr >> 1) & 7;
       const int koff = tb + lkey * kMainStride + 16 * lh;
@@ -1069,7 +1069,7 @@ k_decode(DecodeArgs a) {
     auto pv_fp8 = [&](int tb, const f32x16& p) {
       const int ln = fresh_lane(), lh = ln >> 5;
       const f32x4* sv = reinterpret_cast<const f32x4*>(scl + lh * 16);
-      constexpr int kVa = 3;
+      constexpr int kVa = 2;
       const int voff = tb + (4 * ((ln & 15) >> 2) + lh) * kMainStride + 32 * ((ln >> 4) & 1) + 8 * (ln & 3);
       auto read_v = [&](int i) {  // i = kq * 16 + mt
         const int kq = i >> 4, mt = i & 15;
@@ -1119,7 +1119,7 @@ k_decode(DecodeArgs a) {
     //   10    running sum
     struct SmState {
       float mx, alpha, mref, psum;
-      uint32_t any_need;
+      uint32_t any_need, vmask;
       bf16x8 pf[2];
     };
     auto sm_slice = [&](int k, f32x16& sc, SmState& st, int key0, int st_step) {
@@ -1128,13 +1128,19 @@ k_decode(DecodeArgs a) {
         // the key of register i is kc + half with kc a compile-time constant,
         // so the lane's half is folded into the limits, not into 16 keys
         if constexpr (SPARSE) {
-          const int32_t* ids_h = ids_slot(st_step) + half;
-          const int nvalid_h = (row_ok ? min(kHalfRows, a.topk - key0) : 0) - half;
+          // valid keys of the step as one bit mask (a ballot over the ids),
+          // shifted by the lane's half: key kc + half is bit kc
+          if (k == 0) {
+            const int ln = fresh_lane(), r = ln & 31;
+            const int nvalid = min(kHalfRows, a.topk - key0);
+            const uint64_t bm = __builtin_amdgcn_ballot_w64(ln < 32 && r < nvalid && ids_slot(st_step)[r] >= 0);
+            st.vmask = row_ok ? (uint32_t)bm >> half : 0u;
+          }
 #pragma unroll
           for (int i = 4 * k; i < 4 * k + 4; ++i) {
             const int kc = key_of_row(8 * (i >> 2) + (i & 3));
             float v = sc[i] * srow;
-            v = (kc < nvalid_h && ids_h[kc] >= 0) ? v : -INFINITY;
+            v = ((st.vmask >> kc) & 1u) ? v : -INFINITY;
             sc[i] = v;
             st.mx = fmaxf(st.mx, v);
           }
