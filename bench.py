@@ -7,7 +7,9 @@ seqlens ~ U{1024..8192}, 64-token pages, shuffled block table over a 1.2x
 pool), seeded and synthetic.  Inputs are resident in HBM before timing; the
 KV pool and queries are replicated into several copies that steps rotate
 through, so a step never finds its KV in the 256 MB Infinity Cache left by
-the previous step.
+the previous step.  The timed steps launch their three calls from the host
+(``--graph`` replays one captured hipGraph per copy instead); the decode
+kernel's own duration comes from a second, untimed pass.
 
 Prints one JSON line with the metric (effective HBM GB/s of algorithmic
 bytes per step), the TFLOPS, the decode kernel's roofline position and the
@@ -102,6 +104,9 @@ def main():
     ap.add_argument("--workload", default="dense_b64_h128_L1k-8k")
     ap.add_argument("--rotate", type=int, default=0, help="KV copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each step's three calls once as a hipGraph and replay it "
+                         "(default: launch them from the host)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit: "
                          "the known-size kernel that scales HBM counter readings")
@@ -163,8 +168,6 @@ def main():
                        p.kv_format, ws, out, lse, fused)
         pr.flags = B.MLA_FLAG_DEFER_COMBINE
         params.append(pr)
-    stream = torch.cuda.current_stream(dev)
-    sh = ctypes.c_void_p(stream.cuda_stream)
     sl_p, meta_p, ns_p = ctypes.c_void_p(sl.data_ptr()), ctypes.c_void_p(meta.data_ptr()), ctypes.c_void_p(ns.data_ptr())
 
     # The decode kernel's own start/end timestamps (mla_decode_timed records
@@ -180,13 +183,12 @@ def main():
             raise RuntimeError("hipEventCreate failed")
         return e
 
-    def step(i, ev=None, kev=None):
+    def step(i, kev=None):
+        # the stream is looked up at call time: under graph capture it is the
+        # capturing stream
         pr = params[i % R]
-        if ev is not None:
-            ev[0].record(stream)
+        sh = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         st = lib.mla_get_metadata(sl_p, p.batch, rows, 1, topk, S, meta_p, ns_p, sh)
-        if ev is not None:
-            ev[1].record(stream)
         if kev is not None:
             st |= lib.mla_decode_timed(ctypes.byref(pr), sh, kev[0], kev[1])
         else:
@@ -198,19 +200,61 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    kevs = [(hip_event(), hip_event()) for _ in range(args.steps)]
+
+    # One hipGraph per KV copy, each holding a whole step (metadata, decode,
+    # combine), as a serving loop would replay it.
+    graphs = None
+    if args.graph:
+        graphs = []
+        cap = torch.cuda.Stream(dev)
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+
+    def run_steps(first):
+        if graphs is not None:
+            for i in range(args.steps):
+                graphs[(first + i) % R].replay()
+        else:
+            for i in range(args.steps):
+                step(first + i)
+
+    # Timed region: the steps only, bracketed by two events on the stream.
+    stream = torch.cuda.current_stream(dev)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i], kevs[i])
+    run_steps(args.warmup)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
-    ms = total_ms / args.steps
+    ms = start.elapsed_time(end) / args.steps
+
+    # Second pass, outside the timed region: the decode kernel's own duration
+    # (mla_decode_timed records HIP events at its dispatch, on the launch
+    # stream), and the metadata call's, per step.
+    kevs = [(hip_event(), hip_event()) for _ in range(args.steps)]
+    mevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        mevs[i][0].record(stream)
+        st = lib.mla_get_metadata(sl_p, p.batch, rows, 1, topk, S, meta_p, ns_p,
+                                  ctypes.c_void_p(stream.cuda_stream))
+        mevs[i][1].record(stream)
+        if st != 0:
+            raise RuntimeError(lib.mla_last_error().decode())
+        pr = params[(args.warmup + i) % R]
+        st = lib.mla_decode_timed(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream), kevs[i][0], kevs[i][1])
+        st |= lib.mla_combine(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(lib.mla_last_error().decode())
+    torch.cuda.synchronize()
     dec_ms = []
     for k0, k1 in kevs:
         t = ctypes.c_float()
@@ -219,11 +263,12 @@ def main():
         dec_ms.append(t.value)
         hip.hipEventDestroy(k0)
         hip.hipEventDestroy(k1)
-    meta_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
+    meta_ms = [mevs[i][0].elapsed_time(mevs[i][1]) for i in range(args.steps)]
     dec_avg = float(np.mean(dec_ms))
-    log(f"step {ms * 1e3:.1f} us (wall {wall / args.steps * 1e6:.1f} us); decode kernel avg "
-        f"{dec_avg * 1e3:.1f} us (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 "
-        f"{np.percentile(dec_ms, 90) * 1e3:.1f}); metadata {np.mean(meta_ms) * 1e3:.1f} us; rotation {R}")
+    log(f"step {ms * 1e3:.1f} us ({'eager launches' if graphs is None else 'hipGraph replay'}; wall "
+        f"{wall / args.steps * 1e6:.1f} us); decode kernel avg {dec_avg * 1e3:.1f} us (p10 "
+        f"{np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); metadata "
+        f"{np.mean(meta_ms) * 1e3:.1f} us; rotation {R}")
 
     value = nbytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
@@ -239,7 +284,8 @@ def main():
         "config": {"workload": p.name, "batch": p.batch, "s_q": p.s_q, "h_q": p.h_q, "d_qk": 576,
                    "d_v": 512, "page": 64, "kv_format": p.kv_format, "causal": bool(p.causal),
                    "sparse_topk": topk, "fused": bool(p.fused), "parallelism": "single GPU",
-                   "kv_copies_rotated": R},
+                   "kv_copies_rotated": R,
+                   "launch": "eager" if graphs is None else "hipGraph per step (metadata, decode, combine)"},
         "tflops": round(tflops, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -362,9 +362,9 @@ k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
 // 16-lane phases of the K reads (16 keys, one chunk) and the 32-lane phases
 // of the transposed V reads (keys b, b+4, b+8, b+12 x 4 chunks) both touch
 // 16 distinct 4-bank groups: no bank conflicts, and each read stream needs a
-// single per-lane base address plus immediates.  Half tiles rotate through a
-// ring of 3 slots, so two halves are in flight while the third is computed
-// on.
+// single per-lane base address plus immediates.  bf16 half tiles rotate
+// through a ring of 4 slots: two are computed on (S^T of one, P V of the
+// other) while the next two are in flight.
 // ---------------------------------------------------------------------------
 constexpr int kHalfRows = 32;
 constexpr int kMainStride = 1040;
@@ -372,7 +372,8 @@ constexpr int kRopeOff = kHalfRows * kMainStride;               // 33280
 constexpr int kRopeStride = 128;
 constexpr int kHalfBytes = kRopeOff + kHalfRows * kRopeStride;  // 37376
 constexpr int kLoadsPerHalf = kHalfRows / kWaves + 1;           // 9 per wave: 8 rows + rope
-constexpr int kRing = 3;
+constexpr int kTileRing = 4;  // bf16 half-tile slots
+constexpr int kRing = 3;      // FP8 raw slots
 
 // The key held by row m (0..31) of an S^T tile (and by k-slot m of the
 // matching P^T / V^T operands): keys 4j+c of a 16-row block sit at rows
@@ -606,24 +607,28 @@ __device__ __forceinline__ void rope_cs(double pos, double inv_freq, float sign,
 // ---------------------------------------------------------------------------
 // Decode kernel
 //
-// Query fragments: dims 0..383 (k-steps 0..23) stay in VGPRs, dims 384..575
-// (k-steps 24..35) in a per-wave LDS region [32 rows][24 chunks] swizzled
-// like the KV tile.  This keeps the wave's register file at
-// 96 (Q) + 256 (O, AGPRs) + working set, with no spills.
+// Query fragments.  bf16 KV: all 36 k-steps stay in VGPRs (144), which
+// leaves the LDS to the four-slot tile ring.  FP8 KV, whose dequantisation
+// and per-tile scaling need more registers: dims 0..383 (k-steps 0..23) in
+// VGPRs, dims 384..575 (k-steps 24..35) in a per-wave LDS region
+// [32 rows][24 chunks] swizzled like the KV tile.
 // ---------------------------------------------------------------------------
-constexpr int kQRegSteps = 24;
-constexpr int kQLdsSteps = 36 - kQRegSteps;               // 12
-constexpr int kQLdsRowBytes = kQLdsSteps * 2 * 16;        // 384
-constexpr int kQLdsWaveBytes = 32 * kQLdsRowBytes;        // 12288
+template <int KVF>
+constexpr int q_reg_steps() { return KVF == kKvBf16 ? 36 : 24; }
+template <int KVF>
+constexpr int q_lds_row_bytes() { return (36 - q_reg_steps<KVF>()) * 2 * 16; }    // fp8: 384
+template <int KVF>
+constexpr int q_lds_wave_bytes() { return 32 * q_lds_row_bytes<KVF>(); }          // fp8: 12288
+constexpr int kQRegStepsFp8 = q_reg_steps<kKvFp8V32>();
 constexpr int kIdsSlots = 6;
 
 template <int KVF, bool SPARSE>
 struct DecodeLayout {
   static constexpr int kTileOff = 0;                                   // bf16 half tiles
-  static constexpr int kTiles = KVF == kKvBf16 ? kRing : 1;
+  static constexpr int kTiles = KVF == kKvBf16 ? kTileRing : 1;
   static constexpr int kRawOff = kTiles * kHalfBytes;                  // fp8 raw slots
   static constexpr int kQOff = kRawOff + (KVF == kKvBf16 ? 0 : kRing * kRawSlotBytes);
-  static constexpr int kIdsOff = kQOff + kWaves * kQLdsWaveBytes;
+  static constexpr int kIdsOff = kQOff + kWaves * q_lds_wave_bytes<KVF>();
   static constexpr int kWalkOff = kIdsOff + (SPARSE ? kIdsSlots * 256 : 0);  // 2 words per wave
   static constexpr int kSclOff = kWalkOff + (KVF == kKvBf16 && !SPARSE ? kWaves * 8 : 0);
   static constexpr int kSmem = kSclOff + (KVF == kKvBf16 ? 0 : kScaleBytes);
@@ -774,7 +779,7 @@ k_decode(DecodeArgs a) {
   land();
   // stage the walker's step as step `step` into its ring slot
   auto issue_load = [&](int step) {
-    const int rs = step % kRing;
+    const int rs = step % (KVF == kKvBf16 ? kTileRing : kRing);
     if constexpr (!SPARSE) {
       const bool any = lj * kPage < lL;
       const int valid = any ? min(kPage, lL - lj * kPage) : 0;
@@ -793,10 +798,11 @@ k_decode(DecodeArgs a) {
     }
   };
 
-  // bf16 path: the loads of step+2 are captured by prepare_load() at the
-  // start of step `step` and issued by emit_load(k), k < kLoadsPerHalf.
-  // Past the slot's last step the same instructions stage zeros into the
-  // free slot.  (Spreading the nine instructions between the MFMAs was
+  // bf16 path: the loads of step+3 are captured by prepare_load() at the
+  // start of step `step` and issued by emit_load(k), k < kLoadsPerHalf, after
+  // the walker's and the ids' word loads of that step.  Past the slot's last
+  // step the same instructions stage zeros into the free slot, so every step
+  // issues exactly kLoadsPerHalf tile loads, last.  (Spreading the nine instructions between the MFMAs was
   // measured: no gain, the address unit's queue blocks the wave either way.)
   int pl_step = 0, pl_valid = 0, pl_h = 0, pl_nvalid = 0;
   int64_t pl_phys = 0;
@@ -814,7 +820,7 @@ k_decode(DecodeArgs a) {
     if (do_load) advance_load();
   };
   auto emit_load = [&](int k) {
-    uint8_t* slot = smem + Lay::kTileOff + (pl_step % kRing) * kHalfBytes;
+    uint8_t* slot = smem + Lay::kTileOff + (pl_step % kTileRing) * kHalfBytes;
     if constexpr (!SPARSE) load_row_bf16_dense(slot, a.kv, pl_phys, pl_valid, pl_h, wave, k);
     else load_row_bf16_sparse(slot, a.kv, ids_slot(pl_step), pl_nvalid, wave, k);
   };
@@ -842,7 +848,9 @@ k_decode(DecodeArgs a) {
     }
   };
 
-  // ---- prologue: ids of steps 0..3, loads of steps 0 and 1
+  // ---- prologue: ids of steps 0..3, loads of steps 0 and 1 (bf16: step 2's
+  // follows in the first piece's prologue, once the walker has landed the
+  // block of step 2's item)
   if constexpr (SPARSE) {
     for (int s = 0; s < min(4, nsteps); ++s) {
       fetch_ids(fb, fj, fh, s);
@@ -855,12 +863,14 @@ k_decode(DecodeArgs a) {
     advance_load();
   }
 
-  uint8_t* qlds = smem + Lay::kQOff + wave * kQLdsWaveBytes;
-  // Q rows are 384 B apart (an 8-group shift): chunk c of row r at
+  constexpr int kQR = q_reg_steps<KVF>();
+  uint8_t* qlds = smem + Lay::kQOff + wave * q_lds_wave_bytes<KVF>();
+  // FP8: Q rows are 384 B apart (an 8-group shift): chunk c of row r at
   // c ^ ((r >> 1) & 7) puts the 16 rows of a read phase on distinct groups
   const int x = (r32 >> 1) & 7;
-  bf16x8 qf[kQRegSteps];
+  bf16x8 qf[kQR];
   f32x16 o[16];
+  bool first_piece = true;
 
   int cb = b0, cj = j0, step = 0;
   while (step < nsteps) {
@@ -877,11 +887,9 @@ k_decode(DecodeArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) o[mt] = f32x16{};
 
-    // ---- piece prologue: drain (the previous piece's stores are in flight),
-    // then the query fragments, issued before the next loads so that waiting
-    // for them does not wait for those
-    wait_vmcnt<0>();
-    lds_barrier();  // every wave's loads of the first step landed
+    // ---- piece prologue: the query fragments, then a drain.  The loads of
+    // the piece's first steps (and the previous piece's stores) are older
+    // than the query loads, so their latencies overlap.
     // Query fragments of this piece.  Fused: q^ = inv * RoPE(q (.) w) with
     // inv = 1 / sqrt(mean(q^2) + eps) (RMSNorm over the row's 576 dims, then
     // RoPE on dims 512..575 at position len - s_q + t; RoPE is linear, so the
@@ -893,38 +901,60 @@ k_decode(DecodeArgs a) {
       const uint16_t* qrow = a.q + ((int64_t)cb * a.rows + (row_ok ? row : 0)) * kDqk;
       float ss = 0.f;
       const double pos = (double)Lb - (double)a.s_q + (double)tok;
-#pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
-        bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
-        if constexpr (FUSED) {
-          const bf16x8 wv = *reinterpret_cast<const bf16x8*>(a.norm_w + (2 * ks + half) * 8);
-          float y[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float qv = (float)v[e];
-            ss += qv * qv;
-            y[e] = qv * (float)wv[e];
-          }
-          if (ks >= 32) {
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-              float cs, sn;
-              rope_cs(pos, half ? a.rope_inv_freq[8 * (ks - 32) + 4 + pp] : a.rope_inv_freq[8 * (ks - 32) + pp],
-                      1.0f, cs, sn);
-              const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
-              y[2 * pp] = x0 * cs - x1 * sn;
-              y[2 * pp + 1] = x0 * sn + x1 * cs;
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (__bf16)y[e];
-        }
+      // chunk ks (dims 16ks + 8half .. +7): q-hat chunk, then its home
+      auto put_q = [&](int ks, bf16x8 v) {
         if (!row_ok) v = bf16x8{};
-        if (ks < kQRegSteps) {
+        if (ks < kQR) {
           qf[ks] = v;
         } else {
-          const int cq = 2 * (ks - kQRegSteps) + half;
-          *reinterpret_cast<bf16x8*>(qlds + r32 * kQLdsRowBytes + ((cq ^ x) << 4)) = v;
+          const int cq = 2 * (ks - kQR) + half;
+          *reinterpret_cast<bf16x8*>(qlds + r32 * q_lds_row_bytes<KVF>() + ((cq ^ x) << 4)) = v;
+        }
+      };
+      if constexpr (!FUSED) {
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) put_q(ks, *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8));
+      } else {
+        // Six batches of 6 chunks (the RoPE chunks 32..35 first), each
+        // batch's q and weight loads issued together: all 72 in flight at
+        // once would not fit in the registers beside the fragments.
+        constexpr int kBatch = 6;
+#pragma unroll
+        for (int bt = 0; bt < 36 / kBatch; ++bt) {
+          bf16x8 vb[kBatch], wb[kBatch];
+#pragma unroll
+          for (int i = 0; i < kBatch; ++i) {
+            const int n = bt * kBatch + i, ks = n < 4 ? 32 + n : n - 4;
+            vb[i] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
+            wb[i] = *reinterpret_cast<const bf16x8*>(a.norm_w + (2 * ks + half) * 8);
+          }
+#pragma unroll
+          for (int i = 0; i < kBatch; ++i) {
+            const int n = bt * kBatch + i, ks = n < 4 ? 32 + n : n - 4;
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float qv = (float)vb[i][e];
+              ss += qv * qv;
+              y[e] = qv * (float)wb[i][e];
+            }
+            if (ks >= 32) {
+#pragma unroll
+              for (int pp = 0; pp < 4; ++pp) {
+                float cs, sn;
+                rope_cs(pos, half ? a.rope_inv_freq[8 * (ks - 32) + 4 + pp] : a.rope_inv_freq[8 * (ks - 32) + pp],
+                        1.0f, cs, sn);
+                const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
+                y[2 * pp] = x0 * cs - x1 * sn;
+                y[2 * pp + 1] = x0 * sn + x1 * cs;
+              }
+            }
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (__bf16)y[e];
+            put_q(ks, v);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       if constexpr (FUSED) {
@@ -932,44 +962,46 @@ k_decode(DecodeArgs a) {
         srow *= 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
       }
     }
+    wait_vmcnt<0>();
+    lds_barrier();  // every wave's loads of the piece's first step (and Q in LDS) landed
+    if constexpr (KVF == kKvBf16) {
+      if (first_piece) {
+        // step 2: the drain above landed the walker's block of its item
+        land();
+        prepare_load(2);
+#pragma unroll
+        for (int k = 0; k < kLoadsPerHalf; ++k) emit_load(k);
+      }
+    }
+    first_piece = false;
 
     // ======== building blocks of one 32-key step
     auto tile_off = [&](int st) -> int {
-      if constexpr (KVF == kKvBf16) return Lay::kTileOff + (st % kRing) * kHalfBytes;
+      if constexpr (KVF == kKvBf16) return Lay::kTileOff + (st % kTileRing) * kHalfBytes;
       else return Lay::kTileOff;
     };
     // S^T (32 keys x 32 rows) of the tile at LDS offset tb into sc, with the
     // LDS operands of k-step ks+kLa read before the MFMA of k-step ks (order
     // fixed by scheduling fences); hook(ks) runs after that MFMA is issued.
+    // (bf16 only: the query fragments are all in VGPRs.)
     auto qk = [&](int tb, f32x16& sc, auto&& hook) {
       constexpr int kLa = FUSED ? 3 : 4;
       const int ln = fresh_lane(), lr = ln & 31, lh = ln >> 5;
-      const int lkey = key_of_row(lr), lfr = (lkey >> 1) & 7, lx = (lr >> 1) & 7;
+      const int lkey = key_of_row(lr), lfr = (lkey >> 1) & 7;
       const int koff = tb + lkey * kMainStride + 16 * lh;
       const int kroff = tb + kRopeOff + lkey * kRopeStride;
-      const int qb = Lay::kQOff + wave * kQLdsWaveBytes + lr * kQLdsRowBytes;
-      int qoff[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qoff[e] = qb + ((((2 * e) | lh) ^ lx) << 4);
       auto read_k = [&](int ks) {
         if (ks < 32) return *reinterpret_cast<const bf16x8*>(smem + koff + 32 * ks);
         return *reinterpret_cast<const bf16x8*>(smem + kroff + ((((2 * (ks - 32)) | lh) ^ lfr) << 4));
       };
-      auto read_q = [&](int ks) {
-        return *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegSteps) & 3] +
-                                                ((ks - kQRegSteps) >> 2) * 128);
-      };
-      bf16x8 kbuf[kLa], qbuf[kLa];
+      bf16x8 kbuf[kLa];
 #pragma unroll
       for (int i = 0; i < kLa; ++i) kbuf[i] = read_k(i);
 #pragma unroll
       for (int ks = 0; ks < 36; ++ks) {
         const bf16x8 ka = kbuf[ks % kLa];
-        const bf16x8 qb = ks < kQRegSteps ? qf[ks] : qbuf[ks % kLa];
-        if (ks + kLa < 36) {
-          kbuf[ks % kLa] = read_k(ks + kLa);
-          if (ks + kLa >= kQRegSteps) qbuf[ks % kLa] = read_q(ks + kLa);
-        }
+        const bf16x8 qb = qf[ks < kQR ? ks : 0];
+        if (ks + kLa < 36) kbuf[ks % kLa] = read_k(ks + kLa);
         if (ks == 0) mfma_s_first(sc, ka, qb);
         else mfma_s_acc(sc, ka, qb);
         hook(ks);
@@ -1015,7 +1047,7 @@ k_decode(DecodeArgs a) {
       const int lkey = key_of_row(lr), lfr = (lkey >> 1) & 7, lx = (lr >> 1) & 7;
       const int koff = tb + lkey * kMainStride + 16 * lh;
       const int kroff = tb + kRopeOff + lkey * kRopeStride;
-      const int qb = Lay::kQOff + wave * kQLdsWaveBytes + lr * kQLdsRowBytes;
+      const int qb = Lay::kQOff + wave * q_lds_wave_bytes<KVF>() + lr * q_lds_row_bytes<KVF>();
       int qoff[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) qoff[e] = qb + ((((2 * e) | lh) ^ lx) << 4);
@@ -1024,8 +1056,8 @@ k_decode(DecodeArgs a) {
         return *reinterpret_cast<const bf16x8*>(smem + kroff + ((((2 * (ks - 32)) | lh) ^ lfr) << 4));
       };
       auto read_q = [&](int ks) {
-        return *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegSteps) & 3] +
-                                                ((ks - kQRegSteps) >> 2) * 128);
+        return *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegStepsFp8) & 3] +
+                                                ((ks - kQRegStepsFp8) >> 2) * 128);
       };
       const f32x4* sv = reinterpret_cast<const f32x4*>(scl + lh * 16);
       bf16x8 kbuf[kLa], qbuf[kLa];
@@ -1035,10 +1067,10 @@ k_decode(DecodeArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 36; ++ks) {
         const bf16x8 ka = kbuf[ks % kLa];
-        const bf16x8 qb = ks < kQRegSteps ? qf[ks] : qbuf[ks % kLa];
+        const bf16x8 qb = ks < kQR ? qf[ks < kQR ? ks : 0] : qbuf[ks % kLa];
         if (ks + kLa < 36) {
           kbuf[ks % kLa] = read_k(ks + kLa);
-          if (ks + kLa >= kQRegSteps) qbuf[ks % kLa] = read_q(ks + kLa);
+          if (ks + kLa >= kQRegStepsFp8) qbuf[ks % kLa] = read_q(ks + kLa);
         }
         if (ks % 8 == 0 && ks <= 32) mfma_s_first(part, ka, qb);
         else mfma_s_acc(part, ka, qb);
@@ -1203,7 +1235,8 @@ k_decode(DecodeArgs a) {
     if constexpr (KVF == kKvBf16) {
       // ---- bf16: step ps computes S^T of tile ps+1 with the softmax of tile
       // ps woven between its MFMAs, then O += P V of tile ps.  Tiles ps and
-      // ps+1 are resident; tile ps+2 loads into the third ring slot.
+      // ps+1 are resident; tiles ps+2 (issued a step ago) and ps+3 (issued
+      // now, into tile ps-1's slot) are in flight.
       const int n = 2 * (piece_end - cj);
       f32x16 sc_cur, sc_nxt;
       bool cur_has = has_keys(0);
@@ -1211,10 +1244,13 @@ k_decode(DecodeArgs a) {
       for (int ps = 0; ps < n; ++ps, ++step) {
         const bool has_next = ps + 1 < n;
         const bool nxt_has = has_next && has_keys(ps + 1);
-        wait_vmcnt<0>();  // tile ps+1 (issued a step ago) and the walker's prefetch landed
-        lds_barrier();    // ... for every wave; tile ps-1's slot is free
+        // Tile ps+1 (issued two steps ago) and the word loads of the last step
+        // landed: only that step's kLoadsPerHalf tile loads, issued after its
+        // word loads, may still be in flight (vector loads complete in order).
+        wait_vmcnt<kLoadsPerHalf>();
+        lds_barrier();  // ... for every wave; tile ps-1's slot is free
         land();
-        prepare_load(step + 2);
+        prepare_load(step + 3);
         fetch_next_ids(step);
 #pragma unroll
         for (int k = 0; k < kLoadsPerHalf; ++k) emit_load(k);
@@ -1382,6 +1418,7 @@ k_decode(DecodeArgs a) {
     cj = 0;
     split_k = 0;
   }
+  wait_vmcnt<0>();  // no tile load (zeros past the end) outlives the workgroup's LDS
 }
 
 // ---------------------------------------------------------------------------
