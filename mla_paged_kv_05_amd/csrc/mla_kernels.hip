@@ -1438,45 +1438,66 @@ __global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
   const bool row_ok = row < a.rows;
   __shared__ float amax_s[4][64];
 
-  float m = -INFINITY;
-  for (int s = 0; s < ns; ++s) {
-    const float l = a.part_lse[((int64_t)(s0 + s) * a.groups + g) * kPartialLseFloats + wt * 32 + r32];
-    m = fmaxf(m, l);
-  }
-  float tot = 0.f;
-  if (m != -INFINITY)
-    for (int s = 0; s < ns; ++s) {
-      const float l = a.part_lse[((int64_t)(s0 + s) * a.groups + g) * kPartialLseFloats + wt * 32 + r32];
-      tot += l == -INFINITY ? 0.f : expf(l - m);
+  // this lane's LSE of split s: lsep[s * lstride]
+  const int64_t lstride = (int64_t)a.groups * kPartialLseFloats;
+  const float* lsep = a.part_lse + (int64_t)s0 * lstride + (int64_t)g * kPartialLseFloats + wt * 32 + r32;
+  // LSE = log sum_s exp(lse_s): running max and rescaled sum, eight splits'
+  // loads in flight at a time
+  float m = -INFINITY, tot = 0.f;
+  for (int s = 0; s < ns; s += 8) {
+    float l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l[i] = s + i < ns ? lsep[(s + i) * lstride] : -INFINITY;
+    float mc = m;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mc = fmaxf(mc, l[i]);
+    if (mc != -INFINITY) {
+      float t = m == -INFINITY ? 0.f : tot * expf(m - mc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t += l[i] == -INFINITY ? 0.f : expf(l[i] - mc);
+      tot = t;
+      m = mc;
     }
+  }
   const float lse = m == -INFINITY ? -INFINITY : m + logf(tot);
   // thread (sub, lane) owns d-tiles 4*sub .. 4*sub+3 of its row: acc[4*i + qd]
   // holds quad qd of d-tile 4*sub + i (8 stored quad pairs)
   f32x4 acc[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) acc[k] = f32x4{};
-  if (m != -INFINITY) {
-    for (int s = 0; s < ns; ++s) {
-      const int64_t pidx = (int64_t)(s0 + s) * a.groups + g;
-      const float l = a.part_lse[pidx * kPartialLseFloats + wt * 32 + r32];
-      if (l == -INFINITY) continue;  // lane-divergent skip is fine: loads below are per lane
-      const float w = expf(l - lse);
-      const uint16_t* po = a.part_o + pidx * kPartialOElems + (size_t)wt * (16 * 2 * 64 * 8);
-      uint4 v[8];
+  // O = sum_s exp(lse_s - LSE) O_s, two splits' partials in flight at a time
+  // (a split without keys for the row has lse_s = -inf and weight 0)
+  auto add_split = [&](const uint4 (&v)[8], float w) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const uint4*>(po + ((sub * 8 + k) * 64 + lane) * 8);
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t u[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+      // load k = (d-tile 4*sub + k/2, quad pair k%2); u[e] holds elements
+      // 2e, 2e+1 of the pair, i.e. quad 2*(k%2) + e/2, lanes (2e)%4, (2e+1)%4
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t u[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-        // load k = (d-tile 4*sub + k/2, quad pair k%2); u[e] holds elements
-        // 2e, 2e+1 of the pair, i.e. quad 2*(k%2) + e/2, lanes (2e)%4, (2e+1)%4
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f32x4& t = acc[4 * (k >> 1) + 2 * (k & 1) + (e >> 1)];
-          t[(2 * e) & 3] += w * __uint_as_float(u[e] << 16);
-          t[(2 * e + 1) & 3] += w * __uint_as_float(u[e] & 0xffff0000u);
-        }
+      for (int e = 0; e < 4; ++e) {
+        f32x4& t = acc[4 * (k >> 1) + 2 * (k & 1) + (e >> 1)];
+        t[(2 * e) & 3] += w * __uint_as_float(u[e] << 16);
+        t[(2 * e + 1) & 3] += w * __uint_as_float(u[e] & 0xffff0000u);
       }
+    }
+  };
+  if (m != -INFINITY) {
+    const int64_t pstride = (int64_t)a.groups * kPartialOElems;
+    const uint16_t* pob = a.part_o + (int64_t)s0 * pstride + (int64_t)g * kPartialOElems +
+                          (size_t)wt * (16 * 2 * 64 * 8) + (size_t)((sub * 8) * 64 + lane) * 8;
+    for (int s = 0; s < ns; s += 2) {
+      const bool two = s + 1 < ns;
+      const float l0 = lsep[s * lstride];
+      const float l1 = two ? lsep[(s + 1) * lstride] : -INFINITY;
+      uint4 v0[8], v1[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v0[k] = *reinterpret_cast<const uint4*>(pob + s * pstride + k * 64 * 8);
+      if (two) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v1[k] = *reinterpret_cast<const uint4*>(pob + (s + 1) * pstride + k * 64 * 8);
+      }
+      add_split(v0, l0 == -INFINITY ? 0.f : expf(l0 - lse));
+      if (two) add_split(v1, l1 == -INFINITY ? 0.f : expf(l1 - lse));
     }
   }
   const int64_t orow = (int64_t)b * a.rows + row;
