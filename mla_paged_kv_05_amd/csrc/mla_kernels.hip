@@ -848,9 +848,9 @@ k_decode(DecodeArgs a) {
     }
   };
 
-  // ---- prologue: ids of steps 0..3, loads of steps 0 and 1 (bf16: step 2's
-  // follows in the first piece's prologue, once the walker has landed the
-  // block of step 2's item)
+  // ---- prologue: ids of steps 0..3; the loads of steps 0..2 are issued in
+  // the first piece's prologue (bf16: steps 0 and 1 right after the query
+  // loads, step 2 once the walker has landed the block of its item)
   if constexpr (SPARSE) {
     for (int s = 0; s < min(4, nsteps); ++s) {
       fetch_ids(fb, fj, fh, s);
@@ -858,10 +858,13 @@ k_decode(DecodeArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0);
   }
-  for (int s = 0; s < min(2, nsteps); ++s) {
-    issue_load(s);
-    advance_load();
-  }
+  auto issue_first_loads = [&]() {
+    for (int s = 0; s < min(2, nsteps); ++s) {
+      issue_load(s);
+      advance_load();
+    }
+  };
+  if constexpr (KVF != kKvBf16) issue_first_loads();
 
   constexpr int kQR = q_reg_steps<KVF>();
   uint8_t* qlds = smem + Lay::kQOff + wave * q_lds_wave_bytes<KVF>();
@@ -961,6 +964,9 @@ k_decode(DecodeArgs a) {
         ss = row_sum2(ss);
         srow *= 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
       }
+    }
+    if constexpr (KVF == kKvBf16) {
+      if (first_piece) issue_first_loads();  // after the query loads: latencies overlap
     }
     wait_vmcnt<0>();
     lds_barrier();  // every wave's loads of the piece's first step (and Q in LDS) landed
