@@ -573,7 +573,7 @@ __device__ __forceinline__ void fetch_ids_dma(int32_t* ids_lds, const int32_t* i
   const int first = j * kPage + h * kHalfRows;
   const int32_t* base = indices + row_off + first;
   const int n = max(0, min(kHalfRows, topk - first));
-  dma_buf4(lds_off(ids_lds), (threadIdx.x & 63) * 4, make_rsrc(base, n * 4));
+  dma_buf4(lds_off(ids_lds), fresh_lane() << 2, make_rsrc(base, n * 4));  // lane id not held across the loop
 }
 
 // ---------------------------------------------------------------------------
@@ -1282,7 +1282,6 @@ k_decode(DecodeArgs a) {
       }
     } else {
       // ---- FP8: one bf16 tile, dequantised from the raw ring each step
-      issue_next(step);
       for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
         if (ps > 0) {
           // This step's loads were issued two steps ago; the previous step
@@ -1292,16 +1291,19 @@ k_decode(DecodeArgs a) {
           if (step + 1 >= nsteps) wait_vmcnt<0>();
           else if (SPARSE && step + 3 >= nsteps) wait_vmcnt<kLoadsPerStep>();
           else wait_vmcnt<Lay::kVmPerStep>();
-          lds_barrier();  // every wave's loads of this step landed; slot (step+2)%3 is free
-          issue_next(step);
+          lds_barrier();  // every wave's loads of this step landed
         }
         dequant_codes(smem + Lay::kTileOff, reinterpret_cast<float*>(smem + Lay::kSclOff),
                       smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
-        lds_barrier();
-        if (has_keys(ps)) {
-          f32x16 sc;
-          SmState st;
-          qk_fp8(tile_off(step), sc);
+        lds_barrier();  // the tile is staged; raw slot (step+2)%3 (dequantised last step) is free
+        const bool hk = has_keys(ps);
+        f32x16 sc;
+        SmState st;
+        if (hk) qk_fp8(tile_off(step), sc);
+        // The loads of step+2 go out after S^T: the register reloads inside
+        // S^T wait for every older load, and would otherwise wait for these.
+        issue_next(step);
+        if (hk) {
 #pragma unroll
           for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc, st, key0_of(ps), step);
           rescale_o(st);
