@@ -1,13 +1,14 @@
 """Benchmark of the paged MLA decode hot path on one MI355X.
 
 A step is one pass of the whole path over one batch: the split-KV metadata
-call, the decode kernel and the LSE combine.  The default workload is the
+call, the decode kernel and the LSE combine kernel (``--merge-in-kernel``
+merges the splits inside the decode launch instead).  The default workload is the
 memory-bound bf16 decode (batch 64, s_q 1, h_q 128, d_qk 576, d_v 512,
 seqlens ~ U{1024..8192}, 64-token pages, shuffled block table over a 1.2x
 pool), seeded and synthetic.  Inputs are resident in HBM before timing; the
 KV pool and queries are replicated into several copies that steps rotate
 through, so a step never finds its KV in the 256 MB Infinity Cache left by
-the previous step.  The timed steps launch their three calls from the host
+the previous step.  The timed steps launch their calls from the host
 (``--graph`` replays one captured hipGraph per copy instead); the decode
 kernel's own duration comes from a second, untimed pass.
 
@@ -104,6 +105,9 @@ def main():
     ap.add_argument("--workload", default="dense_b64_h128_L1k-8k")
     ap.add_argument("--rotate", type=int, default=0, help="KV copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--merge-in-kernel", action="store_true",
+                    help="merge the splits inside the decode launch (MLA_FLAG_MERGE_IN_KERNEL) "
+                         "instead of a second launch")
     ap.add_argument("--graph", action="store_true",
                     help="capture each step's three calls once as a hipGraph and replay it "
                          "(default: launch them from the host)")
@@ -152,7 +156,7 @@ def main():
     lib = B.load_library()
     S = B.num_sched_slots(rows, dev)
     meta = torch.empty((S, 8), dtype=torch.int32, device=dev)
-    ns = torch.empty(p.batch + 1, dtype=torch.int32, device=dev)
+    ns = torch.empty(int(lib.mla_num_splits_ints(p.batch)), dtype=torch.int32, device=dev)
     ws = torch.empty(B.workspace_bytes(p.batch, p.s_q, p.h_q, S), dtype=torch.uint8, device=dev)
     out = torch.empty((p.batch, p.s_q, p.h_q, 512), dtype=torch.uint8 if p.fused else torch.bfloat16,
                       device=dev)
@@ -166,7 +170,7 @@ def main():
     for r in range(R):
         pr = B._params(qs[r], kvs[r], bt if idx is None else None, sl, meta, ns, p.causal, idx, p.scale,
                        p.kv_format, ws, out, lse, fused)
-        pr.flags = B.MLA_FLAG_DEFER_COMBINE
+        pr.flags = B.MLA_FLAG_MERGE_IN_KERNEL if args.merge_in_kernel else B.MLA_FLAG_DEFER_COMBINE
         params.append(pr)
     sl_p, meta_p, ns_p = ctypes.c_void_p(sl.data_ptr()), ctypes.c_void_p(meta.data_ptr()), ctypes.c_void_p(ns.data_ptr())
 
@@ -193,7 +197,8 @@ def main():
             st |= lib.mla_decode_timed(ctypes.byref(pr), sh, kev[0], kev[1])
         else:
             st |= lib.mla_decode(ctypes.byref(pr), sh)
-        st |= lib.mla_combine(ctypes.byref(pr), sh)
+        if not args.merge_in_kernel:
+            st |= lib.mla_combine(ctypes.byref(pr), sh)
         if st != 0:
             raise RuntimeError(lib.mla_last_error().decode())
 
@@ -233,6 +238,7 @@ def main():
     start.record(stream)
     run_steps(args.warmup)
     end.record(stream)
+    host = time.perf_counter() - wall0  # host time to enqueue the steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = start.elapsed_time(end) / args.steps
@@ -251,7 +257,8 @@ def main():
             raise RuntimeError(lib.mla_last_error().decode())
         pr = params[(args.warmup + i) % R]
         st = lib.mla_decode_timed(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream), kevs[i][0], kevs[i][1])
-        st |= lib.mla_combine(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream))
+        if not args.merge_in_kernel:
+            st |= lib.mla_combine(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream))
         if st != 0:
             raise RuntimeError(lib.mla_last_error().decode())
     torch.cuda.synchronize()
@@ -266,7 +273,7 @@ def main():
     meta_ms = [mevs[i][0].elapsed_time(mevs[i][1]) for i in range(args.steps)]
     dec_avg = float(np.mean(dec_ms))
     log(f"step {ms * 1e3:.1f} us ({'eager launches' if graphs is None else 'hipGraph replay'}; wall "
-        f"{wall / args.steps * 1e6:.1f} us); decode kernel avg {dec_avg * 1e3:.1f} us (p10 "
+        f"{wall / args.steps * 1e6:.1f} us, host enqueue {host / args.steps * 1e6:.1f} us); decode kernel avg {dec_avg * 1e3:.1f} us (p10 "
         f"{np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); metadata "
         f"{np.mean(meta_ms) * 1e3:.1f} us; rotation {R}")
 
@@ -285,11 +292,13 @@ def main():
                    "d_v": 512, "page": 64, "kv_format": p.kv_format, "causal": bool(p.causal),
                    "sparse_topk": topk, "fused": bool(p.fused), "parallelism": "single GPU",
                    "kv_copies_rotated": R,
-                   "launch": "eager" if graphs is None else "hipGraph per step (metadata, decode, combine)"},
+                   "launch": "eager" if graphs is None else "hipGraph per step (metadata, decode, combine)",
+                   "combine": "in the decode launch" if args.merge_in_kernel else "separate launch"},
         "tflops": round(tflops, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_decode", "kernel_avg_us": round(dec_avg * 1e3, 2),
+                     "kernel": "k_decode" + (" (with the in-kernel LSE combine)" if args.merge_in_kernel else ""),
+                     "kernel_avg_us": round(dec_avg * 1e3, 2),
                      "algorithmic_bytes_per_launch": nbytes},
     }
     if not args.no_cpu:

@@ -72,7 +72,7 @@ int32_t mla_num_sched_slots(int32_t device, int32_t rows_per_kv_head);
 
 /* [host] int32 element counts of the two metadata arrays. */
 size_t mla_sched_meta_ints(int32_t num_slots);  /* = 8 * num_slots  */
-size_t mla_num_splits_ints(int32_t batch);      /* = batch + 1      */
+size_t mla_num_splits_ints(int32_t batch);      /* = 6 * batch + 4  */
 
 /* Split-KV scheduling metadata (once per decoding step; reusable by every
  * decode call with the same cache_seqlens contents, rows and topk).
@@ -82,7 +82,10 @@ size_t mla_num_splits_ints(int32_t batch);      /* = batch + 1      */
  *   topk              0 = dense; > 0: sparse with topk indices per query row
  *   num_slots         S, normally mla_num_sched_slots()
  *   sched_meta        int32 [S][8] out: per slot {b0, j0, b1, j1_end, k0, items, 0, 0}
- *   num_splits        int32 [batch+1] out: prefix offsets of per-sequence splits
+ *   num_splits        int32 [mla_num_splits_ints(batch)] out: [0..batch] prefix
+ *                     offsets of per-sequence splits, then a control area for
+ *                     the decode's in-kernel combine (cleared here; every
+ *                     decode that merges in-kernel leaves it cleared again)
  * The split rule: a sequence has n_b = ceil(len/64) work items (ceil(topk/64)
  * when sparse; an empty sequence keeps one item with no KV); with
  * F = max(1, ceil(min(rows,128)/32)), the items are laid on a line where
@@ -115,7 +118,7 @@ typedef struct mla_decode_params {
   const int32_t* indices;      /* NULL = dense; else int32 [batch][s_q][topk] flat token ids, -1 = masked */
   int32_t topk;
   const int32_t* sched_meta;   /* from mla_get_metadata with the same rows and topk         */
-  const int32_t* num_splits;
+  int32_t* num_splits;         /* the decode updates (and restores) its control area */
   int32_t num_slots;
   void* workspace;             /* >= mla_workspace_bytes(), 256-byte aligned                */
   size_t workspace_bytes;
@@ -132,12 +135,21 @@ typedef struct mla_decode_params {
 /* mla_decode leaves split partials in the workspace for a later
  * mla_combine call on the same stream (e.g. to time or overlap it). */
 #define MLA_FLAG_DEFER_COMBINE 1u
+/* mla_decode merges the splits inside the decode launch: a cooperative
+ * launch (every workgroup resident) whose waves, once out of decode work,
+ * merge each split sequence as soon as all its pieces have arrived.  One
+ * kernel per call instead of two; plain (not fused) output, at most 256
+ * query rows, not under stream capture -- otherwise the flag is ignored.
+ * On the config-2 workload it measured slower than the two launches. */
+#define MLA_FLAG_MERGE_IN_KERNEL 2u
 
 /* Paged MLA decode: O and LSE for every query row (see the file comment).
  * A row that sees no key gets O = 0 and LSE = -inf.  Sequences whose work
  * the schedule splits write partials (O in bf16, LSE in fp32) to the
- * workspace and a combine
- * pass merges them by LSE; others write their output directly.
+ * workspace and a combine launch merges them by LSE (or the decode launch
+ * itself, with MLA_FLAG_MERGE_IN_KERNEL); others write their output
+ * directly.  Decode calls that share a num_splits buffer must be ordered on
+ * one stream.
  * Supported: h_kv = 1, d_qk = 576, d_v = 512, page 64, s_q*h_q <= 65536;
  * sparse needs causal = 0 and (s_q == 1 or h_q % 128 == 0); FP8 KV needs
  * indices; fused needs s_q*h_q of whole heads as above.

@@ -71,6 +71,7 @@ class DecodeParams(ctypes.Structure):
 
 
 MLA_FLAG_DEFER_COMBINE = 1
+MLA_FLAG_MERGE_IN_KERNEL = 2
 
 
 EXPORTED = ["mla_num_sched_slots", "mla_sched_meta_ints", "mla_num_splits_ints", "mla_get_metadata",
@@ -150,7 +151,7 @@ def get_mla_metadata(cache_seqlens: torch.Tensor, rows_per_kv_head: int, h_kv: i
     S = num_slots if num_slots is not None else num_sched_slots(rows_per_kv_head, dev)
     B = cache_seqlens.shape[0]
     meta = torch.empty((S, 8), dtype=torch.int32, device=dev)
-    ns = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    ns = torch.empty(int(lib.mla_num_splits_ints(B)), dtype=torch.int32, device=dev)
     _check(lib.mla_get_metadata(_ptr(cache_seqlens), B, int(rows_per_kv_head), int(h_kv), int(topk),
                                 S, _ptr(meta), _ptr(ns), _stream(dev)))
     return meta, ns

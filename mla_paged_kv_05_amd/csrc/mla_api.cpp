@@ -71,7 +71,7 @@ int32_t mla_num_sched_slots(int32_t device, int32_t rows_per_kv_head) {
 
 size_t mla_sched_meta_ints(int32_t num_slots) { return num_slots > 0 ? 8 * (size_t)num_slots : 0; }
 
-size_t mla_num_splits_ints(int32_t batch) { return batch >= 0 ? (size_t)batch + 1 : 0; }
+size_t mla_num_splits_ints(int32_t batch) { return batch >= 0 ? mla::splits_ints(batch) : 0; }
 
 mla_status mla_get_metadata(const int32_t* cache_seqlens, int32_t batch, int32_t rows_per_kv_head,
                             int32_t h_kv, int32_t topk, int32_t num_slots, int32_t* sched_meta,
@@ -116,7 +116,8 @@ static mla_status build_args(const mla_decode_params* p, mla::DecodeArgs& a, boo
     return fail(MLA_ERR_INVALID_ARG, "q, kv, out, lse and cache_seqlens must be non-NULL");
   if (!aligned(p->q, 16) || !aligned(p->kv, 16) || !aligned(p->out, 16))
     return fail(MLA_ERR_INVALID_ARG, "q, kv and out must be 16-byte aligned");
-  if (p->flags & ~MLA_FLAG_DEFER_COMBINE) return fail(MLA_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
+  if (p->flags & ~(MLA_FLAG_DEFER_COMBINE | MLA_FLAG_MERGE_IN_KERNEL))
+    return fail(MLA_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
   if (p->num_blocks < 0) return fail(MLA_ERR_INVALID_ARG, "num_blocks=%lld", (long long)p->num_blocks);
   sparse = p->indices != nullptr;
   if (sparse) {
@@ -187,7 +188,24 @@ static mla_status decode_impl(const mla_decode_params* p, void* stream, hipEvent
   if (st != MLA_OK) return st;
   if (p->batch == 0) return MLA_OK;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = mla::launch_decode(a, p->kv_format, sparse, p->fused != 0, s, start, stop);
+  hipError_t e;
+  // Merge the splits inside the decode launch (cooperative) when asked to,
+  // unless the caller defers the combine, the call is fused, the row groups
+  // exceed the control area, or the stream is being captured (a cooperative
+  // launch is not captured).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    cap = hipStreamCaptureStatusActive;
+  }
+  if ((p->flags & MLA_FLAG_MERGE_IN_KERNEL) && !(p->flags & MLA_FLAG_DEFER_COMBINE) && !p->fused &&
+      a.groups <= mla::kCtlGroups && cap == hipStreamCaptureStatusNone) {
+    a.ctl = p->num_splits + p->batch + 1;
+    e = mla::launch_decode(a, p->kv_format, sparse, p->fused != 0, s, start, stop);
+    if (e == hipSuccess) return MLA_OK;
+    a.ctl = nullptr;  // cannot be cooperative here: decode, then a combine launch
+  }
+  e = mla::launch_decode(a, p->kv_format, sparse, p->fused != 0, s, start, stop);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (p->flags & MLA_FLAG_DEFER_COMBINE) return MLA_OK;
   e = mla::launch_combine(a, p->fused != 0, s);

@@ -27,6 +27,13 @@ inline int sched_piece_cost(int rows) {
 // Row groups of 128 rows a decode call is cut into.
 inline int row_groups(int rows) { return (rows + kRowsPerWg - 1) / kRowsPerWg; }
 
+// The num_splits buffer: the split prefix [batch+1], then the in-kernel
+// combine's control area: tasks, claim counter, error word, the split
+// sequences [batch], and per (sequence, row group <= 2) counters of arrived
+// pieces and finished tasks [batch][2] each.
+constexpr int kCtlGroups = 2;
+inline size_t splits_ints(int batch) { return (size_t)batch + 1 + 3 + (size_t)batch * (1 + 2 * kCtlGroups); }
+
 // Partial results of one (split, row group): 128 rows x 512 fp32 in the
 // decode kernel's register order plus 128 fp32 LSEs.
 constexpr size_t kPartialOElems = (size_t)kRowsPerWg * kDv;   // bf16 elements
@@ -39,7 +46,8 @@ struct DecodeArgs {
   const int32_t* seqlens;
   const int32_t* indices;    // sparse only
   const int32_t* meta;       // [S][8]
-  const int32_t* num_splits; // [batch+1]
+  const int32_t* num_splits; // [batch+1] split prefix
+  int32_t* ctl;              // in-kernel combine control area (null: separate combine)
   uint16_t* part_o;          // bf16 [max_partials][G][128*512] (register order)
   float* part_lse;           // [max_partials][G][128]
   void* out;                 // bf16 or e4m3 [batch][rows][512]
@@ -57,6 +65,9 @@ enum KvFormat { kKvBf16 = 0, kKvFp8V32 = 1 };
 
 hipError_t launch_sched(const int32_t* seqlens, int batch, int rows, int topk, int num_slots,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream);
+// With a.ctl set the decode is launched cooperatively and merges the splits
+// itself; a launch that cannot be cooperative returns an error (the caller
+// then clears a.ctl and uses launch_combine).
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool fused,
                          hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t launch_combine(const DecodeArgs& a, bool fused, hipStream_t stream);

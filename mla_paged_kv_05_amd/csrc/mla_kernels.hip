@@ -60,6 +60,22 @@ constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer, dword3 for gfx9 f
 // slot indices): move them to scalar registers so buffer descriptors, LDS
 // bases and loop bounds stay scalar.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// Buffer accesses with cache policy sc0 sc1: they go past the CU's L1 and
+// the XCD's L2 to the coherent memory side, so a store that has completed is
+// seen by a load of this kind from any XCD without L2 write-back or
+// invalidation.  Used for the split partials the in-kernel combine reads.
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+constexpr int kCoherent = 1 | 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// A wave-uniform pointer, forced into SGPRs (for "s" asm operands).
+template <typename T>
+__device__ __forceinline__ const T* uni_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
 
 // Read-only int32 arrays indexed by wave-uniform values (schedule, lengths,
 // block table): read through the constant address space so they become
@@ -306,6 +322,30 @@ k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
     s0 += (p0 + items - 1) / cap - p0 / cap + 1;
   }
   if (tid == 0) num_splits[B] = tot_s;
+  // in-kernel combine control area: the split sequences in order, zeroed
+  // counters, and the task count (4 row tiles per row group)
+  {
+    int32_t* ctl = num_splits + B + 1;
+    const int G = (rows + kRowsPerWg - 1) / kRowsPerWg;
+    auto nsplit = [&](int b) {
+      int items = U[b + 1] - U[b] - F;
+      items = items > 0 ? items : 1;
+      int p0 = U[b] + F;
+      return (p0 + items - 1) / cap - p0 / cap + 1;
+    };
+    int fc = 0;
+    for (int b = lo; b < hi; ++b) fc += nsplit(b) > 1;
+    int tot_f;
+    int f0 = block_scan_exclusive(fc, wsum, &tot_f);
+    for (int b = lo; b < hi; ++b)
+      if (nsplit(b) > 1) ctl[3 + f0++] = b;
+    for (int i = tid; i < 2 * kCtlGroups * B; i += kSchedThreads) ctl[3 + B + i] = 0;
+    if (tid == 0) {
+      ctl[0] = tot_f * (G <= kCtlGroups ? G : 0) * 16;  // 16 combine tasks per (sequence, row group)
+      ctl[1] = 0;
+      ctl[2] = 0;
+    }
+  }
   // pass 3: each slot's first and last item
   auto last_pos = [&](int b) {  // position of the last item of sequence b
     int n = U[b + 1] - U[b] - F;
@@ -426,7 +466,7 @@ __device__ __forceinline__ void load_row_bf16_sparse(uint8_t* slot, const uint8_
   if (k < kHalfRows / kWaves) {
     const int r = wave + kWaves * k;
     const int id = uni(r < nvalid ? ids[r] : -1);
-    const uint8_t* src = id >= 0 ? kv + (int64_t)id * kRowBytes : g_zero_row;
+    const uint8_t* src = uni_ptr(id >= 0 ? kv + (int64_t)id * kRowBytes : g_zero_row);
     dma_glb16_s(base + r * kMainStride, l16, src);
   } else {
     const int rr = 8 * wave + (l16 >> 7);
@@ -650,6 +690,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+template <bool FUSED>
+__device__ void combine_phase(const DecodeArgs& a, uint8_t* lds);
+
 template <int KVF, bool SPARSE, bool FUSED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_decode(DecodeArgs a) {
@@ -680,7 +723,12 @@ k_decode(DecodeArgs a) {
   }
   const int32_t* ms = a.meta + 8 * slot;
   const int b0 = uni(sload(ms, 0));
-  if (b0 < 0) return;
+  if (b0 < 0) {  // no decode work: only combine tasks
+    if constexpr (!FUSED) {
+      if (a.ctl) combine_phase<FUSED>(a, smem);
+    }
+    return;
+  }
   const int j0 = uni(sload(ms, 1)), b1 = uni(sload(ms, 2)), j1 = uni(sload(ms, 3)),
             nitems = uni(sload(ms, 5));
   int split_k = uni(sload(ms, 4));
@@ -1404,21 +1452,33 @@ k_decode(DecodeArgs a) {
       } else {
         // partial of split `split_k` of sequence cb, row group g: O/l rounded
         // to bf16, stored in register order [wave][d-tile][quad pair][lane][8]
+        // (coherent stores: the in-kernel combine may read them from another XCD)
         const int64_t pidx = (int64_t)uni(sload(a.num_splits, cb) + split_k) * a.groups + g;
-        uint16_t* po = a.part_o + pidx * kPartialOElems + (size_t)wave * (16 * 2 * 64 * 8);
+        const __amdgpu_buffer_rsrc_t prs = buf_rsrc(uni_ptr(a.part_o + pidx * kPartialOElems), kPartialOElems * 2);
+        const int vbase = (wave * (16 * 2 * 64 * 8) + lane * 8) * 2;
 #pragma unroll
         for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
           for (int q2 = 0; q2 < 2; ++q2) {
-            uint32_t w[4];
+            u32x4 w;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const __bf16 lo = (__bf16)(o[mt][8 * q2 + 2 * e] * inv), hi = (__bf16)(o[mt][8 * q2 + 2 * e + 1] * inv);
               w[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
             }
-            *reinterpret_cast<uint4*>(po + ((mt * 2 + q2) * 64 + lane) * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+            __builtin_amdgcn_raw_buffer_store_b128(w, prs, vbase + (mt * 2 + q2) * 64 * 8 * 2, 0, kCoherent);
           }
-        if (half == 0) a.part_lse[pidx * kPartialLseFloats + wave * 32 + r32] = lse2 * kLn2;
+        if (half == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2 * kLn2),
+                                                buf_rsrc(uni_ptr(a.part_lse + pidx * kPartialLseFloats), kPartialLseFloats * 4),
+                                                (wave * 32 + r32) * 4, 0, kCoherent);
+        if (!FUSED && a.ctl) {
+          // every wave's stores completed (and are visible device-wide);
+          // then the piece counts itself in
+          wait_vmcnt<0>();
+          __syncthreads();
+          if (tid == 0) __hip_atomic_fetch_add(&a.ctl[3 + a.batch + 2 * cb + g], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
     // next piece: first item of the following sequence
@@ -1427,35 +1487,65 @@ k_decode(DecodeArgs a) {
     split_k = 0;
   }
   wait_vmcnt<0>();  // no tile load (zeros past the end) outlives the workgroup's LDS
+  // (the fused decode merges in a separate launch: its main loop has no
+  // registers to spare for the merge code)
+  if constexpr (!FUSED) {
+    if (a.ctl) combine_phase<FUSED>(a, smem);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// LSE combine: one workgroup per (sequence, row group, 32-row wave tile).
-// Thread (sub, lane): lane's row, 16 of the 64 (d-tile, quad) float4s.
+// LSE combine of the 32 rows wt*32.. of row group g of sequence b: wave
+// `sub` (lanes `lane`) merges d-tiles 4*sub .. 4*sub+3; thread (sub, lane)
+// holds lane's row and 16 of the 64 (d-tile, quad) float4s.  Plain output
+// needs one wave per sub; fused output needs all four subs of the rows in
+// one workgroup (amax_s: 1 KB of LDS for the row amax across them).
 // ---------------------------------------------------------------------------
-template <bool FUSED>
-__global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
-  const int wt = blockIdx.x & 3;
-  const int g = (blockIdx.x >> 2) % a.groups;
-  const int b = (blockIdx.x >> 2) / a.groups;
+template <bool FUSED, bool COHERENT>
+__device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub, int lane,
+                             float (*amax_s)[64]) {
   const int s0 = a.num_splits[b], ns = a.num_splits[b + 1] - s0;
   if (ns <= 1) return;
-  const int tid = threadIdx.x, lane = tid & 63, sub = tid >> 6;
   const int half = lane >> 5, r32 = lane & 31;
   const int row = g * kRowsPerWg + wt * 32 + r32;
   const bool row_ok = row < a.rows;
-  __shared__ float amax_s[4][64];
 
   // this lane's LSE of split s: lsep[s * lstride]
   const int64_t lstride = (int64_t)a.groups * kPartialLseFloats;
   const float* lsep = a.part_lse + (int64_t)s0 * lstride + (int64_t)g * kPartialLseFloats + wt * 32 + r32;
+  // COHERENT (in-kernel combine): partials read past L1 and L2, as stored
+  auto lse_of = [&](int s) -> float {
+    if constexpr (COHERENT)
+      return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          buf_rsrc(uni_ptr(a.part_lse + ((int64_t)(s0 + s) * a.groups + g) * kPartialLseFloats), kPartialLseFloats * 4),
+          (wt * 32 + r32) * 4, 0, kCoherent));
+    else
+      return lsep[s * lstride];
+  };
+  auto load_split = [&](int s, uint4 (&v)[8]) {
+    if constexpr (COHERENT) {
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
+          uni_ptr(a.part_o + ((int64_t)(s0 + s) * a.groups + g) * kPartialOElems), kPartialOElems * 2);
+      const int vb = (wt * (16 * 2 * 64 * 8) + ((sub * 8) * 64 + lane) * 8) * 2;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, vb + k * 64 * 8 * 2, 0, kCoherent);
+        v[k] = make_uint4(t[0], t[1], t[2], t[3]);
+      }
+    } else {
+      const uint16_t* pb = a.part_o + ((int64_t)(s0 + s) * a.groups + g) * kPartialOElems +
+                           (size_t)wt * (16 * 2 * 64 * 8) + (size_t)((sub * 8) * 64 + lane) * 8;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const uint4*>(pb + k * 64 * 8);
+    }
+  };
   // LSE = log sum_s exp(lse_s): running max and rescaled sum, eight splits'
   // loads in flight at a time
   float m = -INFINITY, tot = 0.f;
   for (int s = 0; s < ns; s += 8) {
     float l[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) l[i] = s + i < ns ? lsep[(s + i) * lstride] : -INFINITY;
+    for (int i = 0; i < 8; ++i) l[i] = s + i < ns ? lse_of(s + i) : -INFINITY;
     float mc = m;
 #pragma unroll
     for (int i = 0; i < 8; ++i) mc = fmaxf(mc, l[i]);
@@ -1490,20 +1580,13 @@ __global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
     }
   };
   if (m != -INFINITY) {
-    const int64_t pstride = (int64_t)a.groups * kPartialOElems;
-    const uint16_t* pob = a.part_o + (int64_t)s0 * pstride + (int64_t)g * kPartialOElems +
-                          (size_t)wt * (16 * 2 * 64 * 8) + (size_t)((sub * 8) * 64 + lane) * 8;
     for (int s = 0; s < ns; s += 2) {
       const bool two = s + 1 < ns;
-      const float l0 = lsep[s * lstride];
-      const float l1 = two ? lsep[(s + 1) * lstride] : -INFINITY;
+      const float l0 = lse_of(s);
+      const float l1 = two ? lse_of(s + 1) : -INFINITY;
       uint4 v0[8], v1[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v0[k] = *reinterpret_cast<const uint4*>(pob + s * pstride + k * 64 * 8);
-      if (two) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v1[k] = *reinterpret_cast<const uint4*>(pob + (s + 1) * pstride + k * 64 * 8);
-      }
+      load_split(s, v0);
+      if (two) load_split(s + 1, v1);
       add_split(v0, l0 == -INFINITY ? 0.f : expf(l0 - lse));
       if (two) add_split(v1, l1 == -INFINITY ? 0.f : expf(l1 - lse));
     }
@@ -1576,7 +1659,78 @@ __global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
   }
 }
 
+// The combine as its own launch: one workgroup per (sequence, row group,
+// 32-row tile).
+template <bool FUSED>
+__global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
+  __shared__ float amax_s[4][64];
+  const int wt = blockIdx.x & 3;
+  const int g = (blockIdx.x >> 2) % a.groups;
+  const int b = (blockIdx.x >> 2) / a.groups;
+  combine_rows<FUSED, false>(a, b, g, wt, threadIdx.x >> 6, threadIdx.x & 63, amax_s);
+}
+
 // ---------------------------------------------------------------------------
+// In-kernel combine (decode launched cooperatively, so every workgroup is
+// resident; plain output only).  Each split piece, once its partial is
+// stored (coherently) and complete, counts itself in arrived[b][g].  A wave
+// out of decode work claims combine tasks (b, g, 32-row tile, d-quarter) in
+// sequence order from one counter, 16 per (b, g) -- as many as the waves of
+// the launch for 64 split sequences, so a task seldom waits for a claimer --
+// and waits until every piece of (b, g) has arrived.  The last of the 16
+// tasks of (b, g) clears its counters and the last claim clears the claim
+// counter, so the metadata is ready for the next decode call.  The wait is
+// bounded in time: past it the task is skipped and an error word is set.
+// Control area ctl (after the split prefix, written by the scheduler):
+//   [0] tasks T   [1] claim counter   [2] error word
+//   [3 .. 3+B) split sequences in order   then arrived[B][2], done[B][2]
+// ---------------------------------------------------------------------------
+constexpr int kCombineTasksPerGroup = 16;
+template <bool FUSED>
+__device__ void combine_phase(const DecodeArgs& a, uint8_t* /*lds*/) {
+  static_assert(!FUSED, "the fused output merges in its own launch");
+  int32_t* ctl = a.ctl;
+  const int B = a.batch, G = a.groups;
+  int32_t* list = ctl + 3;
+  int32_t* arrived = ctl + 3 + B;
+  int32_t* done = arrived + 2 * B;
+  const int lane = fresh_lane();
+  const int T = uni(ctl[0]);
+  const int claimers = (int)gridDim.x * kWaves;
+  for (;;) {
+    int t = 0;
+    if (lane == 0) t = atomicAdd(&ctl[1], 1);
+    t = uni(t);
+    if (t >= T) {
+      if (lane == 0 && t == T + claimers - 1)
+        __hip_atomic_store(&ctl[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    const int i = t / (kCombineTasksPerGroup * G), g = (t / kCombineTasksPerGroup) % G;
+    const int wt = (t >> 2) & 3, sub = t & 3;
+    const int b = uni(list[i]);
+    const int ns = uni(a.num_splits[b + 1] - a.num_splits[b]);
+    int ok = 1;
+    if (lane == 0) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(&arrived[2 * b + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < ns) {
+        __builtin_amdgcn_s_sleep(32);  // ~2k cycles between polls: a thousand waiting waves stay light on memory
+        if (__builtin_amdgcn_s_memrealtime() - t0 > 100000000ull) {  // 1 s at 100 MHz
+          ok = 0;
+          __hip_atomic_store(&ctl[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    if (uni(ok)) combine_rows<false, true>(a, b, g, wt, sub, lane, nullptr);
+    wait_vmcnt<0>();  // this task's output is written before it counts as done
+    if (lane == 0 && atomicAdd(&done[2 * b + g], 1) == kCombineTasksPerGroup - 1) {
+      __hip_atomic_store(&arrived[2 * b + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&done[2 * b + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Debug gather: stage both halves of one work item with the decode kernel's
 // loaders (and dequantiser), copy them out un-swizzled as [64][576] bf16.
@@ -1635,6 +1789,23 @@ template <int KVF, bool SPARSE, bool FUSED>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
                                   hipEvent_t stop) {
   const int grid = a.num_slots * a.groups;
+  if (a.ctl) {
+    // every workgroup must be resident: the combine tasks wait on other
+    // workgroups' pieces
+    if (start) {
+      const hipError_t e = hipEventRecord(start, stream);
+      if (e != hipSuccess) return e;
+    }
+    DecodeArgs ac = a;
+    void* args[] = {&ac};
+    const hipError_t e = hipLaunchCooperativeKernel((const void*)k_decode<KVF, SPARSE, FUSED>, dim3(grid),
+                                                    dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();  // clear it: the caller falls back to the separate combine
+      return e;
+    }
+    return stop ? hipEventRecord(stop, stream) : hipSuccess;
+  }
   if (start || stop)
     hipExtLaunchKernelGGL((k_decode<KVF, SPARSE, FUSED>), dim3(grid), dim3(kThreads), 0, stream, start,
                           stop, 0, a);

@@ -18,7 +18,7 @@ def _step_fn(torch, lib, B, p, t, S):
     rows = p.s_q * p.h_q
     sparse = p.indices is not None
     meta = torch.empty((S, 8), dtype=torch.int32, device=dev)
-    ns = torch.empty(p.batch + 1, dtype=torch.int32, device=dev)
+    ns = torch.empty(int(lib.mla_num_splits_ints(p.batch)), dtype=torch.int32, device=dev)
     ws = torch.empty(B.workspace_bytes(p.batch, p.s_q, p.h_q, S), dtype=torch.uint8, device=dev)
     out = torch.empty((p.batch, p.s_q, p.h_q, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((p.batch, p.s_q, p.h_q), dtype=torch.float32, device=dev)

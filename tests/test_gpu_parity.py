@@ -110,7 +110,17 @@ def test_metadata_bit_exact():
         torch.cuda.synchronize()
         rm, rn = oracle.sched_plan(np.array(sl, dtype=np.int32), rows, topk, S)
         assert np.array_equal(meta.cpu().numpy(), rm)
-        assert np.array_equal(ns.cpu().numpy(), rn)
+        g = ns.cpu().numpy()
+        B = len(sl)
+        assert np.array_equal(g[:B + 1], rn)
+        # control area of the in-kernel combine: task count, cleared
+        # counters, the split sequences in order
+        split = [b for b in range(B) if rn[b + 1] - rn[b] > 1]
+        G = (rows + 127) // 128
+        ctl = g[B + 1:]
+        assert ctl[0] == len(split) * (G if G <= 2 else 0) * 16 and ctl[1] == 0 and ctl[2] == 0
+        assert list(ctl[3:3 + len(split)]) == split
+        assert not ctl[3 + B:3 + 5 * B].any()
 
 
 def _bf16_round_f32(x):
@@ -233,7 +243,7 @@ def test_decode_timed_matches_decode():
     lib = B.load_library()
     S = 16
     meta = torch.empty((S, 8), dtype=torch.int32, device="cuda:0")
-    ns = torch.empty(p.batch + 1, dtype=torch.int32, device="cuda:0")
+    ns = torch.empty(int(lib.mla_num_splits_ints(p.batch)), dtype=torch.int32, device="cuda:0")
     sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     assert lib.mla_get_metadata(ctypes.c_void_p(t["seqlens"].data_ptr()), p.batch, 128, 1, 0, S,
                                 ctypes.c_void_p(meta.data_ptr()), ctypes.c_void_p(ns.data_ptr()), sh) == 0
