@@ -1541,11 +1541,20 @@ __device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub,
   };
   // LSE = log sum_s exp(lse_s): running max and rescaled sum, eight splits'
   // loads in flight at a time
+  // The first eight splits' LSEs and the first four splits' partials are
+  // loaded together (one round trip for the common case ns <= 4).
+  float l8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) l8[i] = i < ns ? lse_of(i) : -INFINITY;
+  uint4 v[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j < ns) load_split(j, v[j]);
   float m = -INFINITY, tot = 0.f;
   for (int s = 0; s < ns; s += 8) {
     float l[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) l[i] = s + i < ns ? lse_of(s + i) : -INFINITY;
+    for (int i = 0; i < 8; ++i) l[i] = s == 0 ? l8[i] : (s + i < ns ? lse_of(s + i) : -INFINITY);
     float mc = m;
 #pragma unroll
     for (int i = 0; i < 8; ++i) mc = fmaxf(mc, l[i]);
@@ -1563,8 +1572,8 @@ __device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub,
   f32x4 acc[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) acc[k] = f32x4{};
-  // O = sum_s exp(lse_s - LSE) O_s, two splits' partials in flight at a time
-  // (a split without keys for the row has lse_s = -inf and weight 0)
+  // O = sum_s exp(lse_s - LSE) O_s, four splits' partials in flight at a
+  // time (a split without keys for the row has lse_s = -inf and weight 0)
   auto add_split = [&](const uint4 (&v)[8], float w) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -1579,16 +1588,18 @@ __device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub,
       }
     }
   };
+  auto weight = [&](float l) { return l == -INFINITY ? 0.f : expf(l - lse); };
   if (m != -INFINITY) {
-    for (int s = 0; s < ns; s += 2) {
-      const bool two = s + 1 < ns;
-      const float l0 = lse_of(s);
-      const float l1 = two ? lse_of(s + 1) : -INFINITY;
-      uint4 v0[8], v1[8];
-      load_split(s, v0);
-      if (two) load_split(s + 1, v1);
-      add_split(v0, l0 == -INFINITY ? 0.f : expf(l0 - lse));
-      if (two) add_split(v1, l1 == -INFINITY ? 0.f : expf(l1 - lse));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < ns) add_split(v[j], weight(l8[j]));
+    for (int s = 4; s < ns; s += 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (s + j < ns) load_split(s + j, v[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (s + j < ns) add_split(v[j], weight(s + j < 8 ? l8[s + j] : lse_of(s + j)));
     }
   }
   const int64_t orow = (int64_t)b * a.rows + row;
