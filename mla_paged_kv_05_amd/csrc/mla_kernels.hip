@@ -547,14 +547,9 @@ __device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const u
     uint32_t w[4];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      typedef __attribute__((ext_vector_type(2))) float f2;
-      f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], false);
-      f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], true);
-      __bf16 b0 = (__bf16)lo[0], b1 = (__bf16)lo[1], b2 = (__bf16)hi[0], b3 = (__bf16)hi[1];
-      w[2 * hh] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-      w[2 * hh + 1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+      // two codes -> two bf16 in one instruction; with scale 1 the result is exact
+      w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], 1.0f, false));
+      w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], 1.0f, true));
     }
     *reinterpret_cast<uint4*>(tile + r * kMainStride + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
