@@ -230,10 +230,13 @@ __device__ __forceinline__ float row_sum2(float v) {
 // ---------------------------------------------------------------------------
 // Split-KV scheduler (one workgroup).  Implements the split rule stated in
 // mla.h; every per-sequence quantity is a prefix sum, every slot finds its
-// first item by binary search, so there is no serial walk.
+// first item by binary search, so there is no serial walk.  Batches of up to
+// kSchedSmallBatch sequences run on a single wave, whose scans need no
+// cross-wave barrier; larger ones on 1024 threads.
 // ---------------------------------------------------------------------------
-constexpr int kSchedThreads = 1024;
+constexpr int kSchedSmallBatch = 256;
 
+template <int NT>
 __device__ int block_scan_exclusive(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int x = v;
@@ -242,30 +245,37 @@ __device__ int block_scan_exclusive(int v, int* wsum, int* total) {
     int y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
-  if (lane == 63) wsum[w] = x;
-  __syncthreads();
-  if (w == 0) {
-    int s = lane < kSchedThreads / 64 ? wsum[lane] : 0;
+  if constexpr (NT == 64) {
+    *total = __shfl(x, 63, 64);
+    return x - v;
+  } else {
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    if (w == 0) {
+      int s = lane < NT / 64 ? wsum[lane] : 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(s, o, 64);
-      if (lane >= o) s += y;
+      for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(s, o, 64);
+        if (lane >= o) s += y;
+      }
+      if (lane < NT / 64) wsum[lane] = s;
     }
-    if (lane < kSchedThreads / 64) wsum[lane] = s;
+    __syncthreads();
+    int base = w > 0 ? wsum[w - 1] : 0;
+    *total = wsum[NT / 64 - 1];
+    __syncthreads();
+    return base + x - v;
   }
-  __syncthreads();
-  int base = w > 0 ? wsum[w - 1] : 0;
-  *total = wsum[kSchedThreads / 64 - 1];
-  __syncthreads();
-  return base + x - v;
 }
 
-__global__ void __launch_bounds__(kSchedThreads)
+template <int NT, int MAXB>
+__global__ void __launch_bounds__(NT)
 k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
         int32_t* __restrict__ meta, int32_t* __restrict__ num_splits) {
-  __shared__ int32_t U[kMaxBatch + 1];   // cost prefix: start of sequence b on the line
-  __shared__ int32_t I[kMaxBatch + 1];   // item prefix
-  __shared__ int wsum[kSchedThreads / 64];
+  constexpr int kSchedThreads = NT;
+  __shared__ int32_t U[MAXB + 1];   // cost prefix: start of sequence b on the line
+  __shared__ int32_t I[MAXB + 1];   // item prefix
+  __shared__ int wsum[NT / 64];
   const int tid = threadIdx.x;
   const int F = [&] {
     int m = rows < kRowsPerWg ? rows : kRowsPerWg;
@@ -287,8 +297,8 @@ k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
     is += n > 0 ? n : 1;
   }
   int tot_c, tot_i;
-  int c0 = block_scan_exclusive(cs, wsum, &tot_c);
-  int i0 = block_scan_exclusive(is, wsum, &tot_i);
+  int c0 = block_scan_exclusive<NT>(cs, wsum, &tot_c);
+  int i0 = block_scan_exclusive<NT>(is, wsum, &tot_i);
   for (int b = lo; b < hi; ++b) {
     int n = nblk(b);
     U[b] = c0;
@@ -313,7 +323,7 @@ k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
     ss += (p0 + items - 1) / cap - p0 / cap + 1;
   }
   int tot_s;
-  int s0 = block_scan_exclusive(ss, wsum, &tot_s);
+  int s0 = block_scan_exclusive<NT>(ss, wsum, &tot_s);
   for (int b = lo; b < hi; ++b) {
     num_splits[b] = s0;
     int items = U[b + 1] - U[b] - F;
@@ -336,7 +346,7 @@ k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
     int fc = 0;
     for (int b = lo; b < hi; ++b) fc += nsplit(b) > 1;
     int tot_f;
-    int f0 = block_scan_exclusive(fc, wsum, &tot_f);
+    int f0 = block_scan_exclusive<NT>(fc, wsum, &tot_f);
     for (int b = lo; b < hi; ++b)
       if (nsplit(b) > 1) ctl[3 + f0++] = b;
     for (int i = tid; i < 2 * kCtlGroups * B; i += kSchedThreads) ctl[3 + B + i] = 0;
@@ -1786,8 +1796,12 @@ __global__ void __launch_bounds__(kThreads) k_debug_gather(DecodeArgs a, int b, 
 // ---------------------------------------------------------------------------
 hipError_t launch_sched(const int32_t* seqlens, int batch, int rows, int topk, int num_slots,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream) {
-  hipLaunchKernelGGL(k_sched, dim3(1), dim3(kSchedThreads), 0, stream, seqlens, batch, rows, topk,
-                     num_slots, meta, num_splits);
+  if (batch <= kSchedSmallBatch)
+    hipLaunchKernelGGL((k_sched<256, kSchedSmallBatch>), dim3(1), dim3(256), 0, stream, seqlens, batch, rows,
+                       topk, num_slots, meta, num_splits);
+  else
+    hipLaunchKernelGGL((k_sched<1024, kMaxBatch>), dim3(1), dim3(1024), 0, stream, seqlens, batch, rows,
+                       topk, num_slots, meta, num_splits);
   return hipGetLastError();
 }
 

@@ -102,7 +102,9 @@ def test_metadata_bit_exact():
     rng = np.random.default_rng(3)
     cases = [([37, 100], 16, 0, 256), ([0, 0, 5, 0], 128, 0, 8), (list(rng.integers(0, 9000, 64)), 128, 0, 256),
              ([65536] * 4 + list(rng.integers(256, 32768, 124)), 256, 0, 128), ([7] * 64, 128, 2048, 256),
-             (list(rng.integers(0, 3000, 2000)), 32, 0, 256), ([], 128, 0, 8)]
+             (list(rng.integers(0, 3000, 2000)), 32, 0, 256), ([], 128, 0, 8),
+             # the one-wave scheduler's largest batch, and the first on 1024 threads
+             (list(rng.integers(0, 9000, 256)), 128, 0, 256), (list(rng.integers(0, 9000, 257)), 128, 0, 256)]
     for sl, rows, topk, S in cases:
         say(f"metadata B={len(sl)} rows={rows} topk={topk} S={S}")
         t = torch.tensor(np.array(sl, dtype=np.int32), device="cuda:0")
