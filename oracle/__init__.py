@@ -78,6 +78,10 @@ def _load():
     lib.orc_decode.restype = ctypes.c_int
     lib.orc_decode.argtypes = [P(_Problem), P(ctypes.c_double), P(ctypes.c_double),
                                P(ctypes.c_uint8), P(ctypes.c_double), ctypes.c_int]
+    lib.orc_decode_row.restype = ctypes.c_int
+    lib.orc_decode_row.argtypes = [P(_Problem), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   P(ctypes.c_double), P(ctypes.c_double), P(ctypes.c_uint8),
+                                   P(ctypes.c_double)]
     lib.orc_decode_row_subset.restype = ctypes.c_int
     lib.orc_decode_row_subset.argtypes = [P(_Problem), ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int64, P(ctypes.c_int64),
@@ -202,6 +206,27 @@ def decode(p, nthreads: int = 0) -> dict:
     if p.fused:
         out["codes"] = codes.reshape(*shp, p.d_v)
         out["oscale"] = oscale.reshape(shp)
+    return out
+
+
+def decode_row(p, b, t, h) -> dict:
+    """One output row (b, t, h) exactly as decode() computes it: o (d_v,),
+    lse; in fused mode also codes (uint8, d_v) and oscale."""
+    lib = _load()
+    keep = []
+    s = _problem_struct(p, keep)
+    o = np.zeros(p.d_v, dtype=np.float64)
+    lse = np.zeros(1, dtype=np.float64)
+    codes = np.zeros(p.d_v, dtype=np.uint8)
+    oscale = np.zeros(1, dtype=np.float64)
+    rc = lib.orc_decode_row(ctypes.byref(s), int(b), int(t), int(h), _dptr(o), _dptr(lse),
+                            codes.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), _dptr(oscale))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    out = {"o": o, "lse": float(lse[0])}
+    if p.fused:
+        out["codes"] = codes
+        out["oscale"] = float(oscale[0])
     return out
 
 

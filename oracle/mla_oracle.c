@@ -259,6 +259,21 @@ static void query_row(const orc_problem* p, int b, int t, int h, double* q) {
   }
 }
 
+/* Fused epilogue of one output row (query token t of sequence b): the
+ * conjugate RoPE on the last 64 dims of o, then the per-row scale
+ * amax/448 (1 for an all-zero row) and the e4m3 codes of o/scale. */
+static void fused_epilogue(const orc_problem* p, int b, int t, double* orow, uint8_t* crow,
+                           double* oscale) {
+  double pos = (double)p->seqlens[b] - (double)p->s_q + (double)t;
+  orc_rope(orow + (p->d_v - 64), 32, pos, p->rope_base, -1.0);
+  double amax = 0.0;
+  for (int e = 0; e < p->d_v; ++e)
+    if (fabs(orow[e]) > amax) amax = fabs(orow[e]);
+  double sc = amax > 0.0 ? amax / 448.0 : 1.0;
+  *oscale = sc;
+  for (int e = 0; e < p->d_v; ++e) crow[e] = orc_e4m3_encode_rne(orow[e] / sc);
+}
+
 /* Full decode.  o: [batch][s_q][h_q][d_v] fp64; lse: [batch][s_q][h_q].
  * In fused mode o holds the post-RoPE fp64 O, codes the e4m3 bytes
  * [batch][s_q][h_q][d_v] and oscale the per-row fp64 scale. */
@@ -286,22 +301,33 @@ int orc_decode(const orc_problem* p, double* o, double* lse, uint8_t* codes, dou
         query_row(p, b, t, h, q);
         double* orow = o + row * p->d_v;
         orc_attend(q, n, keys, p->d_qk, p->d_v, p->scale, orow, &lse[row]);
-        if (p->fused) {
-          double pos = (double)p->seqlens[b] - (double)p->s_q + (double)t;
-          orc_rope(orow + (p->d_v - 64), 32, pos, p->rope_base, -1.0);
-          double amax = 0.0;
-          for (int e = 0; e < p->d_v; ++e)
-            if (fabs(orow[e]) > amax) amax = fabs(orow[e]);
-          double sc = amax > 0.0 ? amax / 448.0 : 1.0;
-          oscale[row] = sc;
-          for (int e = 0; e < p->d_v; ++e)
-            codes[row * p->d_v + e] = orc_e4m3_encode_rne(orow[e] / sc);
-        }
+        if (p->fused) fused_epilogue(p, b, t, orow, codes + row * p->d_v, &oscale[row]);
       }
       free(keys);
       free(ids);
     }
   }
+  return 0;
+}
+
+/* One output row (b, t, h) over every key it sees, as orc_decode computes
+ * it (fused epilogue included); for checking sampled rows of workloads too
+ * large for a full oracle run. */
+int orc_decode_row(const orc_problem* p, int b, int t, int h, double* o, double* lse, uint8_t* codes,
+                   double* oscale) {
+  if (p->d_qk > 1024 || p->d_v > p->d_qk) return 1;
+  if (p->fused && (p->d_v != 512 || p->d_qk != 576)) return 1;
+  int64_t cap = p->indices ? p->topk : (p->seqlens[b] > 0 ? p->seqlens[b] : 0);
+  int64_t* ids = (int64_t*)malloc(sizeof(int64_t) * (size_t)(cap > 0 ? cap : 1));
+  int64_t n = visible_tokens(p, b, t, ids);
+  double* keys = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * p->d_qk);
+  for (int64_t j = 0; j < n; ++j) fetch_token(p, ids[j], keys + j * p->d_qk);
+  double q[1024];
+  query_row(p, b, t, h, q);
+  orc_attend(q, n, keys, p->d_qk, p->d_v, p->scale, o, lse);
+  if (p->fused) fused_epilogue(p, b, t, o, codes, oscale);
+  free(keys);
+  free(ids);
   return 0;
 }
 

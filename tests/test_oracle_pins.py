@@ -117,6 +117,28 @@ def test_split_combine_equals_unsplit(nparts):
             assert abs(l - full["lse"][b, 0, h]) < 1e-12
 
 
+@pytest.mark.parametrize("kind", ["dense_causal", "sparse_fp8", "fused"])
+def test_decode_row_matches_decode(kind):
+    """The single-row entry (used on sampled rows of full-size workloads)
+    reproduces every row of the full decode bit for bit."""
+    if kind == "dense_causal":
+        p = W.make_dense("row", [1, 70, 129, 0], s_q=2, h_q=4, seed=41, causal=True)
+    elif kind == "sparse_fp8":
+        p = W.make_sparse_fp8("rowf8", batch=2, s_q=1, h_q=4, cache_len=256, topk=100, seed=42, pad_frac=0.5)
+    else:
+        p = W.make_dense("rowfu", [70, 200, 5], s_q=1, h_q=4, seed=43, fused=True)
+    full = oracle.decode(p)
+    for b in range(p.batch):
+        for t in range(p.s_q):
+            for h in range(p.h_q):
+                r = oracle.decode_row(p, b, t, h)
+                assert np.array_equal(r["o"], full["o"][b, t, h])
+                assert r["lse"] == full["lse"][b, t, h] or (np.isneginf(r["lse"]) and np.isneginf(full["lse"][b, t, h]))
+                if p.fused:
+                    assert np.array_equal(r["codes"], full["codes"][b, t, h])
+                    assert r["oscale"] == full["oscale"][b, t, h]
+
+
 def test_combine_empty_parts():
     o, l = oracle.combine(np.array([-np.inf, -np.inf]), np.ones((2, 512)))
     assert l == -np.inf and np.all(o == 0)
