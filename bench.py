@@ -72,15 +72,16 @@ def make_workload(name):
             "fused_b1_h128": lambda: W.config5(1)}[name]()
 
 
-def traffic_record(kernel_src):
+def traffic_record(kernel_src, workload):
     """HBM traffic measured by rocprofv3 PMC counters for the current kernel
-    source, or None when the counters were taken on other code."""
+    source on this workload, or None when the counters were taken on other
+    code or another workload."""
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    return rec if rec.get("kernel_sha") == h else None
+    return rec if rec.get("kernel_sha") == h and rec.get("workload") == workload else None
 
 
 def cpu_baseline(p, nbytes):
@@ -279,9 +280,20 @@ def main():
 
     value = nbytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
-    achieved = nbytes / (dec_avg * 1e-3) / 1e9
+    # The decode kernel's roofline: HBM-bound below the ridge point (peak
+    # flop/s over peak bytes/s, 312.5 flop/B), MFMA-bound above it.
+    hbm_gbs = nbytes / (dec_avg * 1e-3) / 1e9
+    mfma_tflops = flops / (dec_avg * 1e-3) / 1e12
+    intensity = flops / nbytes if nbytes else 0.0
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity > ridge:
+        roof = {"bound": "mfma", "achieved": round(mfma_tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(mfma_tflops / BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
     src = os.path.join(ROOT, "mla_paged_kv_05_amd", "csrc", "mla_kernels.hip")
-    tr = traffic_record(src)
+    tr = None if args.merge_in_kernel else traffic_record(src, p.name)
     traffic = None if tr is None else tr["bytes_per_launch"]
     res = {
         "metric": "MLA paged decode effective HBM GB/s (algorithmic bytes) + TFLOPS, b=64 h_q=128 seq<=8K",
@@ -295,11 +307,14 @@ def main():
                    "launch": "eager" if graphs is None else "hipGraph per step (metadata, decode, combine)",
                    "combine": "in the decode launch" if args.merge_in_kernel else "separate launch"},
         "tflops": round(tflops, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_decode" + (" (with the in-kernel LSE combine)" if args.merge_in_kernel else ""),
-                     "kernel_avg_us": round(dec_avg * 1e3, 2),
-                     "algorithmic_bytes_per_launch": nbytes},
+        "roofline": dict(roof, **{
+            "traffic": traffic,
+            "kernel": "k_decode" + (" (with the in-kernel LSE combine)" if args.merge_in_kernel else ""),
+            "kernel_avg_us": round(dec_avg * 1e3, 2),
+            "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
+            "intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
+            "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+            "mfma_tflops": round(mfma_tflops, 1), "mfma_frac": round(mfma_tflops / BF16_PEAK_TFLOPS, 4)}),
     }
     if not args.no_cpu:
         log("timing the CPU oracle on the same workload ...")
