@@ -624,29 +624,24 @@ __device__ __forceinline__ void fetch_ids_dma(int32_t* ids_lds, const int32_t* i
 // ---------------------------------------------------------------------------
 // Fused prologue / epilogue helpers.  The RoPE angle of pair i at position
 // pos is theta = pos * base^(-2i/64) (the inverse frequencies come from the
-// host in fp64); it is formed and reduced to [-pi, pi] in fp64, since
-// positions reach 10^4 radians, then sin and cos come from Taylor series in
-// fp64 on the quarter-turn-reduced angle |r| <= pi/4 (truncation below 3e-14)
-// and are rounded once to fp32.  Light on registers, unlike a general
-// sincosf with its large-argument path.
+// host in fp64).  Positions reach 10^4 radians, so theta is formed and
+// reduced by quarter turns in fp64 (pi/2 as hi + lo); the remainder
+// |r| <= pi/4 is then exact to ~1e-12 and goes to fp32, where Taylor series
+// (sin to r^9, cos to r^10: truncation below 2e-9) give sin and cos to about
+// 3e-7 absolute.  Light on registers, unlike a general sincosf with its
+// large-argument path, and unlike the same series in fp64.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void sincos_reduced(double x, float& s, float& c) {
-  const double q = rint(x * 0.63661977236758138);                          // x / (pi/2)
-  const double r = (x - q * 1.5707963267948966) - q * 6.123233995736766e-17;  // pi/2 as hi + lo
-  const double r2 = r * r;
-  const double sp = r * (1.0 + r2 * (-1.0 / 6 + r2 * (1.0 / 120 + r2 * (-1.0 / 5040 + r2 * (1.0 / 362880 +
-                    r2 * (-1.0 / 39916800 + r2 * (1.0 / 6227020800.0)))))));
-  const double cp = 1.0 + r2 * (-0.5 + r2 * (1.0 / 24 + r2 * (-1.0 / 720 + r2 * (1.0 / 40320 +
-                    r2 * (-1.0 / 3628800 + r2 * (1.0 / 479001600.0 + r2 * (-1.0 / 87178291200.0)))))));
-  const int qi = (int)q & 3;  // x = r + qi * pi/2 (mod 2 pi)
-  const double ss = qi == 0 ? sp : qi == 1 ? cp : qi == 2 ? -sp : -cp;
-  const double cc = qi == 0 ? cp : qi == 1 ? -sp : qi == 2 ? -cp : sp;
-  s = (float)ss;
-  c = (float)cc;
-}
 __device__ __forceinline__ void rope_cs(double pos, double inv_freq, float sign, float& c, float& s) {
   const double th = (double)sign * pos * inv_freq;
-  sincos_reduced(th - 6.283185307179586 * rint(th * 0.15915494309189535), s, c);
+  const double q = rint(th * 0.63661977236758138);                                     // th / (pi/2)
+  const float r = (float)((th - q * 1.5707963267948966) - q * 6.123233995736766e-17);  // |r| <= pi/4
+  const float r2 = r * r;
+  const float sp = r * (1.0f + r2 * (-1.0f / 6 + r2 * (1.0f / 120 + r2 * (-1.0f / 5040 + r2 * (1.0f / 362880)))));
+  const float cp = 1.0f + r2 * (-0.5f + r2 * (1.0f / 24 + r2 * (-1.0f / 720 + r2 * (1.0f / 40320 +
+                   r2 * (-1.0f / 3628800)))));
+  const int qi = (int)(int64_t)q & 3;  // th = r + qi * pi/2 (mod 2 pi)
+  s = qi == 0 ? sp : qi == 1 ? cp : qi == 2 ? -sp : -cp;
+  c = qi == 0 ? cp : qi == 1 ? -sp : qi == 2 ? -cp : sp;
 }
 
 // ---------------------------------------------------------------------------
