@@ -60,6 +60,9 @@ constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer, dword3 for gfx9 f
 // slot indices): move them to scalar registers so buffer descriptors, LDS
 // bases and loop bounds stay scalar.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uni_u64(uint64_t v) {
+  return ((uint64_t)(uint32_t)uni((int)(v >> 32)) << 32) | (uint32_t)uni((int)(uint32_t)v);
+}
 // Buffer accesses with cache policy sc0 sc1: they go past the CU's L1 and
 // the XCD's L2 to the coherent memory side, so a store that has completed is
 // seen by a load of this kind from any XCD without L2 write-back or
@@ -644,6 +647,40 @@ __device__ __forceinline__ void rope_cs(double pos, double inv_freq, float sign,
   c = qi == 0 ? cp : qi == 1 ? -sp : qi == 2 ? -cp : sp;
 }
 
+// RoPE angles of one wave's rows.  A lane needs pair i0 when it holds the
+// low half of its row's dims and i1 for the high half.  When every row of
+// the wave sits at one position (always with one query token per sequence),
+// each of the 32 pairs is computed once, pair lane & 31 on each lane, and
+// read back by lane index; otherwise each lane computes its own pairs.
+struct RopeRow {
+  bool shared;
+  double pos;
+  float c, s;
+};
+__device__ __forceinline__ RopeRow rope_row(double pos, bool row_ok, const double* inv_freq, float sign) {
+  RopeRow r;
+  const double pos0 = __builtin_bit_cast(double, uni_u64(__builtin_bit_cast(uint64_t, pos)));
+  r.shared = __builtin_amdgcn_ballot_w64(row_ok && pos != pos0) == 0;
+  r.pos = pos;
+  r.c = 0.f;
+  r.s = 0.f;
+  if (r.shared) rope_cs(pos0, inv_freq[fresh_lane() & 31], sign, r.c, r.s);
+  return r;
+}
+__device__ __forceinline__ void rope_pair(const RopeRow& r, const double* inv_freq, float sign, int i0, int i1,
+                                          bool hi, float& c, float& s) {
+  if (r.shared) {
+    const float c0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r.c), i0));
+    const float c1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r.c), i1));
+    const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r.s), i0));
+    const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r.s), i1));
+    c = hi ? c1 : c0;
+    s = hi ? s1 : s0;
+  } else {
+    rope_cs(r.pos, hi ? inv_freq[i1] : inv_freq[i0], sign, c, s);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Decode kernel
 //
@@ -970,6 +1007,7 @@ k_decode(DecodeArgs a) {
         // batch's q and weight loads issued together: all 72 in flight at
         // once would not fit in the registers beside the fragments.
         constexpr int kBatch = 6;
+        const RopeRow rr = rope_row(pos, row_ok, a.rope_inv_freq, 1.0f);
 #pragma unroll
         for (int bt = 0; bt < 36 / kBatch; ++bt) {
           bf16x8 vb[kBatch], wb[kBatch];
@@ -993,8 +1031,7 @@ k_decode(DecodeArgs a) {
 #pragma unroll
               for (int pp = 0; pp < 4; ++pp) {
                 float cs, sn;
-                rope_cs(pos, half ? a.rope_inv_freq[8 * (ks - 32) + 4 + pp] : a.rope_inv_freq[8 * (ks - 32) + pp],
-                        1.0f, cs, sn);
+                rope_pair(rr, a.rope_inv_freq, 1.0f, 8 * (ks - 32) + pp, 8 * (ks - 32) + 4 + pp, half, cs, sn);
                 const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
                 y[2 * pp] = x0 * cs - x1 * sn;
                 y[2 * pp + 1] = x0 * sn + x1 * cs;
@@ -1393,6 +1430,7 @@ k_decode(DecodeArgs a) {
           // move the 256 accumulators into VGPRs).  amax(O/l) = amax(O)/l
           // exactly, since scaling by a positive constant keeps the order.
           const double pos = (double)Lb - (double)a.s_q + (double)tok;
+          const RopeRow rr = rope_row(pos, row_ok, a.rope_inv_freq, -1.0f);
           float rot[2][16];
 #pragma unroll
           for (int t = 0; t < 2; ++t)
@@ -1402,7 +1440,7 @@ k_decode(DecodeArgs a) {
               for (int pp = 0; pp < 2; ++pp) {
                 const int k0 = 16 * t + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * half
                 float cs, sn;
-                rope_cs(pos, half ? a.rope_inv_freq[k0 + 2] : a.rope_inv_freq[k0], -1.0f, cs, sn);
+                rope_pair(rr, a.rope_inv_freq, -1.0f, k0, k0 + 2, half, cs, sn);
                 const float x0 = o[14 + t][4 * qd + 2 * pp] * inv, x1 = o[14 + t][4 * qd + 2 * pp + 1] * inv;
                 rot[t][4 * qd + 2 * pp] = x0 * cs - x1 * sn;
                 rot[t][4 * qd + 2 * pp + 1] = x0 * sn + x1 * cs;
@@ -1624,6 +1662,7 @@ __device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub,
     const int Lb = a.seqlens[b];
     const int tok = row_ok ? row / a.h_q : 0;
     const double pos = (double)Lb - (double)a.s_q + (double)tok;
+    const RopeRow rr = rope_row(pos, row_ok, a.rope_inv_freq, -1.0f);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int e = sub * 16 + k, mt = e >> 2, qd = e & 3;
@@ -1632,7 +1671,7 @@ __device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub,
       for (int pp = 0; pp < 2; ++pp) {
         const int k0 = 16 * (mt - 14) + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * half
         float cs, sn;
-        rope_cs(pos, half ? a.rope_inv_freq[k0 + 2] : a.rope_inv_freq[k0], -1.0f, cs, sn);
+        rope_pair(rr, a.rope_inv_freq, -1.0f, k0, k0 + 2, half, cs, sn);
         const float x0 = acc[k][2 * pp], x1 = acc[k][2 * pp + 1];
         acc[k][2 * pp] = x0 * cs - x1 * sn;
         acc[k][2 * pp + 1] = x0 * sn + x1 * cs;

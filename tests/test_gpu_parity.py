@@ -89,6 +89,16 @@ def test_fused(slots):
 
 
 @gpu
+@pytest.mark.parametrize("h_q", [16, 64])
+def test_fused_multi_token(h_q):
+    """Two query tokens per sequence: with h_q 16 a wave's 32 rows span both
+    tokens (RoPE angles per lane), with h_q 64 each wave has one token but
+    the workgroup two (angles shared across the wave)."""
+    p = W.make_dense("fused_mt", [70, 1500, 3, 400], s_q=2, h_q=h_q, seed=17, fused=True)
+    _parity(p, num_slots=16, what=f"fused s_q=2 h{h_q}", fused_lse_tol=FUSED_BF16_QHAT_LSE)
+
+
+@gpu
 @pytest.mark.xfail(strict=True, reason="q-hat is rounded to bf16 before QK^T: LSE error 3.3e-3 > 1e-3")
 def test_fused_lse_1e3():
     p = W.make_dense("fused", [70, 2048, 5, 700], s_q=1, h_q=128, seed=15, fused=True)
