@@ -182,42 +182,6 @@ __device__ __forceinline__ void mfma_s_settle(f32x16& c) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
 }
 
-// o *= alpha on one 16-register AGPR accumulator tile when `cond` (a
-// wave-uniform SGPR value) is non-zero; otherwise nothing.  Wait states
-// around the accvgpr moves are explicit: the compiler does not look inside.
-__device__ __forceinline__ void rescale_tile(f32x16& o, float alpha, uint32_t cond) {
-  float t;
-  asm volatile(
-      "s_cmp_eq_u32 %17, 0\n\t"
-      "s_cbranch_scc1 1f\n\t"
-      "s_nop 7\n\t"
-      "s_nop 7\n\t"
-      "v_accvgpr_read_b32 %16, %0\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %0, %16\n\t"
-      "v_accvgpr_read_b32 %16, %1\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %1, %16\n\t"
-      "v_accvgpr_read_b32 %16, %2\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %2, %16\n\t"
-      "v_accvgpr_read_b32 %16, %3\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %3, %16\n\t"
-      "v_accvgpr_read_b32 %16, %4\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %4, %16\n\t"
-      "v_accvgpr_read_b32 %16, %5\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %5, %16\n\t"
-      "v_accvgpr_read_b32 %16, %6\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %6, %16\n\t"
-      "v_accvgpr_read_b32 %16, %7\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %7, %16\n\t"
-      "v_accvgpr_read_b32 %16, %8\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %8, %16\n\t"
-      "v_accvgpr_read_b32 %16, %9\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %9, %16\n\t"
-      "v_accvgpr_read_b32 %16, %10\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %10, %16\n\t"
-      "v_accvgpr_read_b32 %16, %11\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %11, %16\n\t"
-      "v_accvgpr_read_b32 %16, %12\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %12, %16\n\t"
-      "v_accvgpr_read_b32 %16, %13\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %13, %16\n\t"
-      "v_accvgpr_read_b32 %16, %14\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %14, %16\n\t"
-      "v_accvgpr_read_b32 %16, %15\n\tv_mul_f32 %16, %16, %18\n\tv_accvgpr_write_b32 %15, %16\n\t"
-      "s_nop 7\n\t"
-      "s_nop 7\n"
-      "1:"
-      : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]),
-        "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]),
-        "+a"(o[14]), "+a"(o[15]), "=&v"(t)
-      : "s"(cond), "v"(alpha)
-      : "scc");
-}
-
 // Max / sum over the lane pair (l, l ^ 32) that holds one query row:
 // v_permlane32_swap leaves {v[l], v[l ^ 32]} in the two results of every lane.
 __device__ __forceinline__ float row_max2(float v) {
@@ -229,7 +193,6 @@ __device__ __forceinline__ float row_sum2(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // Split-KV scheduler (one workgroup).  Implements the split rule stated in
 // mla.h; every per-sequence quantity is a prefix sum, every slot finds its
