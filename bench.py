@@ -65,6 +65,10 @@ def algorithmic(p):
     return nbytes, flops
 
 
+WORKLOADS = ("dense_b64_h128_L1k-8k", "splitkv_b128_sq2_causal", "sparse_fp8_b64_top2048", "fused_b32_h128",
+             "fused_b1_h128")
+
+
 def make_workload(name):
     from mla_paged_kv_05_amd import workloads as W
     return {"dense_b64_h128_L1k-8k": W.config2, "splitkv_b128_sq2_causal": W.config3,
@@ -103,7 +107,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense_b64_h128_L1k-8k")
+    ap.add_argument("--workload", default="dense_b64_h128_L1k-8k", choices=WORKLOADS)
     ap.add_argument("--rotate", type=int, default=0, help="KV copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--merge-in-kernel", action="store_true",
