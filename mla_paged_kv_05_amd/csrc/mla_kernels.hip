@@ -1115,7 +1115,19 @@ k_decode(DecodeArgs a) {
       };
       const f32x4* sv = reinterpret_cast<const f32x4*>(scl + lh * 16);
       bf16x8 kbuf[kLa], qbuf[kLa];
-      f32x16 part;
+      // Two partial accumulators alternate between the 128-dim tiles: tile
+      // t's fold (sc += part * scale) runs between the first MFMAs of tile
+      // t+1, so the MFMA pipe does not wait for it.  Fold of tile tp: settle
+      // and scale reads after MFMA 8(tp+1), quarter q after MFMA 8(tp+1)+1+q
+      // (tile 3's last quarter after the loop).  The RoPE tile (ks 32..35)
+      // adds unscaled at the end.
+      f32x16 part[2];
+      f32x4 s4[4];
+      auto fold_quarter = [&](int tp, int q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sc[4 * q + e] = (tp == 0 ? 0.f : sc[4 * q + e]) + part[tp & 1][4 * q + e] * s4[q][e];
+      };
 #pragma unroll
       for (int i = 0; i < kLa; ++i) kbuf[i] = read_k(i);
 #pragma unroll
@@ -1126,29 +1138,25 @@ k_decode(DecodeArgs a) {
           kbuf[ks % kLa] = read_k(ks + kLa);
           if (ks + kLa >= kQRegStepsFp8) qbuf[ks % kLa] = read_q(ks + kLa);
         }
-        if (ks % 8 == 0 && ks <= 32) mfma_s_first(part, ka, qb);
-        else mfma_s_acc(part, ka, qb);
-        if (ks % 8 == 7 || ks == 35) {
-          mfma_s_settle(part);
-          const int t = ks >> 3;
-          if (t < 4) {
-            // compiler-only fence: each fold reads its tile's scales here,
-            // not hoisted with the other tiles' into registers up front
-            asm volatile("" ::: "memory");
+        const int t = ks >> 3, u = ks & 7;
+        if (u == 0) mfma_s_first(part[t & 1], ka, qb);
+        else mfma_s_acc(part[t & 1], ka, qb);
+        if (t >= 1) {
+          const int tp = t - 1;
+          if (u == 0) {
+            mfma_s_settle(part[tp & 1]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 s4 = sv[t * 8 + q];
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                sc[4 * q + e] = (t == 0 ? 0.f : sc[4 * q + e]) + part[4 * q + e] * s4[e];
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sc[i] += part[i];
+            for (int q = 0; q < 4; ++q) s4[q] = sv[tp * 8 + q];
+          } else if (u <= 4) {
+            fold_quarter(tp, u - 1);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      fold_quarter(3, 3);
+      mfma_s_settle(part[0]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] += part[0][i];
     };
     // FP8: O^T += V^T P_t^T where V holds the exact codes and P_t = p * the
     // keys' scale of tile t (d-tiles 4t..4t+3), rounded once to bf16.
