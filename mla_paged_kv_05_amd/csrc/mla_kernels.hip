@@ -1174,28 +1174,43 @@ k_decode(DecodeArgs a) {
             (__attribute__((address_space(3))) s16x4*)(pp + 2 * kMainStride));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      // mt order: the four d-tiles of one scale tile, both key halves
+      // mt order: the four d-tiles of one scale tile, both key halves; one
+      // stream of 32 MFMAs, i = 8t + j.  The V reads run kVa MFMAs ahead
+      // across tile boundaries.  Tile t+1's scaled P goes to the other half
+      // of pt while tile t's MFMAs run: scale reads after MFMA j = 0, one
+      // quarter after each of MFMAs 3..6 (three MFMAs after the last read of
+      // that half by tile t-1), settled after MFMA 7.
+      auto scale_p = [&](bf16x8 (&dst)[2], int q, const f32x4& s4) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        bf16x8 pt[2];
-        asm volatile("" ::: "memory");
+        for (int e = 0; e < 4; ++e) dst[q >> 1][4 * (q & 1) + e] = (__bf16)(p[4 * q + e] * s4[e]);
+      };
+      auto v_index = [](int i) { return ((i & 7) >> 2) * 16 + 4 * (i >> 3) + (i & 3); };  // kq * 16 + mt
+      bf16x8 pt[2][2];
+      f32x4 s4[4];
+      asm volatile("" ::: "memory");
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 s4 = sv[t * 8 + q];
+      for (int q = 0; q < 4; ++q) scale_p(pt[0], q, sv[q]);
+      valu_to_mfma_settle(pt[0][0], pt[0][1]);
+      bf16x8 vbuf[kVa];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pt[q >> 1][4 * (q & 1) + e] = (__bf16)(p[4 * q + e] * s4[e]);
+      for (int i = 0; i < kVa; ++i) vbuf[i] = read_v(v_index(i));
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int t = i >> 3, j = i & 7;
+        const bf16x8 va = vbuf[i % kVa];
+        if (i + kVa < 32) vbuf[i % kVa] = read_v(v_index(i + kVa));
+        mfma_o(o[4 * t + (j & 3)], va, pt[t & 1][j >> 2]);
+        if (t + 1 < 4) {
+          if (j == 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) s4[q] = sv[(t + 1) * 8 + q];
+          } else if (j >= 3 && j <= 6) {
+            scale_p(pt[(t + 1) & 1], j - 3, s4[j - 3]);
+          } else if (j == 7) {
+            valu_to_mfma_settle(pt[(t + 1) & 1][0], pt[(t + 1) & 1][1]);
+          }
         }
-        valu_to_mfma_settle(pt[0], pt[1]);
-        bf16x8 vbuf[kVa];
-#pragma unroll
-        for (int i = 0; i < kVa; ++i) vbuf[i] = read_v((i >> 2) * 16 + 4 * t + (i & 3));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {  // i = kq * 4 + (mt - 4t)
-          const bf16x8 va = vbuf[i % kVa];
-          if (i + kVa < 8) vbuf[i % kVa] = read_v(((i + kVa) >> 2) * 16 + 4 * t + ((i + kVa) & 3));
-          mfma_o(o[4 * t + (i & 3)], va, pt[i >> 2]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     auto key0_of = [&](int ps) { return (cj + (ps >> 1)) * kPage + (ps & 1) * kHalfRows; };
