@@ -514,11 +514,22 @@ __device__ __forceinline__ int scale_slot(int key) {  // key -> h*16 + i
 // zero row with zero scales.
 __device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const uint8_t* raw, int tid) {
   tid = (tid & ~63) | fresh_lane();  // keep the per-thread addresses out of the loop's live set
+  // All code reads first, then the conversions and writes: the compiler
+  // cannot move a read of the raw slot above a write to the tile (same LDS
+  // array), so interleaved they would each wait out a full LDS latency.
+  constexpr int kPer = kHalfRows * 64 / kThreads;
+  uint2 codes[kPer];
 #pragma unroll
-  for (int kk = 0; kk < kHalfRows * 64 / kThreads; ++kk) {
+  for (int kk = 0; kk < kPer; ++kk) {
+    const int k = kk * kThreads + tid;
+    codes[kk] = *reinterpret_cast<const uint2*>(raw + (k >> 6) * kFp8TokenBytes + (k & 63) * 8);
+  }
+  const uint4 rope = *reinterpret_cast<const uint4*>(raw + (tid >> 3) * kFp8TokenBytes + 528 + (tid & 7) * 16);
+#pragma unroll
+  for (int kk = 0; kk < kPer; ++kk) {
     const int k = kk * kThreads + tid;
     const int r = k >> 6, c = k & 63;
-    const uint2 code = *reinterpret_cast<const uint2*>(raw + r * kFp8TokenBytes + c * 8);
+    const uint2 code = codes[kk];
     const uint32_t cw[2] = {code.x, code.y};
     uint32_t w[4];
 #pragma unroll
@@ -531,8 +542,7 @@ __device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const u
   }
   {
     const int r = tid >> 3, c = tid & 7;
-    const uint4 v = *reinterpret_cast<const uint4*>(raw + r * kFp8TokenBytes + 528 + c * 16);
-    *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = v;
+    *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = rope;
   }
   if (tid < 4 * kHalfRows) {
     const int r = tid >> 2, t = tid & 3;
