@@ -9,6 +9,9 @@ Layouts (row-major, contiguous):
   kv (bf16)    bf16 bits  uint16 [num_blocks][64][576]
   kv (fp8)     bytes      uint8  [num_blocks][64][656]: 512 e4m3 codes,
                4 little-endian fp32 scales (one per 128 dims), 64 bf16 RoPE
+  kv (fp8 V4.1) bytes     uint8  [num_blocks][64][528]: 512 e4m3 codes of all
+               512 dims, 16 e8m0 scales (one per 32 dims); q is then
+               [batch][s_q][h_q][512] and d_qk = d_v = 512
   block_table  int32 [batch][max_blocks], -1 past a sequence's blocks
   seqlens      int32 [batch]
   indices      int32 [batch][s_q][topk] flat token ids (block*64+offset), -1 masked
@@ -34,6 +37,8 @@ PAGE = 64
 D_QK = 576
 D_V = 512
 FP8_TOKEN_BYTES = 656
+FP8V41_TOKEN_BYTES = 528
+D_QK_V41 = 512
 BF16_NAN = 0x7FC0
 FP8_NAN = 0x7F
 
@@ -65,7 +70,7 @@ class Problem:
     num_blocks: int
     q: np.ndarray
     kv: np.ndarray
-    kv_format: str = "bf16"          # "bf16" or "fp8v32"
+    kv_format: str = "bf16"          # "bf16", "fp8v32" or "fp8v41"
     causal: bool = False
     indices: Optional[np.ndarray] = None
     topk: int = 0
@@ -186,6 +191,50 @@ def make_sparse_fp8(name, batch, s_q, h_q, cache_len, topk, seed, pad_frac=0.1,
                    indices=idx.astype(np.int32), topk=topk)
 
 
+def make_sparse_fp8_v41(name, batch, s_q, h_q, cache_len, topk, seed, pad_frac=0.1,
+                        pool_factor=1.2) -> Problem:
+    """Token-level sparse decode over a V4.1 FP8 paged cache (528 B per
+    token, head dim 512 with V = K).
+
+    Indices are drawn as in make_sparse_fp8.  Values are x/scale rounded to
+    e4m3 with x ~ N(0,1) and one power-of-two scale per 32 dims, 2^k with k
+    uniform in -4..4 (stored as the e8m0 byte k + 127).  Unused records hold
+    NaN codes and NaN (0xFF) scales."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seqlens = np.full(batch, cache_len, dtype=np.int32)
+    nblk = (cache_len + PAGE - 1) // PAGE
+    need = nblk * batch
+    pool = int(math.ceil(pool_factor * need))
+    perm = rng.permutation(pool).astype(np.int32)
+    bt = perm[: need].reshape(batch, nblk).copy()
+    q = _draw_bf16(rng, batch * s_q * h_q * D_QK_V41).reshape(batch, s_q, h_q, D_QK_V41)
+    idx = np.empty((batch, s_q, topk), dtype=np.int64)
+    for b in range(batch):
+        for t in range(s_q):
+            lp = np.sort(rng.choice(cache_len, size=topk, replace=False))
+            idx[b, t] = bt[b, lp // PAGE].astype(np.int64) * PAGE + lp % PAGE
+    npad = int(round(pad_frac * batch * s_q))
+    pad_rows = rng.choice(batch * s_q, size=npad, replace=False)
+    for r_i, r in enumerate(pad_rows):
+        b, t = divmod(int(r), s_q)
+        k_valid = 0 if r_i == 0 else int(rng.integers(0, topk))
+        idx[b, t, k_valid:] = -1
+    used = np.unique(idx[idx >= 0])
+    kv = np.zeros((pool * PAGE, FP8V41_TOKEN_BYTES), dtype=np.uint8)
+    kv[:, :512] = FP8_NAN
+    kv[:, 512:] = 0xFF
+    n = int(used.shape[0])
+    x = rng.standard_normal((n, 512), dtype=np.float32)
+    k = rng.integers(-4, 5, size=(n, 16))
+    codes = _e4m3_codes(x / np.repeat(np.exp2(k).astype(np.float32), 32, axis=1))
+    kv[used, :512] = codes
+    kv[used, 512:] = (k + 127).astype(np.uint8)
+    kv = kv.reshape(pool, PAGE, FP8V41_TOKEN_BYTES)
+    return Problem(name=name, batch=batch, s_q=s_q, h_q=h_q, seqlens=seqlens, block_table=bt,
+                   num_blocks=pool, q=q, kv=kv, kv_format="fp8v41", indices=idx.astype(np.int32),
+                   topk=topk, scale=D_QK_V41 ** -0.5, d_qk=D_QK_V41, d_v=D_V)
+
+
 def make_sparse_bf16_from_dense(p: Problem, topk: int, seed: int) -> Problem:
     """Sparse indices over an existing dense bf16 problem (s_q rows share
     nothing): each (b, t) draws topk positions < L_b with replacement off
@@ -240,6 +289,12 @@ def config4(seed=1004, batch=64, cache_len=65536, topk=2048) -> Problem:
     """Sparse top-k over an FP8 V3.2 cache."""
     return make_sparse_fp8(f"sparse_fp8_b{batch}_top{topk}", batch, 1, 128, cache_len, topk,
                            seed)
+
+
+def config_v41(seed=1006, batch=64, cache_len=65536, topk=2048) -> Problem:
+    """Config 4's shape over a V4.1 FP8 cache (528 B per token, head dim 512):
+    the workload of the format the pages name as current."""
+    return make_sparse_fp8_v41(f"sparse_fp8v41_b{batch}_top{topk}", batch, 1, 128, cache_len, topk, seed)
 
 
 def config5(batch=32, seed=None) -> Problem:

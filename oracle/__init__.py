@@ -60,6 +60,8 @@ def _load():
     lib.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.orc_e4m3_decode.restype = ctypes.c_double
     lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e8m0_decode.restype = ctypes.c_double
+    lib.orc_e8m0_decode.argtypes = [ctypes.c_uint8]
     lib.orc_e4m3_encode_rne.restype = ctypes.c_uint8
     lib.orc_e4m3_encode_rne.argtypes = [ctypes.c_double]
     lib.orc_rmsnorm.restype = None
@@ -112,6 +114,12 @@ def e4m3_decode(codes) -> np.ndarray:
     lib = _load()
     c = np.asarray(codes, dtype=np.uint8).ravel()
     return np.array([lib.orc_e4m3_decode(int(x)) for x in c], dtype=np.float64)
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8).ravel()
+    return np.array([lib.orc_e8m0_decode(int(x)) for x in c], dtype=np.float64)
 
 
 def e4m3_encode(x) -> np.ndarray:
@@ -170,7 +178,7 @@ def _problem_struct(p, keep):
     keep.extend([q, kv, bt, sl, idx, w])
     s = _Problem()
     s.batch, s.s_q, s.h_q, s.d_qk, s.d_v = p.batch, p.s_q, p.h_q, p.d_qk, p.d_v
-    s.kv_format = 0 if p.kv_format == "bf16" else 1
+    s.kv_format = {"bf16": 0, "fp8v32": 1, "fp8v41": 2}[p.kv_format]
     s.num_blocks = int(p.num_blocks)
     s.q, s.kv, s.block_table, s.seqlens = _vp(q), _vp(kv), _vp(bt), _vp(sl)
     s.max_blocks = int(bt.shape[1])

@@ -60,6 +60,7 @@
 
 #define ORC_PAGE 64
 #define ORC_FP8_TOKEN_BYTES 656
+#define ORC_FP8V41_TOKEN_BYTES 528
 
 /* ------------------------------------------------------------------ */
 /* Number formats                                                      */
@@ -86,6 +87,13 @@ double orc_e4m3_decode(uint8_t code) {
   else
     v = ldexp(1.0 + (double)m / 8.0, e - 7);
   return s ? -v : v;
+}
+
+/* OCP E8M0 (a scale): an 8-bit biased exponent, value 2^(e - 127); the
+ * all-ones code is NaN.  No sign, no mantissa. */
+double orc_e8m0_decode(uint8_t code) {
+  if (code == 0xFF) return NAN;
+  return ldexp(1.0, (int)code - 127);
 }
 
 /* OCP E4M3FN encode: round to nearest, ties to even mantissa, finite
@@ -116,7 +124,8 @@ uint8_t orc_e4m3_encode_rne(double x) {
 
 typedef struct {
   int32_t batch, s_q, h_q, d_qk, d_v;
-  int32_t kv_format;       /* 0: bf16 [nblk][64][d_qk]; 1: V3.2 fp8 [nblk][64][656] */
+  int32_t kv_format;       /* 0: bf16 [nblk][64][d_qk]; 1: V3.2 fp8 [nblk][64][656];
+                              2: V4.1 fp8 [nblk][64][528] (d_qk = 512) */
   int64_t num_blocks;
   const uint16_t* q;       /* bf16 bits [batch][s_q][h_q][d_qk] */
   const void* kv;
@@ -138,6 +147,11 @@ static void fetch_token(const orc_problem* p, int64_t tok, double* k) {
   if (p->kv_format == 0) {
     const uint16_t* src = (const uint16_t*)p->kv + tok * (int64_t)p->d_qk;
     for (int d = 0; d < p->d_qk; ++d) k[d] = orc_bf16_to_f64(src[d]);
+  } else if (p->kv_format == 2) {
+    /* V4.1 record (AI Wiki, The FP8 and FP4 KV cache): [0,512) e4m3 codes
+     * of all 512 dims, then 16 e8m0 scales, scale j for dims 32j..32j+31. */
+    const uint8_t* rec = (const uint8_t*)p->kv + tok * (int64_t)ORC_FP8V41_TOKEN_BYTES;
+    for (int d = 0; d < 512; ++d) k[d] = orc_e4m3_decode(rec[d]) * orc_e8m0_decode(rec[512 + d / 32]);
   } else {
     /* V3.2 record: [0,512) e4m3 codes, [512,528) four little-endian fp32
      * tile scales (one per 128 dims), [528,656) 64 bf16 RoPE values. */

@@ -320,6 +320,54 @@ def test_fp8_record_dequant():
     assert abs(r["lse"][0, 0, 0] - p.scale * float(bf16(p.q[0, 0, 0]) @ key)) < 1e-12
 
 
+def test_e8m0_decode_all_codes():
+    """E8M0 is a bare biased exponent: 2^(e-127), 0xFF is NaN."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e8m0_decode(codes)
+    assert np.isnan(got[255]) and not np.isnan(got[:255]).any()
+    assert np.array_equal(got[:255], np.ldexp(1.0, codes[:255].astype(np.int64) - 127))
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def test_fp8v41_record_dequant():
+    """A V4.1 record dequantises as code * 2^(e-127) with one e8m0 scale per
+    32 dims over all 512 dims: the oracle's sparse read of one token equals a
+    key built by hand from the record's bytes, and V is all of K."""
+    p = W.make_sparse_fp8_v41("f41", batch=1, s_q=1, h_q=1, cache_len=128, topk=1, seed=3, pad_frac=0)
+    tok = int(p.indices[0, 0, 0])
+    rec = p.kv.reshape(-1, 528)[tok]
+    key = np.array([e4m3_bitfield(int(c)) for c in rec[:512]]) * np.repeat(
+        np.ldexp(1.0, rec[512:].astype(np.int64) - 127), 32)
+    r = oracle.decode(p)
+    assert np.array_equal(r["o"][0, 0, 0], key)
+    assert abs(r["lse"][0, 0, 0] - p.scale * float(bf16(p.q[0, 0, 0]) @ key)) < 1e-12
+
+
+def test_fp8v41_matches_bruteforce():
+    """Several keys, masked and padded rows: the oracle's decode over a V4.1
+    cache equals a numpy softmax over keys dequantised with torch's e4m3
+    cast and numpy's ldexp."""
+    p = W.make_sparse_fp8_v41("f41b", batch=2, s_q=2, h_q=3, cache_len=256, topk=40, seed=4, pad_frac=0.5)
+    flat = p.kv.reshape(-1, 528)
+    r = oracle.decode(p)
+    for b in range(p.batch):
+        for t in range(p.s_q):
+            ids = p.indices[b, t]
+            ids = ids[ids >= 0]
+            if ids.size == 0:
+                assert np.all(r["o"][b, t] == 0) and np.all(np.isneginf(r["lse"][b, t]))
+                continue
+            rec = flat[ids]
+            codes = torch.from_numpy(np.ascontiguousarray(rec[:, :512])).view(torch.float8_e4m3fn)
+            keys = codes.to(torch.float64).numpy() * np.repeat(np.ldexp(1.0, rec[:, 512:].astype(np.int64) - 127), 32, axis=1)
+            qv = bf16(p.q[b, t])                              # [h_q][512]
+            s_ = p.scale * qv @ keys.T                        # [h_q][n]
+            lse = logsumexp(s_, axis=1)
+            o = softmax(s_, axis=1) @ keys
+            assert np.max(np.abs(r["o"][b, t] - o)) < 1e-12
+            assert np.max(np.abs(r["lse"][b, t] - lse)) < 1e-12
+
+
 # ------------------------------------------------------- norm and rope
 def test_rmsnorm_closed_form():
     w = np.linspace(0.5, 1.5, 576)
