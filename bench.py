@@ -54,26 +54,26 @@ def algorithmic(p):
     else:
         valid = (p.indices >= 0)
         keys_flops = int(valid.sum()) * p.h_q
-        per = 656 if p.kv_format == "fp8v32" else 1152
+        per = {"fp8v32": 656, "fp8v41": 528}.get(p.kv_format, 1152)
         kv = sum(len(np.unique(p.indices[b][p.indices[b] >= 0])) for b in range(p.batch)) * per
         tables = p.indices.size * 4
-    q = p.batch * rows * 576 * 2
+    q = p.batch * rows * p.d_qk * 2
     o = p.batch * rows * (512 + 4 if p.fused else 512 * 2)
     lse = p.batch * rows * 4
     nbytes = kv + q + o + lse + tables + p.batch * 4
-    flops = 2 * keys_flops * (576 + 512)
+    flops = 2 * keys_flops * (p.d_qk + p.d_v)
     return nbytes, flops
 
 
 WORKLOADS = ("dense_b64_h128_L1k-8k", "splitkv_b128_sq2_causal", "sparse_fp8_b64_top2048", "fused_b32_h128",
-             "fused_b1_h128")
+             "fused_b1_h128", "sparse_fp8v41_b64_top2048")
 
 
 def make_workload(name):
     from mla_paged_kv_05_amd import workloads as W
     return {"dense_b64_h128_L1k-8k": W.config2, "splitkv_b128_sq2_causal": W.config3,
             "sparse_fp8_b64_top2048": W.config4, "fused_b32_h128": lambda: W.config5(32),
-            "fused_b1_h128": lambda: W.config5(1)}[name]()
+            "fused_b1_h128": lambda: W.config5(1), "sparse_fp8v41_b64_top2048": W.config_v41}[name]()
 
 
 def traffic_record(kernel_src, workload):
@@ -304,7 +304,7 @@ def main():
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, shaped like the workload)",
-        "config": {"workload": p.name, "batch": p.batch, "s_q": p.s_q, "h_q": p.h_q, "d_qk": 576,
+        "config": {"workload": p.name, "batch": p.batch, "s_q": p.s_q, "h_q": p.h_q, "d_qk": p.d_qk,
                    "d_v": 512, "page": 64, "kv_format": p.kv_format, "causal": bool(p.causal),
                    "sparse_topk": topk, "fused": bool(p.fused), "parallelism": "single GPU",
                    "kv_copies_rotated": R,

@@ -57,11 +57,18 @@ typedef enum {
 
 typedef enum {
   MLA_KV_BF16 = 0,     /* [num_blocks][64][576] bf16, 1152 B per token                  */
-  MLA_KV_FP8_V32 = 1   /* [num_blocks][64][656] bytes: 512 e4m3 | 4 fp32 LE | 64 bf16    */
+  MLA_KV_FP8_V32 = 1,  /* [num_blocks][64][656] bytes: 512 e4m3 | 4 fp32 LE | 64 bf16    */
+  /* [num_blocks][64][528] bytes: 512 e4m3 codes of all dims, then 16 e8m0
+   * scales, scale j (value 2^(e-127); 0xFF is NaN) for dims 32j..32j+31.  The
+   * head dim of this format is 512 (AI Wiki, The FP8 and FP4 KV cache, the
+   * V4.1 row): d_qk = d_v = 512, V = K, q is [b][s_q][h_q][512].  Sparse
+   * (indices) and unfused only. */
+  MLA_KV_FP8_V41 = 2
 } mla_kv_format;
 
 #define MLA_PAGE_SIZE 64
 #define MLA_D_QK 576
+#define MLA_D_QK_V41 512
 #define MLA_D_V 512
 #define MLA_MAX_BATCH 16384
 

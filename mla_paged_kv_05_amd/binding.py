@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_OK = 0
 MLA_KV_BF16 = 0
 MLA_KV_FP8_V32 = 1
+MLA_KV_FP8_V41 = 2
+KV_FORMATS = {"bf16": MLA_KV_BF16, "fp8v32": MLA_KV_FP8_V32, "fp8v41": MLA_KV_FP8_V41}
 PAGE = 64
 D_QK = 576
 D_V = 512
@@ -169,14 +171,14 @@ def _params(q, kvcache, block_table, cache_seqlens, sched_meta, num_splits, caus
     p.batch, p.s_q, p.h_q, p.h_kv, p.d_qk, p.d_v = b, s_q, h_q, 1, d_qk, D_V
     p.q = q.data_ptr()
     p.kv = kvcache.data_ptr()
-    p.kv_format = MLA_KV_BF16 if kv_format == "bf16" else MLA_KV_FP8_V32
+    p.kv_format = KV_FORMATS[kv_format]
     p.page_size = kvcache.shape[1]
     p.num_blocks = kvcache.shape[0]
     if block_table is not None:
         p.block_table = block_table.data_ptr()
         p.max_blocks_per_seq = block_table.shape[1]
     p.cache_seqlens = cache_seqlens.data_ptr()
-    p.softmax_scale = float(D_QK ** -0.5 if softmax_scale is None else softmax_scale)
+    p.softmax_scale = float(d_qk ** -0.5 if softmax_scale is None else softmax_scale)
     p.causal = int(bool(causal))
     if indices is not None:
         p.indices = indices.data_ptr()
@@ -207,7 +209,9 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
                             fused: Optional[dict] = None):
     """Paged MLA decode.  q bf16 [b, s_q, h_q, 576]; kvcache bf16
     [blocks, 64, 1, 576] / [blocks, 64, 576] or uint8 [blocks, 64, 656]
-    (kv_format "fp8v32"); returns (o, lse) with o bf16 [b, s_q, h_q, 512]
+    (kv_format "fp8v32"), or with q [b, s_q, h_q, 512] a uint8
+    [blocks, 64, 528] V4.1 cache (kv_format "fp8v41", sparse only);
+    returns (o, lse) with o bf16 [b, s_q, h_q, 512]
     (uint8 e4m3 codes when fused) and lse fp32 [b, s_q, h_q].  Fused mode
     takes fused={"norm_weight": bf16 [576], "eps", "rope_base"} and also
     returns the per-row fp32 scale as a third value."""

@@ -104,11 +104,17 @@ static mla_status build_args(const mla_decode_params* p, mla::DecodeArgs& a, boo
   if (p->batch < 0 || p->s_q < 1 || p->h_q < 1)
     return fail(MLA_ERR_INVALID_ARG, "batch=%d s_q=%d h_q=%d", p->batch, p->s_q, p->h_q);
   if (p->h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv=%d (only 1)", p->h_kv);
-  if (p->d_qk != MLA_D_QK) return fail(MLA_ERR_UNSUPPORTED, "d_qk=%d (only 576)", p->d_qk);
+  if (p->kv_format == MLA_KV_FP8_V41) {
+    if (p->d_qk != MLA_D_QK_V41) return fail(MLA_ERR_UNSUPPORTED, "d_qk=%d (the V4.1 format has 512)", p->d_qk);
+  } else if (p->d_qk != MLA_D_QK) {
+    return fail(MLA_ERR_UNSUPPORTED, "d_qk=%d (only 576)", p->d_qk);
+  }
   if (p->d_v != MLA_D_V) return fail(MLA_ERR_UNSUPPORTED, "d_v=%d (only 512)", p->d_v);
   if (p->page_size != MLA_PAGE_SIZE) return fail(MLA_ERR_UNSUPPORTED, "page_size=%d (only 64)", p->page_size);
-  if (p->kv_format != MLA_KV_BF16 && p->kv_format != MLA_KV_FP8_V32)
+  if (p->kv_format != MLA_KV_BF16 && p->kv_format != MLA_KV_FP8_V32 && p->kv_format != MLA_KV_FP8_V41)
     return fail(MLA_ERR_INVALID_ARG, "kv_format=%d", p->kv_format);
+  if (p->kv_format == MLA_KV_FP8_V41 && (!p->indices || p->fused))
+    return fail(MLA_ERR_UNSUPPORTED, "the V4.1 FP8 format is decoded sparse (indices) and unfused only");
   const int64_t rows = (int64_t)p->s_q * p->h_q;
   if (rows > mla::kMaxRows) return fail(MLA_ERR_UNSUPPORTED, "s_q*h_q=%lld > %d", (long long)rows, mla::kMaxRows);
   if (p->batch > MLA_MAX_BATCH) return fail(MLA_ERR_UNSUPPORTED, "batch %d > %d", p->batch, MLA_MAX_BATCH);
@@ -239,6 +245,8 @@ mla_status mla_debug_gather(const mla_decode_params* p, int32_t b, int32_t t, in
   bool sparse = false;
   mla_status st = build_args(p, a, sparse);
   if (st != MLA_OK) return st;
+  if (p->kv_format == MLA_KV_FP8_V41)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_debug_gather: not available for the V4.1 FP8 format");
   if (!dst || b < 0 || b >= p->batch || t < 0 || t >= p->s_q || j < 0 ||
       (!sparse && j >= p->max_blocks_per_seq) || (sparse && j * MLA_PAGE_SIZE >= p->topk))
     return fail(MLA_ERR_INVALID_ARG, "mla_debug_gather: bad (b=%d, t=%d, j=%d) or dst", b, t, j);

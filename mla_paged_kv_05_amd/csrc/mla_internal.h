@@ -61,7 +61,8 @@ struct DecodeArgs {
   double rope_inv_freq[32];  // fused only: rope_base^(-2i/64), computed on the host in fp64
 };
 
-enum KvFormat { kKvBf16 = 0, kKvFp8V32 = 1 };
+enum KvFormat { kKvBf16 = 0, kKvFp8V32 = 1, kKvFp8V41 = 2 };
+constexpr int kFp8V41TokenBytes = 528;  // 512 e4m3 codes (all dims) + 16 e8m0 scales
 
 hipError_t launch_sched(const int32_t* seqlens, int batch, int rows, int topk, int num_slots,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream);

@@ -462,10 +462,19 @@ __device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8
 // FP8 V3.2 records of one half (32 x 656 B = 1312 chunks) are staged raw by
 // LDS-DMA into a 24 KB slot (24 loads per half, 6 per wave; the tail of the
 // slot is padding), then dequantised LDS -> LDS into a bf16 half tile.
+// V4.1 records (32 x 528 B = 1056 chunks) use the same slot with 20 loads.
 constexpr int kFp8ChunksPerTok = kFp8TokenBytes / 16;        // 41
 constexpr int kRawHalfChunks = kHalfRows * kFp8ChunksPerTok;  // 1312
 constexpr int kRawSlotBytes = 24 * 1024;
 constexpr int kRawLoadsPerWave = kRawSlotBytes / 1024 / kWaves;  // 6
+template <int KVF>
+constexpr int tok_bytes() { return KVF == kKvFp8V41 ? kFp8V41TokenBytes : kFp8TokenBytes; }
+template <int KVF>
+constexpr int raw_loads_per_wave() {  // 1 KB loads per wave covering a half's records
+  return (kHalfRows * tok_bytes<KVF>() / 16 + 64 * kWaves - 1) / (64 * kWaves);
+}
+static_assert(raw_loads_per_wave<kKvFp8V32>() == kRawLoadsPerWave, "V3.2 slot");
+static_assert(raw_loads_per_wave<kKvFp8V41>() * kWaves * 1024 <= kRawSlotBytes, "V4.1 slot");
 
 __device__ __forceinline__ void load_half_fp8_dense(uint8_t* raw, const uint8_t* kv, int64_t phys,
                                                     int valid, int h, int wave, int lane) {
@@ -480,19 +489,21 @@ __device__ __forceinline__ void load_half_fp8_dense(uint8_t* raw, const uint8_t*
   }
 }
 
+template <int KVF = kKvFp8V32>
 __device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t* kv,
                                                      const int32_t* ids, int nvalid, int wave,
                                                      int lane) {
+  constexpr int kTok = tok_bytes<KVF>(), kChunks = kTok / 16, kHalfChunks = kHalfRows * kChunks;
   lane = fresh_lane();
 #pragma unroll
-  for (int ii = 0; ii < kRawLoadsPerWave; ++ii) {
+  for (int ii = 0; ii < raw_loads_per_wave<KVF>(); ++ii) {
     const int i = ii * kWaves + wave;
     const int pos_all = i * 64 + lane;
-    const int r = pos_all / kFp8ChunksPerTok;
-    const int c = pos_all - r * kFp8ChunksPerTok;
-    const int id = (pos_all < kRawHalfChunks && r < nvalid) ? ids[r] : -1;
+    const int r = pos_all / kChunks;
+    const int c = pos_all - r * kChunks;
+    const int id = (pos_all < kHalfChunks && r < nvalid) ? ids[r] : -1;
     const uint8_t* g =
-        id >= 0 ? kv + (int64_t)id * kFp8TokenBytes + c * 16 : g_zero_row + (pos_all & 63) * 16;
+        id >= 0 ? kv + (int64_t)id * kTok + c * 16 : g_zero_row + (pos_all & 63) * 16;
     dma_glb16(lds_off(raw) + i * 1024, g);
   }
 }
@@ -547,6 +558,40 @@ __device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const u
   if (tid < 4 * kHalfRows) {
     const int r = tid >> 2, t = tid & 3;
     scl[t * 32 + scale_slot(r)] = *reinterpret_cast<const float*>(raw + r * kFp8TokenBytes + 512 + 4 * t);
+  }
+}
+
+// 32 raw V4.1 records -> the bf16 half tile's 512 main dims.  Every scale
+// is a power of two, 2^(e-127) (e8m0), so code * scale is a bf16 value and
+// each conversion (two codes, the scale folded in) is exact; no scale is
+// kept for later.  Code reads go out before any tile write, as above.
+__device__ __forceinline__ void dequant_v41(uint8_t* tile, const uint8_t* raw, int tid) {
+  tid = (tid & ~63) | fresh_lane();
+  constexpr int kPer = kHalfRows * 64 / kThreads;
+  uint2 codes[kPer];
+  uint32_t ebits[kPer];
+#pragma unroll
+  for (int kk = 0; kk < kPer; ++kk) {
+    const int k = kk * kThreads + tid;
+    const uint8_t* rec = raw + (k >> 6) * kFp8V41TokenBytes;
+    codes[kk] = *reinterpret_cast<const uint2*>(rec + (k & 63) * 8);
+    ebits[kk] = rec[512 + ((k & 63) >> 2)];  // 8 codes of dims 8c.. share scale c/4
+  }
+#pragma unroll
+  for (int kk = 0; kk < kPer; ++kk) {
+    const int k = kk * kThreads + tid;
+    const int r = k >> 6, c = k & 63;
+    // e8m0 -> fp32: 2^(e-127) for 1 <= e <= 254, 2^-127 (subnormal) for 0, NaN for 255
+    const uint32_t e = ebits[kk];
+    const float scale = __uint_as_float(e == 0 ? 0x00400000u : e == 255 ? 0x7FC00000u : e << 23);
+    const uint32_t cw[2] = {codes[kk].x, codes[kk].y};
+    uint32_t w[4];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], scale, false));
+      w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], scale, true));
+    }
+    *reinterpret_cast<uint4*>(tile + r * kMainStride + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -663,10 +708,15 @@ __device__ __forceinline__ void rope_pair(const RopeRow& r, const double* inv_fr
 // VGPRs, dims 384..575 (k-steps 24..35) in a per-wave LDS region
 // [32 rows][24 chunks] swizzled like the KV tile.
 // ---------------------------------------------------------------------------
+// k-steps of 16 dims in a query row: d_qk = 576, or 512 for V4.1 records
 template <int KVF>
-constexpr int q_reg_steps() { return KVF == kKvBf16 ? 36 : 24; }
+constexpr int ksteps() { return KVF == kKvFp8V41 ? 32 : 36; }
 template <int KVF>
-constexpr int q_lds_row_bytes() { return (36 - q_reg_steps<KVF>()) * 2 * 16; }    // fp8: 384
+constexpr int dqk_of() { return 16 * ksteps<KVF>(); }
+template <int KVF>
+constexpr int q_reg_steps() { return KVF == kKvFp8V32 ? 24 : ksteps<KVF>(); }
+template <int KVF>
+constexpr int q_lds_row_bytes() { return (ksteps<KVF>() - q_reg_steps<KVF>()) * 2 * 16; }    // fp8: 384
 template <int KVF>
 constexpr int q_lds_wave_bytes() { return 32 * q_lds_row_bytes<KVF>(); }          // fp8: 12288
 constexpr int kQRegStepsFp8 = q_reg_steps<kKvFp8V32>();
@@ -681,10 +731,10 @@ struct DecodeLayout {
   static constexpr int kIdsOff = kQOff + kWaves * q_lds_wave_bytes<KVF>();
   static constexpr int kWalkOff = kIdsOff + (SPARSE ? kIdsSlots * 256 : 0);  // 2 words per wave
   static constexpr int kSclOff = kWalkOff + (KVF == kKvBf16 && !SPARSE ? kWaves * 8 : 0);
-  static constexpr int kSmem = kSclOff + (KVF == kKvBf16 ? 0 : kScaleBytes);
+  static constexpr int kSmem = kSclOff + (KVF == kKvFp8V32 ? kScaleBytes : 0);
   // per-step VMEM instructions issued by every wave (loads + id fetch)
   static constexpr int kVmPerStep =
-      (KVF == kKvBf16 ? kLoadsPerHalf : kRawLoadsPerWave) + (SPARSE ? 1 : 0);
+      (KVF == kKvBf16 ? kLoadsPerHalf : raw_loads_per_wave<KVF>()) + (SPARSE ? 1 : 0);
 };
 
 __device__ __forceinline__ int seq_items(const DecodeArgs& a, int b) {
@@ -851,7 +901,7 @@ k_decode(DecodeArgs a) {
         load_half_bf16_sparse(smem + Lay::kTileOff + rs * kHalfBytes, a.kv, ids_slot(step), nvalid,
                               wave, lane);
       else
-        load_half_fp8_sparse(smem + Lay::kRawOff + rs * kRawSlotBytes, a.kv, ids_slot(step), nvalid,
+        load_half_fp8_sparse<KVF>(smem + Lay::kRawOff + rs * kRawSlotBytes, a.kv, ids_slot(step), nvalid,
                              wave, lane);
     }
   };
@@ -959,7 +1009,7 @@ k_decode(DecodeArgs a) {
     // fp32; no chunk has to wait for the whole row's statistic.
     float srow = a.scale_log2;  // log2(e) * softmax scale (* inv when fused)
     {
-      const uint16_t* qrow = a.q + ((int64_t)cb * a.rows + (row_ok ? row : 0)) * kDqk;
+      const uint16_t* qrow = a.q + ((int64_t)cb * a.rows + (row_ok ? row : 0)) * dqk_of<KVF>();
       float ss = 0.f;
       const double pos = (double)Lb - (double)a.s_q + (double)tok;
       // chunk ks (dims 16ks + 8half .. +7): q-hat chunk, then its home
@@ -974,7 +1024,7 @@ k_decode(DecodeArgs a) {
       };
       if constexpr (!FUSED) {
 #pragma unroll
-        for (int ks = 0; ks < 36; ++ks) put_q(ks, *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8));
+        for (int ks = 0; ks < ksteps<KVF>(); ++ks) put_q(ks, *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8));
       } else {
         // Six batches of 6 chunks (the RoPE chunks 32..35 first), each
         // batch's q and weight loads issued together: all 72 in flight at
@@ -1047,7 +1097,8 @@ k_decode(DecodeArgs a) {
     // S^T (32 keys x 32 rows) of the tile at LDS offset tb into sc, with the
     // LDS operands of k-step ks+kLa read before the MFMA of k-step ks (order
     // fixed by scheduling fences); hook(ks) runs after that MFMA is issued.
-    // (bf16 only: the query fragments are all in VGPRs.)
+    // (bf16 and V4.1 records: the query fragments are all in VGPRs; V4.1 has
+    // 32 k-steps, its 512 dims all in the main part of the tile.)
     auto qk = [&](int tb, f32x16& sc, auto&& hook) {
       constexpr int kLa = FUSED ? 3 : 4;
       const int ln = fresh_lane(), lr = ln & 31, lh = ln >> 5;
@@ -1058,14 +1109,15 @@ k_decode(DecodeArgs a) {
         if (ks < 32) return *reinterpret_cast<const bf16x8*>(smem + koff + 32 * ks);
         return *reinterpret_cast<const bf16x8*>(smem + kroff + ((((2 * (ks - 32)) | lh) ^ lfr) << 4));
       };
+      constexpr int kKS = ksteps<KVF>();
       bf16x8 kbuf[kLa];
 #pragma unroll
       for (int i = 0; i < kLa; ++i) kbuf[i] = read_k(i);
 #pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
+      for (int ks = 0; ks < kKS; ++ks) {
         const bf16x8 ka = kbuf[ks % kLa];
         const bf16x8 qb = qf[ks < kQR ? ks : 0];
-        if (ks + kLa < 36) kbuf[ks % kLa] = read_k(ks + kLa);
+        if (ks + kLa < kKS) kbuf[ks % kLa] = read_k(ks + kLa);
         if (ks == 0) mfma_s_first(sc, ka, qb);
         else mfma_s_acc(sc, ka, qb);
         hook(ks);
@@ -1374,13 +1426,19 @@ k_decode(DecodeArgs a) {
           else wait_vmcnt<Lay::kVmPerStep>();
           lds_barrier();  // every wave's loads of this step landed
         }
-        dequant_codes(smem + Lay::kTileOff, reinterpret_cast<float*>(smem + Lay::kSclOff),
-                      smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
+        if constexpr (KVF == kKvFp8V41)
+          dequant_v41(smem + Lay::kTileOff, smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
+        else
+          dequant_codes(smem + Lay::kTileOff, reinterpret_cast<float*>(smem + Lay::kSclOff),
+                        smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
         lds_barrier();  // the tile is staged; raw slot (step+2)%3 (dequantised last step) is free
         const bool hk = has_keys(ps);
         f32x16 sc;
         SmState st;
-        if (hk) qk_fp8(tile_off(step), sc);
+        if (hk) {
+          if constexpr (KVF == kKvFp8V41) qk(tile_off(step), sc, [](int) {});  // exact bf16 K: plain S^T
+          else qk_fp8(tile_off(step), sc);
+        }
         // The loads of step+2 go out after S^T: the register reloads inside
         // S^T wait for every older load, and would otherwise wait for these.
         issue_next(step);
@@ -1388,7 +1446,12 @@ k_decode(DecodeArgs a) {
 #pragma unroll
           for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc, st, key0_of(ps), step);
           rescale_o(st);
-          pv_fp8(tile_off(step), sc);
+          if constexpr (KVF == kKvFp8V41) {
+            valu_to_mfma_settle(st.pf[0], st.pf[1]);
+            pv(tile_off(step), st.pf);
+          } else {
+            pv_fp8(tile_off(step), sc);
+          }
         }
       }
     }
@@ -1871,6 +1934,10 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool f
                               : launch_decode_t<kKvBf16, false, false>(a, stream, start, stop);
     return fused ? launch_decode_t<kKvBf16, true, true>(a, stream, start, stop)
                  : launch_decode_t<kKvBf16, true, false>(a, stream, start, stop);
+  }
+  if (kv_format == kKvFp8V41) {  // sparse, unfused only (checked by the caller)
+    if (!sparse || fused) return hipErrorInvalidValue;
+    return launch_decode_t<kKvFp8V41, true, false>(a, stream, start, stop);
   }
   if (!sparse) return fused ? launch_decode_t<kKvFp8V32, false, true>(a, stream, start, stop)
                             : launch_decode_t<kKvFp8V32, false, false>(a, stream, start, stop);

@@ -109,6 +109,22 @@ def test_sparse_rules():
     assert st == 2, msg
 
 
+def test_v41_format_rules():
+    """The V4.1 FP8 format: head dim 512, sparse indices, no fusion."""
+    a = Fake.ADDR
+    v41 = dict(kv_format=2, d_qk=512, indices=a + 65536, topk=64, block_table=None, softmax_scale=512 ** -0.5)
+    st, msg = status(good_params(**{**v41, "d_qk": 576}))
+    assert st == 2 and "512" in msg, msg
+    st, msg = status(good_params(**{**v41, "indices": None, "topk": 0, "block_table": a + 8192}))
+    assert st == 2, msg
+    st, msg = status(good_params(**{**v41, "fused": 1, "norm_weight": a + 4096, "out_scale": a + 8192,
+                                    "rope_base": 10000.0}))
+    assert st == 2, msg
+    # d_qk 512 is still refused for the other formats
+    st, msg = status(good_params(kv_format=1, d_qk=512))
+    assert st == 2, msg
+
+
 def test_row_groups_need_slots_multiple_of_8():
     ws = B.load_library().mla_workspace_bytes(2, 2, 128, 12)
     st, msg = status(good_params(s_q=2, num_slots=12, workspace_bytes=ws))

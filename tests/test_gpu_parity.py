@@ -73,6 +73,16 @@ def test_sparse_fp8(slots):
     _parity(p, num_slots=slots, what="sparse-fp8")
 
 
+@gpu
+@pytest.mark.parametrize("slots,s_q", [(None, 1), (8, 1), (16, 2)])
+def test_sparse_fp8_v41(slots, s_q):
+    """V4.1 cache (528 B records, head dim 512, V = K): ragged valid counts,
+    padded rows, forced splits, and two query tokens (two row groups)."""
+    p = W.make_sparse_fp8_v41("spf8v41", batch=4, s_q=s_q, h_q=128, cache_len=1024, topk=300, seed=19,
+                              pad_frac=0.5)
+    _parity(p, num_slots=slots, what=f"sparse-fp8-v41 s_q={s_q}")
+
+
 # The fused path rounds q-hat = RoPE(RMSNorm(q)) to bf16 before the MFMA; on
 # this workload that rounding alone moves the LSE by 3.35e-3 in exact
 # arithmetic (the kernel adds ~1e-7 on top).  The O / FP8 output meets its
@@ -240,6 +250,15 @@ def test_full_config4_sampled():
     pad = [int(b) for b in range(p.batch) if (p.indices[b, 0] < 0).any()][:3]
     rows += [(b, 0, 5) for b in pad]
     _sampled(p, rows, "config4")
+
+
+@gpu
+def test_full_config_v41_sampled():
+    p = W.config_v41()
+    rows = _rows(p, 16, 9)
+    pad = [int(b) for b in range(p.batch) if (p.indices[b, 0] < 0).any()][:3]
+    rows += [(b, 0, 11) for b in pad]
+    _sampled(p, rows, "config-v41")
 
 
 @gpu
