@@ -561,6 +561,11 @@ __device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const u
   }
 }
 
+// e8m0 scale -> fp32 2^(e-127), branch-free (one v_ldexp_f32).  Codes 0..254
+// are exact (0 gives the fp32 subnormal 2^-127); the NaN code 0xFF gives
+// +inf, so a record with it still turns its keys non-finite.
+__device__ __forceinline__ float e8m0_scale(uint32_t e) { return __builtin_ldexpf(1.0f, (int)e - 127); }
+
 // 32 raw V4.1 records -> the bf16 half tile's 512 main dims.  Every scale
 // is a power of two, 2^(e-127) (e8m0), so code * scale is a bf16 value and
 // each conversion (two codes, the scale folded in) is exact; no scale is
@@ -581,9 +586,7 @@ __device__ __forceinline__ void dequant_v41(uint8_t* tile, const uint8_t* raw, i
   for (int kk = 0; kk < kPer; ++kk) {
     const int k = kk * kThreads + tid;
     const int r = k >> 6, c = k & 63;
-    // e8m0 -> fp32: 2^(e-127) for 1 <= e <= 254, 2^-127 (subnormal) for 0, NaN for 255
-    const uint32_t e = ebits[kk];
-    const float scale = __uint_as_float(e == 0 ? 0x00400000u : e == 255 ? 0x7FC00000u : e << 23);
+    const float scale = e8m0_scale(ebits[kk]);
     const uint32_t cw[2] = {codes[kk].x, codes[kk].y};
     uint32_t w[4];
 #pragma unroll
@@ -593,6 +596,30 @@ __device__ __forceinline__ void dequant_v41(uint8_t* tile, const uint8_t* raw, i
     }
     *reinterpret_cast<uint4*>(tile + r * kMainStride + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
+}
+
+// The same conversion one chunk at a time (chunk kk: 8 codes per thread),
+// for spreading it between the MFMAs of another step's S^T.
+struct V41Chunk {
+  uint2 code;
+  uint32_t e;
+};
+__device__ __forceinline__ V41Chunk v41_read(const uint8_t* raw, int wave_base, int kk) {
+  const int k = kk * kThreads + (wave_base | fresh_lane());
+  const uint8_t* rec = raw + (k >> 6) * kFp8V41TokenBytes;
+  return V41Chunk{*reinterpret_cast<const uint2*>(rec + (k & 63) * 8), rec[512 + ((k & 63) >> 2)]};
+}
+__device__ __forceinline__ void v41_write(uint8_t* tile, int wave_base, int kk, const V41Chunk& ch) {
+  const int k = kk * kThreads + (wave_base | fresh_lane());
+  const float scale = e8m0_scale(ch.e);
+  const uint32_t cw[2] = {ch.code.x, ch.code.y};
+  uint32_t w[4];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], scale, false));
+    w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], scale, true));
+  }
+  *reinterpret_cast<uint4*>(tile + (k >> 6) * kMainStride + (k & 63) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Dequantise 32 raw records into the bf16 half tile: dims < 512 are
@@ -725,7 +752,7 @@ constexpr int kIdsSlots = 6;
 template <int KVF, bool SPARSE>
 struct DecodeLayout {
   static constexpr int kTileOff = 0;                                   // bf16 half tiles
-  static constexpr int kTiles = KVF == kKvBf16 ? kTileRing : 1;
+  static constexpr int kTiles = KVF == kKvBf16 ? kTileRing : KVF == kKvFp8V41 ? 2 : 1;
   static constexpr int kRawOff = kTiles * kHalfBytes;                  // fp8 raw slots
   static constexpr int kQOff = kRawOff + (KVF == kKvBf16 ? 0 : kRing * kRawSlotBytes);
   static constexpr int kIdsOff = kQOff + kWaves * q_lds_wave_bytes<KVF>();
@@ -943,14 +970,17 @@ k_decode(DecodeArgs a) {
       }
     }
   };
+  // FP8 loads lead by kRawAhead steps, ids by kRawAhead + 2 (V4.1, whose
+  // step dequantises one step ahead, by one more)
+  constexpr int kRawAhead = KVF == kKvFp8V41 ? 3 : 2;
   auto issue_next = [&](int step) {
-    if (step + 2 < nsteps) {
-      issue_load(step + 2);
+    if (step + kRawAhead < nsteps) {
+      issue_load(step + kRawAhead);
       advance_load();
     }
     if constexpr (SPARSE) {
-      if (step + 4 < nsteps) {
-        fetch_ids(fb, fj, fh, step + 4);
+      if (step + kRawAhead + 2 < nsteps) {
+        fetch_ids(fb, fj, fh, step + kRawAhead + 2);
         advance(fb, fj, fh);
       }
     }
@@ -960,14 +990,14 @@ k_decode(DecodeArgs a) {
   // the first piece's prologue (bf16: steps 0 and 1 right after the query
   // loads, step 2 once the walker has landed the block of its item)
   if constexpr (SPARSE) {
-    for (int s = 0; s < min(4, nsteps); ++s) {
+    for (int s = 0; s < min(KVF == kKvFp8V41 ? 5 : 4, nsteps); ++s) {
       fetch_ids(fb, fj, fh, s);
       advance(fb, fj, fh);
     }
     __builtin_amdgcn_s_waitcnt(0);
   }
   auto issue_first_loads = [&]() {
-    for (int s = 0; s < min(2, nsteps); ++s) {
+    for (int s = 0; s < min(KVF == kKvFp8V41 ? 3 : 2, nsteps); ++s) {
       issue_load(s);
       advance_load();
     }
@@ -1092,6 +1122,7 @@ k_decode(DecodeArgs a) {
     // ======== building blocks of one 32-key step
     auto tile_off = [&](int st) -> int {
       if constexpr (KVF == kKvBf16) return Lay::kTileOff + (st % kTileRing) * kHalfBytes;
+      else if constexpr (KVF == kKvFp8V41) return Lay::kTileOff + (st & 1) * kHalfBytes;
       else return Lay::kTileOff;
     };
     // S^T (32 keys x 32 rows) of the tile at LDS offset tb into sc, with the
@@ -1413,6 +1444,52 @@ k_decode(DecodeArgs a) {
         sc_cur = sc_nxt;
         cur_has = nxt_has;
       }
+    } else if constexpr (KVF == kKvFp8V41) {
+      // ---- V4.1: two bf16 tiles.  Step s runs S^T, softmax and P.V on tile
+      // s%2 and meanwhile dequantises step s+1's records into the other tile,
+      // one chunk between every four MFMAs of S^T; one barrier per step.
+      // Raw records go out three steps ahead (into the slot of the records
+      // dequantised a step ago), ids five.
+      const int wave_base = tid & ~63;
+      auto dq_tile = [&](int st) { return smem + tile_off(st); };
+      auto dq_raw = [&](int st) { return smem + Lay::kRawOff + (st % kRing) * kRawSlotBytes; };
+      if (step == 0) {  // the first step's tile: the prologue drain landed its records
+        dequant_v41(dq_tile(0), dq_raw(0), tid);
+        lds_barrier();
+      }
+      for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
+        if (ps > 0) {
+          // The previous step issued raw(step+2) (if any) and ids(step+4) (if
+          // any), after everything this step needs: raw(step+1), ids(step+3).
+          if (step + 2 >= nsteps) wait_vmcnt<0>();
+          else if (step + 4 >= nsteps) wait_vmcnt<Lay::kVmPerStep - 1>();
+          else wait_vmcnt<Lay::kVmPerStep>();
+          lds_barrier();  // tile step%2 staged by every wave; P.V(step-1) done with the other
+        }
+        issue_next(step);
+        const bool hk = has_keys(ps);
+        const bool dq = step + 1 < nsteps;
+        f32x16 sc;
+        SmState st;
+        if (hk && dq) {
+          V41Chunk ch;
+          qk(tile_off(step), sc, [&](int ks) {
+            if ((ks & 3) == 0) ch = v41_read(dq_raw(step + 1), wave_base, ks >> 2);
+            else if ((ks & 3) == 3) v41_write(dq_tile(step + 1), wave_base, ks >> 2, ch);
+          });
+        } else if (hk) {
+          qk(tile_off(step), sc, [](int) {});
+        } else if (dq) {
+          dequant_v41(dq_tile(step + 1), dq_raw(step + 1), tid);
+        }
+        if (hk) {
+#pragma unroll
+          for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc, st, key0_of(ps), step);
+          rescale_o(st);
+          valu_to_mfma_settle(st.pf[0], st.pf[1]);
+          pv(tile_off(step), st.pf);
+        }
+      }
     } else {
       // ---- FP8: one bf16 tile, dequantised from the raw ring each step
       for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
@@ -1426,19 +1503,13 @@ k_decode(DecodeArgs a) {
           else wait_vmcnt<Lay::kVmPerStep>();
           lds_barrier();  // every wave's loads of this step landed
         }
-        if constexpr (KVF == kKvFp8V41)
-          dequant_v41(smem + Lay::kTileOff, smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
-        else
-          dequant_codes(smem + Lay::kTileOff, reinterpret_cast<float*>(smem + Lay::kSclOff),
-                        smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
+        dequant_codes(smem + Lay::kTileOff, reinterpret_cast<float*>(smem + Lay::kSclOff),
+                      smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
         lds_barrier();  // the tile is staged; raw slot (step+2)%3 (dequantised last step) is free
         const bool hk = has_keys(ps);
         f32x16 sc;
         SmState st;
-        if (hk) {
-          if constexpr (KVF == kKvFp8V41) qk(tile_off(step), sc, [](int) {});  // exact bf16 K: plain S^T
-          else qk_fp8(tile_off(step), sc);
-        }
+        if (hk) qk_fp8(tile_off(step), sc);
         // The loads of step+2 go out after S^T: the register reloads inside
         // S^T wait for every older load, and would otherwise wait for these.
         issue_next(step);
@@ -1446,12 +1517,7 @@ k_decode(DecodeArgs a) {
 #pragma unroll
           for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc, st, key0_of(ps), step);
           rescale_o(st);
-          if constexpr (KVF == kKvFp8V41) {
-            valu_to_mfma_settle(st.pf[0], st.pf[1]);
-            pv(tile_off(step), st.pf);
-          } else {
-            pv_fp8(tile_off(step), sc);
-          }
+          pv_fp8(tile_off(step), sc);
         }
       }
     }
