@@ -1834,15 +1834,26 @@ __device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub,
   }
 }
 
-// The combine as its own launch: one workgroup per (sequence, row group,
-// 32-row tile).
+// The combine as its own launch, per (sequence, row group, 32-row tile).
+// Plain output: the tile's four d-tile quarters go to two workgroups of two
+// waves each (twice the workgroups in flight on a streaming kernel).  Fused:
+// one workgroup of four waves, which share the row amax.
 template <bool FUSED>
-__global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
+__global__ void __launch_bounds__(FUSED ? 256 : 128) k_combine(DecodeArgs a) {
   __shared__ float amax_s[4][64];
-  const int wt = blockIdx.x & 3;
-  const int g = (blockIdx.x >> 2) % a.groups;
-  const int b = (blockIdx.x >> 2) / a.groups;
-  combine_rows<FUSED, false>(a, b, g, wt, threadIdx.x >> 6, threadIdx.x & 63, amax_s);
+  if constexpr (FUSED) {
+    const int wt = blockIdx.x & 3;
+    const int g = (blockIdx.x >> 2) % a.groups;
+    const int b = (blockIdx.x >> 2) / a.groups;
+    combine_rows<FUSED, false>(a, b, g, wt, threadIdx.x >> 6, threadIdx.x & 63, amax_s);
+  } else {
+    const int u = blockIdx.x >> 1;
+    const int wt = u & 3;
+    const int g = (u >> 2) % a.groups;
+    const int b = (u >> 2) / a.groups;
+    combine_rows<FUSED, false>(a, b, g, wt, 2 * (blockIdx.x & 1) + (threadIdx.x >> 6), threadIdx.x & 63,
+                               amax_s);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2015,7 +2026,7 @@ hipError_t launch_combine(const DecodeArgs& a, bool fused, hipStream_t stream) {
   const int grid = a.batch * a.groups * 4;
   if (grid == 0) return hipSuccess;
   if (fused) hipLaunchKernelGGL(k_combine<true>, dim3(grid), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(k_combine<false>, dim3(grid), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(k_combine<false>, dim3(2 * grid), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 
