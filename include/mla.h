@@ -184,7 +184,8 @@ mla_status mla_combine(const mla_decode_params* params, void* stream);
 /* Test hook: the 64 x 576 bf16 tile the KV loader stages for work item j
  * of sequence b (query token t when sparse), written un-swizzled to
  * dst [64][576] bf16: gathered rows, dequantised when FP8, zero rows past
- * the sequence or for -1 indices. */
+ * the sequence or for -1 indices.  Not available for MLA_KV_FP8_V41
+ * (MLA_ERR_UNSUPPORTED). */
 mla_status mla_debug_gather(const mla_decode_params* params, int32_t b, int32_t t, int32_t j,
                             void* dst, void* stream);
 
