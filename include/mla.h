@@ -157,9 +157,11 @@ typedef struct mla_decode_params {
  * itself, with MLA_FLAG_MERGE_IN_KERNEL); others write their output
  * directly.  Decode calls that share a num_splits buffer must be ordered on
  * one stream.
- * Supported: h_kv = 1, d_qk = 576, d_v = 512, page 64, s_q*h_q <= 65536;
- * sparse needs causal = 0 and (s_q == 1 or h_q % 128 == 0); FP8 KV needs
- * indices; fused needs s_q*h_q of whole heads as above.
+ * Supported: h_kv = 1, d_qk = 576 (512 with MLA_KV_FP8_V41), d_v = 512,
+ * page 64, s_q*h_q <= 65536;
+ * sparse needs causal = 0 and (s_q == 1 or h_q % 128 == 0); MLA_KV_FP8_V32
+ * works paged or sparse, fused or not; MLA_KV_FP8_V41 needs indices and
+ * fused = 0; fused needs s_q*h_q of whole heads as above.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP (launch failure). */
 mla_status mla_decode(const mla_decode_params* params, void* stream);
 

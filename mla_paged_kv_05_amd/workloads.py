@@ -256,6 +256,32 @@ def make_sparse_bf16_from_dense(p: Problem, topk: int, seed: int) -> Problem:
     return q
 
 
+def with_fp8v32(p: Problem, seed: int) -> Problem:
+    """The same problem over a V3.2 FP8 cache: every stored token (a bf16 row
+    that is not the NaN poison) becomes a 656 B record whose latent dims are
+    its bf16 values divided by one scale per 128 dims, 2^U(-4,4), rounded to
+    e4m3, and whose RoPE dims are its bf16 values unchanged.  Poisoned rows
+    stay poisoned (NaN codes, scales and RoPE)."""
+    assert p.kv_format == "bf16" and p.d_qk == D_QK
+    rng = np.random.Generator(np.random.PCG64(seed))
+    flat = p.kv.reshape(-1, D_QK)
+    used = np.nonzero(flat[:, 0] != BF16_NAN)[0]
+    kv = np.zeros((flat.shape[0], FP8_TOKEN_BYTES), dtype=np.uint8)
+    kv[:, :512] = FP8_NAN
+    kv[:, 512:528] = np.frombuffer(np.full(4, np.nan, dtype=np.float32).tobytes(), dtype=np.uint8)
+    kv[:, 528:] = np.frombuffer(np.full(64, BF16_NAN, dtype=np.uint16).tobytes(), dtype=np.uint8)
+    n = int(used.shape[0])
+    x = (flat[used, :512].astype(np.uint32) << 16).view(np.float32)
+    sc = np.exp2(rng.uniform(-4.0, 4.0, size=(n, 4))).astype(np.float32)
+    kv[used, :512] = _e4m3_codes(x / np.repeat(sc, 128, axis=1))
+    kv[used, 512:528] = sc.view(np.uint8).reshape(n, 16)
+    kv[used, 528:] = np.ascontiguousarray(flat[used, 512:]).view(np.uint8).reshape(n, 128)
+    q = Problem(**{**p.__dict__})
+    q.kv = kv.reshape(-1, PAGE, FP8_TOKEN_BYTES)
+    q.kv_format = "fp8v32"
+    return q
+
+
 # ---------------------------------------------------------------------------
 # The five standard workloads
 # ---------------------------------------------------------------------------

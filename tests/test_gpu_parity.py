@@ -92,6 +92,34 @@ FUSED_BF16_QHAT_LSE = 4e-3
 
 
 @gpu
+@pytest.mark.parametrize("causal,s_q,slots", [(False, 1, None), (True, 2, 16)])
+def test_dense_fp8(causal, s_q, slots):
+    """Paged (not sparse) decode over a V3.2 FP8 cache: ragged lengths with an
+    empty row, forced splits, causal multi-token queries."""
+    base = W.make_dense("df8", [1, 63, 700, 0, 129, 2000], s_q=s_q, h_q=128, seed=18,
+                        causal=causal)
+    _parity(W.with_fp8v32(base, seed=6), num_slots=slots, what=f"dense-fp8 causal={causal}")
+
+
+@gpu
+@pytest.mark.parametrize("sparse", [False, True])
+def test_fused_fp8(sparse):
+    """The fused prologue/epilogue over a V3.2 FP8 cache, paged and sparse."""
+    base = W.make_dense("ff8", [70, 1500, 5, 700], s_q=1, h_q=128, seed=19, fused=True)
+    if sparse:
+        base = W.make_sparse_bf16_from_dense(base, topk=300, seed=7)
+    _parity(W.with_fp8v32(base, seed=8), num_slots=8, what=f"fused-fp8 sparse={sparse}",
+            fused_lse_tol=FUSED_BF16_QHAT_LSE)
+
+
+@gpu
+def test_fused_sparse_bf16():
+    base = W.make_dense("fsp", [90, 400, 3, 1000], s_q=1, h_q=128, seed=20, fused=True)
+    p = W.make_sparse_bf16_from_dense(base, topk=200, seed=9)
+    _parity(p, num_slots=16, what="fused-sparse-bf16", fused_lse_tol=FUSED_BF16_QHAT_LSE)
+
+
+@gpu
 @pytest.mark.parametrize("slots", [None, 8])
 def test_fused(slots):
     p = W.make_dense("fused", [70, 2048, 5, 700], s_q=1, h_q=128, seed=15, fused=True)
