@@ -162,6 +162,9 @@ typedef struct mla_decode_params {
  * sparse needs causal = 0 and (s_q == 1 or h_q % 128 == 0); MLA_KV_FP8_V32
  * works paged or sparse, fused or not; MLA_KV_FP8_V41 needs indices and
  * fused = 0; fused needs s_q*h_q of whole heads as above.
+ * batch = 0 is a no-op that launches nothing; q, kv, block_table,
+ * cache_seqlens, out and lse may then be NULL (sched_meta, num_splits and
+ * the workspace may not).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP (launch failure). */
 mla_status mla_decode(const mla_decode_params* params, void* stream);
 

@@ -118,7 +118,10 @@ static mla_status build_args(const mla_decode_params* p, mla::DecodeArgs& a, boo
   const int64_t rows = (int64_t)p->s_q * p->h_q;
   if (rows > mla::kMaxRows) return fail(MLA_ERR_UNSUPPORTED, "s_q*h_q=%lld > %d", (long long)rows, mla::kMaxRows);
   if (p->batch > MLA_MAX_BATCH) return fail(MLA_ERR_UNSUPPORTED, "batch %d > %d", p->batch, MLA_MAX_BATCH);
-  if (!p->q || !p->kv || !p->out || !p->lse || !p->cache_seqlens)
+  // an empty batch reads and writes none of the per-sequence arrays, so
+  // they may be NULL then (zero-size tensors have no address)
+  const bool empty = p->batch == 0;
+  if (!empty && (!p->q || !p->kv || !p->out || !p->lse || !p->cache_seqlens))
     return fail(MLA_ERR_INVALID_ARG, "q, kv, out, lse and cache_seqlens must be non-NULL");
   if (!aligned(p->q, 16) || !aligned(p->kv, 16) || !aligned(p->out, 16))
     return fail(MLA_ERR_INVALID_ARG, "q, kv and out must be 16-byte aligned");
@@ -133,7 +136,7 @@ static mla_status build_args(const mla_decode_params* p, mla::DecodeArgs& a, boo
       return fail(MLA_ERR_UNSUPPORTED, "sparse needs s_q == 1 or h_q %% 128 == 0 (s_q=%d h_q=%d)",
                   p->s_q, p->h_q);
   } else {
-    if (!p->block_table || p->max_blocks_per_seq < 1)
+    if ((!empty && !p->block_table) || p->max_blocks_per_seq < 1)
       return fail(MLA_ERR_INVALID_ARG, "dense decode needs block_table and max_blocks_per_seq >= 1");
     if (p->topk != 0) return fail(MLA_ERR_INVALID_ARG, "topk=%d without indices", p->topk);
   }

@@ -145,3 +145,13 @@ def test_metadata_rejects():
 def test_zero_batch_is_a_noop():
     st, msg = status(good_params(batch=0, workspace_bytes=B.load_library().mla_workspace_bytes(0, 1, 128, 8)))
     assert st == 0, msg
+    # zero-size tensors have no address: an empty batch may pass NULL for
+    # every per-sequence array, but not for the metadata or the workspace
+    nulls = dict(q=None, kv=None, block_table=None, cache_seqlens=None, out=None, lse=None)
+    ws0 = B.load_library().mla_workspace_bytes(0, 1, 128, 8)
+    st, msg = status(good_params(batch=0, workspace_bytes=ws0, **nulls))
+    assert st == 0, msg
+    st, _ = status(good_params(batch=0, workspace_bytes=ws0, sched_meta=None, **nulls))
+    assert st == 1
+    st, _ = status(good_params(batch=1, workspace_bytes=ws0, q=None))
+    assert st == 1
