@@ -40,7 +40,11 @@
  *    sequence of length L sees keys j <= L - s_q + t.
  *  - A row with no visible key has O = 0 and LSE = -inf.
  *  - Sparse ids are flat token ids into the pool (block * 64 + offset);
- *    duplicates count as separate keys; -1 entries are skipped.
+ *    duplicates count as separate keys; -1 entries are skipped, and so is
+ *    any id outside the pool [0, num_blocks * 64).
+ *  - A block_table entry outside [0, num_blocks) names no page: its 64
+ *    positions read as all-zero keys (they stay visible, as positions);
+ *    so do positions past max_blocks_per_seq pages, which have no entry.
  *  - e4m3 is OCP E4M3FN (bias 7, no infinities, S.1111.111 is NaN, max
  *    448); encoding rounds to nearest, ties to even, saturating to +-448.
  *  - RMSNorm runs over all 576 dims of a head with a 576-entry weight;
@@ -142,8 +146,13 @@ typedef struct {
   double rope_base;
 } orc_problem;
 
-/* Fetch key vector (all d_qk dims) of flat token id `tok` as fp64. */
+/* Fetch key vector (all d_qk dims) of flat token id `tok` as fp64; a token
+ * outside the pool reads as the zero vector. */
 static void fetch_token(const orc_problem* p, int64_t tok, double* k) {
+  if (tok < 0 || tok >= p->num_blocks * ORC_PAGE) {
+    for (int d = 0; d < p->d_qk; ++d) k[d] = 0.0;
+    return;
+  }
   if (p->kv_format == 0) {
     const uint16_t* src = (const uint16_t*)p->kv + tok * (int64_t)p->d_qk;
     for (int d = 0; d < p->d_qk; ++d) k[d] = orc_bf16_to_f64(src[d]);
@@ -167,9 +176,12 @@ static void fetch_token(const orc_problem* p, int64_t tok, double* k) {
   }
 }
 
-/* Flat token id of logical position j of sequence b (dense paging). */
+/* Flat token id of logical position j of sequence b (dense paging); -1
+ * when the block_table entry names no page of the pool. */
 static int64_t dense_token(const orc_problem* p, int b, int64_t j) {
+  if (j / ORC_PAGE >= p->max_blocks) return -1; /* no block_table entry */
   int32_t blk = p->block_table[(int64_t)b * p->max_blocks + j / ORC_PAGE];
+  if (blk < 0 || blk >= p->num_blocks) return -1;
   return (int64_t)blk * ORC_PAGE + (j % ORC_PAGE);
 }
 
@@ -249,7 +261,7 @@ static int64_t visible_tokens(const orc_problem* p, int b, int t, int64_t* ids) 
   if (p->indices) {
     const int32_t* row = p->indices + ((int64_t)b * p->s_q + t) * p->topk;
     for (int k = 0; k < p->topk; ++k)
-      if (row[k] >= 0) ids[n++] = row[k];
+      if (row[k] >= 0 && row[k] < p->num_blocks * ORC_PAGE) ids[n++] = row[k];
     return n;
   }
   int64_t L = p->seqlens[b];
@@ -368,7 +380,7 @@ int orc_decode_row_subset(const orc_problem* p, int b, int t, int h, int64_t n,
  * n_b   = ceil(topk/64) if topk > 0 else ceil(seqlens[b]/64)   (work items)
  * F     = max(1, ceil(min(M,128)/32))                            (piece cost)
  * U_0 = 0, U_{b+1} = U_b + F + n_b, T = U_B
- * cap   = max(ceil((T+1)/S), 2F)
+ * cap   = ceil((T+1)/S)
  * Batch b has max(n_b,1) items; item j sits at P(b,j) = U_b + F + j and
  * belongs to slot floor(P/cap).  (An empty batch has one item, no KV.)
  * splits_b = floor(P(b,last)/cap) - floor(P(b,0)/cap) + 1
@@ -393,7 +405,6 @@ int orc_sched_plan(const int32_t* seqlens, int B, int M, int topk, int S, int32_
   }
   int64_t T = U[B];
   int64_t cap = (T + 1 + S - 1) / S;
-  if (cap < 2 * F) cap = 2 * F;
   for (int s = 0; s < S; ++s) {
     int32_t* ms = meta + 8 * (int64_t)s;
     ms[0] = -1; ms[1] = 0; ms[2] = -1; ms[3] = 0; ms[4] = 0; ms[5] = 0; ms[6] = 0; ms[7] = 0;

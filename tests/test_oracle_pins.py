@@ -483,7 +483,10 @@ def sched_check(seqlens, rows, topk, S):
         assert len(run) == cnt
         cost = len(run) + F * sum(1 for (b, j) in run if j == 0)
         tot = sum(items) + F * B
-        assert cost <= max(-(-(tot + 1) // S), 2 * F) + F
+        cap = -(-(tot + 1) // S)
+        assert cost <= cap + F
+        if tot + 1 <= S:  # a small total: one item per slot, spread over the machine
+            assert cnt == 1
         seen += run
     assert seen == [(b, j) for b in range(B) for j in range(items[b])]
     # splits per batch = number of slots touching it; k0 numbers them in order
@@ -499,6 +502,8 @@ def sched_check(seqlens, rows, topk, S):
     for b in range(B):
         assert ns[b + 1] - ns[b] == len(touch[b])
     assert ns[B] <= B + S - 1
+    if sum(items) + F * B + 1 <= S:
+        assert sum(1 for s in range(S) if meta[s, 0] >= 0) == sum(items)
     return meta, ns
 
 
@@ -510,6 +515,8 @@ def sched_check(seqlens, rows, topk, S):
     ([10] * 64, 128, 2048, 256),
     ([1], 128, 0, 1),
     ([], 128, 0, 16),
+    ([4000], 128, 0, 256),          # one sequence: 63 items over 63 slots
+    ([2048, 16384, 0], 128, 0, 256),
 ])
 def test_sched_plan_invariants(seqlens, rows, topk, S):
     sched_check(np.array(seqlens, dtype=np.int32), rows, topk, S)
@@ -521,3 +528,59 @@ def test_sched_plan_workload_sizes():
     rng = np.random.default_rng(0)
     sched_check(rng.integers(1024, 8193, 64).astype(np.int32), 128, 0, 256)
     sched_check(rng.integers(0, 3000, 300).astype(np.int32), 32, 0, 80)
+
+
+# ------------------------------------------------- indices outside the pool
+# The pages give -1 as the mark of an invalid sparse entry (AI Wiki, FlashMLA,
+# section "Interfaces") and say nothing of ids or block_table entries that
+# name no token of the pool.  Reading: such a sparse id is masked like -1; a
+# block_table entry outside [0, num_blocks), and a position past
+# max_blocks_per_seq pages, reads as an all-zero key.  Each pin compares the
+# oracle on the bad input with the oracle on an input that means the same by
+# the pinned rules above (a -1 entry, or an explicit all-zero page).
+def test_out_of_pool_sparse_ids_are_masked():
+    import dataclasses
+    p = W.make_sparse_bf16_from_dense(tiny((37, 150, 3), s_q=2), topk=70, seed=3)
+    ntok = p.num_blocks * 64
+    rng = np.random.default_rng(5)
+    sel = rng.random(p.indices.shape) < 0.3
+    repl = rng.choice(np.array([ntok, ntok + 63, 2 ** 31 - 1, -2, -7], dtype=np.int64),
+                      size=p.indices.shape).astype(np.int32)
+    bad = p.indices.copy()
+    bad[sel] = repl[sel]
+    masked = p.indices.copy()
+    masked[sel] = -1
+    r_bad = oracle.decode(dataclasses.replace(p, indices=bad))
+    r_masked = oracle.decode(dataclasses.replace(p, indices=masked))
+    assert np.array_equal(r_bad["o"], r_masked["o"]) and np.array_equal(r_bad["lse"], r_masked["lse"])
+    o, lse = brute_decode(dataclasses.replace(p, indices=masked))
+    assert np.max(np.abs(r_masked["o"] - o)) < 1e-12
+
+
+def test_out_of_pool_block_reads_as_zero_page():
+    import dataclasses
+    p = tiny((37, 200, 70))
+    nb = p.num_blocks
+    zero_pool = np.concatenate([p.kv, np.zeros((1,) + p.kv.shape[1:], dtype=p.kv.dtype)])
+    bt_zero, bt_bad = p.block_table.copy(), p.block_table.copy()
+    bt_zero[1, 1] = nb       # the appended all-zero page
+    bt_zero[2, 0] = nb
+    bt_bad[1, 1] = nb + 5    # outside the pool
+    bt_bad[2, 0] = -3
+    r_zero = oracle.decode(dataclasses.replace(p, kv=zero_pool, num_blocks=nb + 1, block_table=bt_zero))
+    r_bad = oracle.decode(dataclasses.replace(p, block_table=bt_bad))
+    assert np.array_equal(r_zero["o"], r_bad["o"]) and np.array_equal(r_zero["lse"], r_bad["lse"])
+    o, lse = brute_decode(dataclasses.replace(p, kv=zero_pool, num_blocks=nb + 1, block_table=bt_zero))
+    assert np.max(np.abs(r_zero["o"] - o)) < 1e-12 and np.max(np.abs(r_zero["lse"] - lse)) < 1e-12
+
+
+def test_positions_past_the_block_table_read_as_zero_keys():
+    import dataclasses
+    p = tiny((37, 200, 70))  # sequence 1 spans 4 pages
+    nb = p.num_blocks
+    zero_pool = np.concatenate([p.kv, np.zeros((1,) + p.kv.shape[1:], dtype=p.kv.dtype)])
+    bt_zero = p.block_table.copy()
+    bt_zero[1, 2:] = nb
+    r_zero = oracle.decode(dataclasses.replace(p, kv=zero_pool, num_blocks=nb + 1, block_table=bt_zero))
+    r_short = oracle.decode(dataclasses.replace(p, block_table=np.ascontiguousarray(p.block_table[:, :2])))
+    assert np.array_equal(r_zero["o"], r_short["o"]) and np.array_equal(r_zero["lse"], r_short["lse"])
