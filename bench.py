@@ -1,8 +1,7 @@
 """Benchmark of the paged MLA decode hot path on one MI355X.
 
 A step is one pass of the whole path over one batch: the split-KV metadata
-call, the decode kernel and the LSE combine kernel (``--merge-in-kernel``
-merges the splits inside the decode launch instead).  The default workload is the
+call, the decode kernel and the LSE combine kernel.  The default workload is the
 memory-bound bf16 decode (batch 64, s_q 1, h_q 128, d_qk 576, d_v 512,
 seqlens ~ U{1024..8192}, 64-token pages, shuffled block table over a 1.2x
 pool), seeded and synthetic.  Inputs are resident in HBM before timing; the
@@ -110,9 +109,6 @@ def main():
     ap.add_argument("--workload", default="dense_b64_h128_L1k-8k", choices=WORKLOADS)
     ap.add_argument("--rotate", type=int, default=0, help="KV copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--merge-in-kernel", action="store_true",
-                    help="merge the splits inside the decode launch (MLA_FLAG_MERGE_IN_KERNEL) "
-                         "instead of a second launch")
     ap.add_argument("--graph", action="store_true",
                     help="capture each step's three calls once as a hipGraph and replay it "
                          "(default: launch them from the host)")
@@ -175,7 +171,7 @@ def main():
     for r in range(R):
         pr = B._params(qs[r], kvs[r], bt if idx is None else None, sl, meta, ns, p.causal, idx, p.scale,
                        p.kv_format, ws, out, lse, fused)
-        pr.flags = B.MLA_FLAG_MERGE_IN_KERNEL if args.merge_in_kernel else B.MLA_FLAG_DEFER_COMBINE
+        pr.flags = B.MLA_FLAG_DEFER_COMBINE
         params.append(pr)
     sl_p, meta_p, ns_p = ctypes.c_void_p(sl.data_ptr()), ctypes.c_void_p(meta.data_ptr()), ctypes.c_void_p(ns.data_ptr())
 
@@ -202,8 +198,7 @@ def main():
             st |= lib.mla_decode_timed(ctypes.byref(pr), sh, kev[0], kev[1])
         else:
             st |= lib.mla_decode(ctypes.byref(pr), sh)
-        if not args.merge_in_kernel:
-            st |= lib.mla_combine(ctypes.byref(pr), sh)
+        st |= lib.mla_combine(ctypes.byref(pr), sh)
         if st != 0:
             raise RuntimeError(lib.mla_last_error().decode())
 
@@ -262,8 +257,7 @@ def main():
             raise RuntimeError(lib.mla_last_error().decode())
         pr = params[(args.warmup + i) % R]
         st = lib.mla_decode_timed(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream), kevs[i][0], kevs[i][1])
-        if not args.merge_in_kernel:
-            st |= lib.mla_combine(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream))
+        st |= lib.mla_combine(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream))
         if st != 0:
             raise RuntimeError(lib.mla_last_error().decode())
     torch.cuda.synchronize()
@@ -297,7 +291,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
     src = os.path.join(ROOT, "mla_paged_kv_05_amd", "csrc", "mla_kernels.hip")
-    tr = None if args.merge_in_kernel else traffic_record(src, p.name)
+    tr = traffic_record(src, p.name)
     traffic = None if tr is None else tr["bytes_per_launch"]
     res = {
         "metric": "MLA paged decode effective HBM GB/s (algorithmic bytes) + TFLOPS, b=64 h_q=128 seq<=8K",
@@ -309,11 +303,11 @@ def main():
                    "sparse_topk": topk, "fused": bool(p.fused), "parallelism": "single GPU",
                    "kv_copies_rotated": R,
                    "launch": "eager" if graphs is None else "hipGraph per step (metadata, decode, combine)",
-                   "combine": "in the decode launch" if args.merge_in_kernel else "separate launch"},
+                   "combine": "separate launch"},
         "tflops": round(tflops, 2),
         "roofline": dict(roof, **{
             "traffic": traffic,
-            "kernel": "k_decode" + (" (with the in-kernel LSE combine)" if args.merge_in_kernel else ""),
+            "kernel": "k_decode",
             "kernel_avg_us": round(dec_avg * 1e3, 2),
             "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
             "intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),

@@ -73,7 +73,6 @@ class DecodeParams(ctypes.Structure):
 
 
 MLA_FLAG_DEFER_COMBINE = 1
-MLA_FLAG_MERGE_IN_KERNEL = 2
 
 
 EXPORTED = ["mla_num_sched_slots", "mla_sched_meta_ints", "mla_num_splits_ints", "mla_get_metadata",
@@ -149,7 +148,11 @@ def get_mla_metadata(cache_seqlens: torch.Tensor, rows_per_kv_head: int, h_kv: i
     num_splits int32 [batch+1]), both on cache_seqlens' device."""
     lib = load_library()
     dev = cache_seqlens.device
-    assert cache_seqlens.dtype == torch.int32 and cache_seqlens.is_contiguous()
+    if cache_seqlens.dim() != 1:
+        raise ValueError("cache_seqlens must be int32 [batch]")
+    _need(cache_seqlens, "cache_seqlens", torch.int32)
+    if dev.type != "cuda":
+        raise ValueError("cache_seqlens must be on a GPU")
     S = num_slots if num_slots is not None else num_sched_slots(rows_per_kv_head, dev)
     B = cache_seqlens.shape[0]
     meta = torch.empty((S, 8), dtype=torch.int32, device=dev)
@@ -163,9 +166,65 @@ def workspace_bytes(batch: int, s_q: int, h_q: int, num_slots: int) -> int:
     return int(load_library().mla_workspace_bytes(batch, s_q, h_q, num_slots))
 
 
+_TOKEN_SHAPE = {"bf16": (torch.bfloat16, D_QK), "fp8v32": (torch.uint8, 656), "fp8v41": (torch.uint8, 528)}
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    """Argument check before a pointer crosses the C ABI: the library reads
+    raw memory with the layout include/mla.h states, so a wrong dtype,
+    stride, device or shape would be read silently."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def _params(q, kvcache, block_table, cache_seqlens, sched_meta, num_splits, causal, indices,
             softmax_scale, kv_format, workspace, out, lse, fused):
+    if kv_format not in _TOKEN_SHAPE:
+        raise ValueError(f"kv_format must be one of {sorted(_TOKEN_SHAPE)}")
+    if q.dim() != 4:
+        raise ValueError(f"q must be [batch, s_q, h_q, d_qk], got {tuple(q.shape)}")
     b, s_q, h_q, d_qk = q.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, device=dev)
+    kv_dtype, tok = _TOKEN_SHAPE[kv_format]
+    _need(kvcache, "kvcache", kv_dtype, device=dev)
+    kv_tail = tuple(kvcache.shape[2:])
+    if kvcache.dim() < 3 or kvcache.shape[1] != PAGE or kv_tail not in ((tok,), (1, tok)):
+        raise ValueError(f"kvcache for {kv_format} must be [blocks, {PAGE}, {tok}] or "
+                         f"[blocks, {PAGE}, 1, {tok}], got {tuple(kvcache.shape)}")
+    if kv_format == "fp8v41" and d_qk != 512:
+        raise ValueError("the fp8v41 cache has head dim 512: q must be [b, s_q, h_q, 512]")
+    if kv_format != "fp8v41" and d_qk != D_QK:
+        raise ValueError(f"q must have {D_QK} dims per head, got {d_qk}")
+    _need(cache_seqlens, "cache_seqlens", torch.int32, (b,), dev)
+    if indices is None:
+        if block_table is None or block_table.dim() != 2 or block_table.shape[0] != b:
+            raise ValueError("dense decode needs block_table int32 [batch, max_blocks_per_seq]")
+        _need(block_table, "block_table", torch.int32, device=dev)
+    else:
+        if indices.dim() != 3 or tuple(indices.shape[:2]) != (b, s_q):
+            raise ValueError(f"indices must be int32 [batch, s_q, topk], got {tuple(indices.shape)}")
+        _need(indices, "indices", torch.int32, device=dev)
+    _need(sched_meta, "sched_meta", torch.int32, device=dev)
+    if sched_meta.dim() != 2 or sched_meta.shape[1] != 8:
+        raise ValueError(f"sched_meta must be int32 [num_slots, 8], got {tuple(sched_meta.shape)}")
+    _need(num_splits, "num_splits", torch.int32, device=dev)
+    if num_splits.numel() < int(load_library().mla_num_splits_ints(b)):
+        raise ValueError(f"num_splits holds {num_splits.numel()} ints, fewer than batch + 1")
+    _need(workspace, "workspace", torch.uint8, device=dev)
+    _need(out, "out", torch.uint8 if fused is not None else torch.bfloat16, (b, s_q, h_q, D_V), dev)
+    _need(lse, "lse", torch.float32, (b, s_q, h_q), dev)
+    if fused is not None:
+        _need(fused["norm_weight"], "norm_weight", torch.bfloat16, (D_QK,), dev)
+        _need(fused["out_scale"], "out_scale", torch.float32, (b, s_q, h_q), dev)
     p = DecodeParams()
     p.struct_size = ctypes.sizeof(DecodeParams)
     p.batch, p.s_q, p.h_q, p.h_kv, p.d_qk, p.d_v = b, s_q, h_q, 1, d_qk, D_V
@@ -247,8 +306,8 @@ def debug_gather(q, kvcache, block_table, cache_seqlens, sched_meta, num_splits,
     if workspace is None:
         workspace = torch.empty(max(workspace_bytes(bsz, s_q, h_q, sched_meta.shape[0]), 256),
                                 dtype=torch.uint8, device=dev)
-    out = torch.empty(16, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty(16, dtype=torch.float32, device=dev)
+    out = torch.empty((bsz, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)  # not written
+    lse = torch.empty((bsz, s_q, h_q), dtype=torch.float32, device=dev)
     p = _params(q, kvcache, block_table, cache_seqlens, sched_meta, num_splits, False, indices, None,
                 kv_format, workspace, out, lse, None)
     dst = torch.empty((PAGE, D_QK), dtype=torch.bfloat16, device=dev)

@@ -125,7 +125,7 @@ static mla_status build_args(const mla_decode_params* p, mla::DecodeArgs& a, boo
     return fail(MLA_ERR_INVALID_ARG, "q, kv, out, lse and cache_seqlens must be non-NULL");
   if (!aligned(p->q, 16) || !aligned(p->kv, 16) || !aligned(p->out, 16))
     return fail(MLA_ERR_INVALID_ARG, "q, kv and out must be 16-byte aligned");
-  if (p->flags & ~(MLA_FLAG_DEFER_COMBINE | MLA_FLAG_MERGE_IN_KERNEL))
+  if (p->flags & ~MLA_FLAG_DEFER_COMBINE)
     return fail(MLA_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
   if (p->num_blocks < 0) return fail(MLA_ERR_INVALID_ARG, "num_blocks=%lld", (long long)p->num_blocks);
   sparse = p->indices != nullptr;
@@ -184,8 +184,7 @@ static mla_status build_args(const mla_decode_params* p, mla::DecodeArgs& a, boo
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   a.norm_eps = p->norm_eps;
   a.rope_base = p->rope_base;
-  if (p->fused)
-    for (int i = 0; i < 32; ++i) a.rope_inv_freq[i] = std::pow((double)p->rope_base, -2.0 * i / 64.0);
+  a.rope_log2_base = std::log2((double)p->rope_base);
   return MLA_OK;
 }
 
@@ -197,24 +196,7 @@ static mla_status decode_impl(const mla_decode_params* p, void* stream, hipEvent
   if (st != MLA_OK) return st;
   if (p->batch == 0) return MLA_OK;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  // Merge the splits inside the decode launch (cooperative) when asked to,
-  // unless the caller defers the combine, the call is fused, the row groups
-  // exceed the control area, or the stream is being captured (a cooperative
-  // launch is not captured).
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
-    (void)hipGetLastError();
-    cap = hipStreamCaptureStatusActive;
-  }
-  if ((p->flags & MLA_FLAG_MERGE_IN_KERNEL) && !(p->flags & MLA_FLAG_DEFER_COMBINE) && !p->fused &&
-      a.groups <= mla::kCtlGroups && cap == hipStreamCaptureStatusNone) {
-    a.ctl = p->num_splits + p->batch + 1;
-    e = mla::launch_decode(a, p->kv_format, sparse, p->fused != 0, s, start, stop);
-    if (e == hipSuccess) return MLA_OK;
-    a.ctl = nullptr;  // cannot be cooperative here: decode, then a combine launch
-  }
-  e = mla::launch_decode(a, p->kv_format, sparse, p->fused != 0, s, start, stop);
+  hipError_t e = mla::launch_decode(a, p->kv_format, sparse, p->fused != 0, s, start, stop);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (p->flags & MLA_FLAG_DEFER_COMBINE) return MLA_OK;
   e = mla::launch_combine(a, p->fused != 0, s);

@@ -27,12 +27,8 @@ inline int sched_piece_cost(int rows) {
 // Row groups of 128 rows a decode call is cut into.
 inline int row_groups(int rows) { return (rows + kRowsPerWg - 1) / kRowsPerWg; }
 
-// The num_splits buffer: the split prefix [batch+1], then the in-kernel
-// combine's control area: tasks, claim counter, error word, the split
-// sequences [batch], and per (sequence, row group <= 2) counters of arrived
-// pieces and finished tasks [batch][2] each.
-constexpr int kCtlGroups = 2;
-inline size_t splits_ints(int batch) { return (size_t)batch + 1 + 3 + (size_t)batch * (1 + 2 * kCtlGroups); }
+// The num_splits buffer: the prefix offsets of each sequence's splits [batch+1].
+inline size_t splits_ints(int batch) { return (size_t)batch + 1; }
 
 // Partial results of one (split, row group): 128 rows x 512 fp32 in the
 // decode kernel's register order plus 128 fp32 LSEs.
@@ -47,7 +43,6 @@ struct DecodeArgs {
   const int32_t* indices;    // sparse only
   const int32_t* meta;       // [S][8]
   const int32_t* num_splits; // [batch+1] split prefix
-  int32_t* ctl;              // in-kernel combine control area (null: separate combine)
   uint16_t* part_o;          // bf16 [max_partials][G][128*512] (register order)
   float* part_lse;           // [max_partials][G][128]
   void* out;                 // bf16 or e4m3 [batch][rows][512]
@@ -58,7 +53,7 @@ struct DecodeArgs {
   int batch, s_q, h_q, rows, groups, max_blocks, topk, causal, num_slots;
   float scale_log2;          // softmax_scale * log2(e)
   float norm_eps, rope_base;
-  double rope_inv_freq[32];  // fused only: rope_base^(-2i/64), computed on the host in fp64
+  double rope_log2_base;     // fused only: log2(rope_base), in fp64
 };
 
 enum KvFormat { kKvBf16 = 0, kKvFp8V32 = 1, kKvFp8V41 = 2 };
@@ -66,9 +61,6 @@ constexpr int kFp8V41TokenBytes = 528;  // 512 e4m3 codes (all dims) + 16 e8m0 s
 
 hipError_t launch_sched(const int32_t* seqlens, int batch, int rows, int topk, int num_slots,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream);
-// With a.ctl set the decode is launched cooperatively and merges the splits
-// itself; a launch that cannot be cooperative returns an error (the caller
-// then clears a.ctl and uses launch_combine).
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool fused,
                          hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t launch_combine(const DecodeArgs& a, bool fused, hipStream_t stream);

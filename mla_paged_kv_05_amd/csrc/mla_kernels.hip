@@ -20,8 +20,9 @@
 //    second product, so P never goes through LDS.
 //  * O^T = V^T . P^T: V^T fragments come from the same LDS tile as K via
 //    ds_read_b64_tr_b16 transposed reads (V = K[:, :512], no second load).
-//  * KV blocks are staged with LDS-DMA (buffer_load ... lds, 16 B per lane)
-//    into a double-buffered, XOR-swizzled [64][576] bf16 tile.  The buffer
+//  * KV blocks are staged half a block (32 tokens) at a time with LDS-DMA
+//    (buffer_load ... lds, 16 B per lane) into a ring of padded, swizzled
+//    bf16 half tiles, two steps ahead of their use.  The buffer
 //    resource of a block covers only its valid tokens, so rows past the
 //    sequence length are written as zeros by the hardware and poisoned
 //    (NaN) tail slots are never read.
@@ -63,12 +64,11 @@ __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlan
 __device__ __forceinline__ uint64_t uni_u64(uint64_t v) {
   return ((uint64_t)(uint32_t)uni((int)(v >> 32)) << 32) | (uint32_t)uni((int)(uint32_t)v);
 }
-// Buffer accesses with cache policy sc0 sc1: they go past the CU's L1 and
-// the XCD's L2 to the coherent memory side, so a store that has completed is
-// seen by a load of this kind from any XCD without L2 write-back or
-// invalidation.  Used for the split partials the in-kernel combine reads.
+// Buffer stores with cache policy sc0 sc1 go past the CU's L1 and the XCD's
+// L2 to the memory side.  The split partials are stored this way: lines left
+// dirty in L2 would be written back while the next launch streams its KV.
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-constexpr int kCoherent = 1 | 16;
+constexpr int kPastL2 = 1 | 16;  // sc0 sc1
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -144,23 +144,37 @@ __device__ __forceinline__ int fresh_lane() {
   return opaque(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
 }
 
-// S^T = K Q^T step on v_mfma_f32_32x32x16_bf16 with the accumulator held in
+// S^T = K Q^T step on v_mfma_f32_32x32x16 with the accumulator held in
 // VGPRs.  Written as inline asm because the builtin lets the compiler move
 // every MFMA accumulator to AGPRs, and the 256 AGPRs are exactly the O
 // accumulator of a 32-row wave tile; S then overflows and spills.  The asm is
 // not volatile, so the scheduler still hoists the LDS reads feeding it.
+// F16 selects the fp16 operand form (the fused path), otherwise bf16; the
+// operands are eight 16-bit values either way.
+template <bool F16>
 __device__ __forceinline__ void mfma_s_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  if constexpr (F16) asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
 }
+template <bool F16>
 __device__ __forceinline__ void mfma_s_acc(f32x16& c, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  if constexpr (F16) asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 // O^T += V^T P^T step with the accumulator pinned to AGPRs for its whole
 // life (a builtin leaves O's register class to the allocator, which then
 // shuffles the 256 accumulators between VGPRs and AGPRs inside the loop).
 // Back-to-back accumulation into the same registers needs no wait states.
+template <bool F16>
 __device__ __forceinline__ void mfma_o(f32x16& c, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  if constexpr (F16) asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// One fp32 value as the 16-bit MFMA operand element: fp16 or bf16, RNE.
+template <bool F16>
+__device__ __forceinline__ __bf16 to_op16(float x) {
+  if constexpr (F16) return __builtin_bit_cast(__bf16, (_Float16)x);
+  else return (__bf16)x;
 }
 // VALU-written B operand -> MFMA read.
 __device__ __forceinline__ void valu_to_mfma_settle(bf16x8& p0, bf16x8& p1) {
@@ -278,8 +292,7 @@ k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
   }
   __syncthreads();
   const int T = tot_c;
-  int cap = (T + 1 + S - 1) / S;
-  if (cap < 2 * F) cap = 2 * F;
+  const int cap = (T + 1 + S - 1) / S;
   // pass 2: splits per sequence -> num_splits prefix
   int ss = 0;
   for (int b = lo; b < hi; ++b) {
@@ -298,30 +311,6 @@ k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
     s0 += (p0 + items - 1) / cap - p0 / cap + 1;
   }
   if (tid == 0) num_splits[B] = tot_s;
-  // in-kernel combine control area: the split sequences in order, zeroed
-  // counters, and the task count (4 row tiles per row group)
-  {
-    int32_t* ctl = num_splits + B + 1;
-    const int G = (rows + kRowsPerWg - 1) / kRowsPerWg;
-    auto nsplit = [&](int b) {
-      int items = U[b + 1] - U[b] - F;
-      items = items > 0 ? items : 1;
-      int p0 = U[b] + F;
-      return (p0 + items - 1) / cap - p0 / cap + 1;
-    };
-    int fc = 0;
-    for (int b = lo; b < hi; ++b) fc += nsplit(b) > 1;
-    int tot_f;
-    int f0 = block_scan_exclusive<NT>(fc, wsum, &tot_f);
-    for (int b = lo; b < hi; ++b)
-      if (nsplit(b) > 1) ctl[3 + f0++] = b;
-    for (int i = tid; i < 2 * kCtlGroups * B; i += kSchedThreads) ctl[3 + B + i] = 0;
-    if (tid == 0) {
-      ctl[0] = tot_f * (G <= kCtlGroups ? G : 0) * 16;  // 16 combine tasks per (sequence, row group)
-      ctl[1] = 0;
-      ctl[2] = 0;
-    }
-  }
   // pass 3: each slot's first and last item
   auto last_pos = [&](int b) {  // position of the last item of sequence b
     int n = U[b + 1] - U[b] - F;
@@ -379,8 +368,8 @@ k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
 // of the transposed V reads (keys b, b+4, b+8, b+12 x 4 chunks) both touch
 // 16 distinct 4-bank groups: no bank conflicts, and each read stream needs a
 // single per-lane base address plus immediates.  bf16 half tiles rotate
-// through a ring of 4 slots: two are computed on (S^T of one, P V of the
-// other) while the next two are in flight.
+// through a ring of kTileRing slots: one is computed on while the next
+// kDepth are in flight.
 // ---------------------------------------------------------------------------
 constexpr int kHalfRows = 32;
 constexpr int kMainStride = 1040;
@@ -388,7 +377,11 @@ constexpr int kRopeOff = kHalfRows * kMainStride;               // 33280
 constexpr int kRopeStride = 128;
 constexpr int kHalfBytes = kRopeOff + kHalfRows * kRopeStride;  // 37376
 constexpr int kLoadsPerHalf = kHalfRows / kWaves + 1;           // 9 per wave: 8 rows + rope
-constexpr int kTileRing = 4;  // bf16 half-tile slots
+// bf16 tiles are prefetched kDepth steps ahead into a ring of kDepth + 1
+// slots.  A CU holds ~40 KB of loads in flight before their issue blocks;
+// two steps (one half page landing, one issued) keep it there.
+constexpr int kDepth = 2;
+constexpr int kTileRing = kDepth + 1;  // bf16 half-tile slots
 constexpr int kRing = 3;      // FP8 raw slots
 
 // The key held by row m (0..31) of an S^T tile (and by k-slot m of the
@@ -433,30 +426,35 @@ __device__ __forceinline__ void load_half_bf16_dense(uint8_t* slot, const uint8_
   for (int k = 0; k < kLoadsPerHalf; ++k) load_row_bf16_dense(slot, kv, phys, valid, h, wave, k);
 }
 
-// Sparse bf16: row r is flat pool token ids[r] when r < nvalid and
-// ids[r] >= 0, else zeros.  Same 9 loads per wave as the dense loader.
-__device__ __forceinline__ void load_row_bf16_sparse(uint8_t* slot, const uint8_t* kv,
+// A sparse id names a token of the pool iff 0 <= id < ntok (= num_blocks *
+// 64); -1 and every other id outside the pool are masked.
+__device__ __forceinline__ bool id_in_pool(int id, int64_t ntok) { return id >= 0 && (int64_t)id < ntok; }
+
+// Sparse bf16: row r is flat pool token ids[r] when r < nvalid and the id
+// is in the pool, else zeros.  Same 9 loads per wave as the dense loader.
+__device__ __forceinline__ void load_row_bf16_sparse(uint8_t* slot, const uint8_t* kv, int64_t ntok,
                                                      const int32_t* ids, int nvalid, int wave, int k) {
   const int l16 = fresh_lane() << 4;
   const uint32_t base = lds_off(slot);
   if (k < kHalfRows / kWaves) {
     const int r = wave + kWaves * k;
     const int id = uni(r < nvalid ? ids[r] : -1);
-    const uint8_t* src = uni_ptr(id >= 0 ? kv + (int64_t)id * kRowBytes : g_zero_row);
+    const uint8_t* src = uni_ptr(id_in_pool(id, ntok) ? kv + (int64_t)id * kRowBytes : g_zero_row);
     dma_glb16_s(base + r * kMainStride, l16, src);
   } else {
     const int rr = 8 * wave + (l16 >> 7);
     const int id = rr < nvalid ? ids[rr] : -1;
     const int cc = rope_phys_chunk(rr, (l16 >> 4) & 7);
-    const uint8_t* g = id >= 0 ? kv + (int64_t)id * kRowBytes + 1024 + cc * 16 : g_zero_row + 1024 + cc * 16;
+    const uint8_t* g = id_in_pool(id, ntok) ? kv + (int64_t)id * kRowBytes + 1024 + cc * 16
+                                            : g_zero_row + 1024 + cc * 16;
     dma_glb16(base + kRopeOff + wave * 1024, g);
   }
 }
-__device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8_t* kv,
+__device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8_t* kv, int64_t ntok,
                                                       const int32_t* ids, int nvalid, int wave,
                                                       int /*lane*/) {
 #pragma unroll
-  for (int k = 0; k < kLoadsPerHalf; ++k) load_row_bf16_sparse(slot, kv, ids, nvalid, wave, k);
+  for (int k = 0; k < kLoadsPerHalf; ++k) load_row_bf16_sparse(slot, kv, ntok, ids, nvalid, wave, k);
 }
 
 // FP8 V3.2 records of one half (32 x 656 B = 1312 chunks) are staged raw by
@@ -490,7 +488,7 @@ __device__ __forceinline__ void load_half_fp8_dense(uint8_t* raw, const uint8_t*
 }
 
 template <int KVF = kKvFp8V32>
-__device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t* kv,
+__device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t* kv, int64_t ntok,
                                                      const int32_t* ids, int nvalid, int wave,
                                                      int lane) {
   constexpr int kTok = tok_bytes<KVF>(), kChunks = kTok / 16, kHalfChunks = kHalfRows * kChunks;
@@ -503,7 +501,7 @@ __device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t
     const int c = pos_all - r * kChunks;
     const int id = (pos_all < kHalfChunks && r < nvalid) ? ids[r] : -1;
     const uint8_t* g =
-        id >= 0 ? kv + (int64_t)id * kTok + c * 16 : g_zero_row + (pos_all & 63) * 16;
+        id_in_pool(id, ntok) ? kv + (int64_t)id * kTok + c * 16 : g_zero_row + (pos_all & 63) * 16;
     dma_glb16(lds_off(raw) + i * 1024, g);
   }
 }
@@ -517,12 +515,19 @@ __device__ __forceinline__ int scale_slot(int key) {  // key -> h*16 + i
   return h * 16 + 8 * (kc >> 4) + 4 * ((rem >> 1) & 1) + (rem >> 2);
 }
 
-// 32 raw records -> the bf16 half tile with the e4m3 codes of dims < 512
-// converted exactly (every e4m3 value is a bf16 value), dims 512..575
-// copied, and the fp32 tile scales moved to `scl`.  The decode applies the
-// scales in fp32: to each tile's partial scores in QK^T and to P in P.V, so
-// no product code*scale is ever rounded to bf16.  An all-zero record gives a
-// zero row with zero scales.
+// 32 raw records -> the half tile with the e4m3 codes of dims < 512
+// converted exactly (every e4m3 value is a bf16 value and an fp16 value),
+// dims 512..575 copied (bf16) or converted to fp16 (F16, the fused path),
+// and the fp32 tile scales moved to `scl`.  The decode applies the scales in
+// fp32: to each tile's partial scores in QK^T and to P in P.V, so no product
+// code*scale is ever rounded to 16 bits.  An all-zero record gives a zero row
+// with zero scales.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+template <bool F16>
 __device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const uint8_t* raw, int tid) {
   tid = (tid & ~63) | fresh_lane();  // keep the per-thread addresses out of the loop's live set
   // All code reads first, then the conversions and writes: the compiler
@@ -535,7 +540,7 @@ __device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const u
     const int k = kk * kThreads + tid;
     codes[kk] = *reinterpret_cast<const uint2*>(raw + (k >> 6) * kFp8TokenBytes + (k & 63) * 8);
   }
-  const uint4 rope = *reinterpret_cast<const uint4*>(raw + (tid >> 3) * kFp8TokenBytes + 528 + (tid & 7) * 16);
+  uint4 rope = *reinterpret_cast<const uint4*>(raw + (tid >> 3) * kFp8TokenBytes + 528 + (tid & 7) * 16);
 #pragma unroll
   for (int kk = 0; kk < kPer; ++kk) {
     const int k = kk * kThreads + tid;
@@ -545,19 +550,56 @@ __device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const u
     uint32_t w[4];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      // two codes -> two bf16 in one instruction; with scale 1 the result is exact
-      w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], 1.0f, false));
-      w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], 1.0f, true));
+      // two codes -> two 16-bit values in one instruction; with scale 1 exact
+      if constexpr (F16) {
+        w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[hh], 1.0f, false));
+        w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[hh], 1.0f, true));
+      } else {
+        w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], 1.0f, false));
+        w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], 1.0f, true));
+      }
     }
     *reinterpret_cast<uint4*>(tile + r * kMainStride + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
   {
     const int r = tid >> 3, c = tid & 7;
+    if constexpr (F16)
+      rope = make_uint4(bf16x2_to_f16x2(rope.x), bf16x2_to_f16x2(rope.y), bf16x2_to_f16x2(rope.z),
+                        bf16x2_to_f16x2(rope.w));
     *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = rope;
   }
   if (tid < 4 * kHalfRows) {
     const int r = tid >> 2, t = tid & 3;
     scl[t * 32 + scale_slot(r)] = *reinterpret_cast<const float*>(raw + r * kFp8TokenBytes + 512 + 4 * t);
+  }
+}
+
+// A staged bf16 half tile (main and RoPE parts) converted in place to fp16,
+// for the fused path's fp16 products.  Exact for |x| in fp16's normal range
+// [2^-14, 65504]; smaller magnitudes keep 2^-24 absolute resolution.  Each
+// thread converts every 256th 16-byte chunk of the tile (pad included), in
+// two batches whose reads all go out before their writes.
+__device__ __forceinline__ void tile_to_f16(uint8_t* tile, int tid) {
+  tid = (tid & ~63) | fresh_lane();
+  constexpr int kChunks = kHalfBytes / 16;                       // 2336
+  constexpr int kPer = (kChunks + kThreads - 1) / kThreads;      // 10, the last partly
+  constexpr int kBatch = kPer / 2;
+  static_assert(kPer == 2 * kBatch, "two equal batches");
+#pragma unroll
+  for (int bt = 0; bt < 2; ++bt) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = (bt * kBatch + i) * kThreads + tid;
+      if (c < kChunks) v[i] = *reinterpret_cast<const uint4*>(tile + c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = (bt * kBatch + i) * kThreads + tid;
+      if (c < kChunks)
+        *reinterpret_cast<uint4*>(tile + c * 16) =
+            make_uint4(bf16x2_to_f16x2(v[i].x), bf16x2_to_f16x2(v[i].y), bf16x2_to_f16x2(v[i].z), bf16x2_to_f16x2(v[i].w));
+    }
   }
 }
 
@@ -702,17 +744,19 @@ struct RopeRow {
   double pos;
   float c, s;
 };
-__device__ __forceinline__ RopeRow rope_row(double pos, bool row_ok, const double* inv_freq, float sign) {
+// Inverse frequency of pair i: base^(-2i/64) = 2^(-(i/32) log2(base)), in fp64.
+__device__ __forceinline__ double rope_inv_freq(int i, double log2_base) { return exp2(-(double)i / 32.0 * log2_base); }
+__device__ __forceinline__ RopeRow rope_row(double pos, bool row_ok, double log2_base, float sign) {
   RopeRow r;
   const double pos0 = __builtin_bit_cast(double, uni_u64(__builtin_bit_cast(uint64_t, pos)));
   r.shared = __builtin_amdgcn_ballot_w64(row_ok && pos != pos0) == 0;
   r.pos = pos;
   r.c = 0.f;
   r.s = 0.f;
-  if (r.shared) rope_cs(pos0, inv_freq[fresh_lane() & 31], sign, r.c, r.s);
+  if (r.shared) rope_cs(pos0, rope_inv_freq(fresh_lane() & 31, log2_base), sign, r.c, r.s);
   return r;
 }
-__device__ __forceinline__ void rope_pair(const RopeRow& r, const double* inv_freq, float sign, int i0, int i1,
+__device__ __forceinline__ void rope_pair(const RopeRow& r, double log2_base, float sign, int i0, int i1,
                                           bool hi, float& c, float& s) {
   if (r.shared) {
     const float c0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r.c), i0));
@@ -722,7 +766,7 @@ __device__ __forceinline__ void rope_pair(const RopeRow& r, const double* inv_fr
     c = hi ? c1 : c0;
     s = hi ? s1 : s0;
   } else {
-    rope_cs(r.pos, hi ? inv_freq[i1] : inv_freq[i0], sign, c, s);
+    rope_cs(r.pos, rope_inv_freq(hi ? i1 : i0, log2_base), sign, c, s);
   }
 }
 
@@ -730,7 +774,7 @@ __device__ __forceinline__ void rope_pair(const RopeRow& r, const double* inv_fr
 // Decode kernel
 //
 // Query fragments.  bf16 KV: all 36 k-steps stay in VGPRs (144), which
-// leaves the LDS to the four-slot tile ring.  FP8 KV, whose dequantisation
+// leaves the LDS to the tile ring.  FP8 KV, whose dequantisation
 // and per-tile scaling need more registers: dims 0..383 (k-steps 0..23) in
 // VGPRs, dims 384..575 (k-steps 24..35) in a per-wave LDS region
 // [32 rows][24 chunks] swizzled like the KV tile.
@@ -740,25 +784,31 @@ template <int KVF>
 constexpr int ksteps() { return KVF == kKvFp8V41 ? 32 : 36; }
 template <int KVF>
 constexpr int dqk_of() { return 16 * ksteps<KVF>(); }
+// FP8 KV and the fused bf16 path (whose prologue and epilogue need the
+// registers) keep k-steps 24..35 of the query in LDS.
+template <int KVF, bool FUSED>
+constexpr int q_reg_steps() { return KVF == kKvFp8V32 || (KVF == kKvBf16 && FUSED) ? 24 : ksteps<KVF>(); }
+template <int KVF, bool FUSED>
+constexpr int q_lds_row_bytes() { return (ksteps<KVF>() - q_reg_steps<KVF, FUSED>()) * 2 * 16; }  // 384 or 0
+template <int KVF, bool FUSED>
+constexpr int q_lds_wave_bytes() { return 32 * q_lds_row_bytes<KVF, FUSED>(); }                 // 12288 or 0
+constexpr int kQRegStepsFp8 = q_reg_steps<kKvFp8V32, false>();
+// Sparse id slots: ids are fetched 4 steps ahead (5 for V4.1 records), and
+// a slot is rewritten only after the step that last read it.
 template <int KVF>
-constexpr int q_reg_steps() { return KVF == kKvFp8V32 ? 24 : ksteps<KVF>(); }
-template <int KVF>
-constexpr int q_lds_row_bytes() { return (ksteps<KVF>() - q_reg_steps<KVF>()) * 2 * 16; }    // fp8: 384
-template <int KVF>
-constexpr int q_lds_wave_bytes() { return 32 * q_lds_row_bytes<KVF>(); }          // fp8: 12288
-constexpr int kQRegStepsFp8 = q_reg_steps<kKvFp8V32>();
-constexpr int kIdsSlots = 6;
+constexpr int ids_slots() { return KVF == kKvFp8V41 ? 6 : 5; }
 
-template <int KVF, bool SPARSE>
+template <int KVF, bool SPARSE, bool FUSED>
 struct DecodeLayout {
   static constexpr int kTileOff = 0;                                   // bf16 half tiles
   static constexpr int kTiles = KVF == kKvBf16 ? kTileRing : KVF == kKvFp8V41 ? 2 : 1;
   static constexpr int kRawOff = kTiles * kHalfBytes;                  // fp8 raw slots
   static constexpr int kQOff = kRawOff + (KVF == kKvBf16 ? 0 : kRing * kRawSlotBytes);
-  static constexpr int kIdsOff = kQOff + kWaves * q_lds_wave_bytes<KVF>();
-  static constexpr int kWalkOff = kIdsOff + (SPARSE ? kIdsSlots * 256 : 0);  // 2 words per wave
+  static constexpr int kIdsOff = kQOff + kWaves * q_lds_wave_bytes<KVF, FUSED>();
+  static constexpr int kWalkOff = kIdsOff + (SPARSE ? ids_slots<KVF>() * 256 : 0);  // 2 words per wave
   static constexpr int kSclOff = kWalkOff + (KVF == kKvBf16 && !SPARSE ? kWaves * 8 : 0);
-  static constexpr int kSmem = kSclOff + (KVF == kKvFp8V32 ? kScaleBytes : 0);
+  static constexpr int kWOff = kSclOff + (KVF == kKvFp8V32 ? kScaleBytes : 0);  // fused: norm weight row
+  static constexpr int kSmem = kWOff + (FUSED ? kDqk * 2 : 0);
   // per-step VMEM instructions issued by every wave (loads + id fetch)
   static constexpr int kVmPerStep =
       (KVF == kKvBf16 ? kLoadsPerHalf : raw_loads_per_wave<KVF>()) + (SPARSE ? 1 : 0);
@@ -777,13 +827,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <bool FUSED>
-__device__ void combine_phase(const DecodeArgs& a, uint8_t* lds);
-
 template <int KVF, bool SPARSE, bool FUSED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_decode(DecodeArgs a) {
-  using Lay = DecodeLayout<KVF, SPARSE>;
+  using Lay = DecodeLayout<KVF, SPARSE, FUSED>;
+  constexpr bool kF16 = FUSED;  // the fused path runs both products in fp16
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Lay::kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
@@ -810,11 +858,12 @@ k_decode(DecodeArgs a) {
   }
   const int32_t* ms = a.meta + 8 * slot;
   const int b0 = uni(sload(ms, 0));
-  if (b0 < 0) {  // no decode work: only combine tasks
-    if constexpr (!FUSED) {
-      if (a.ctl) combine_phase<FUSED>(a, smem);
-    }
-    return;
+  if (b0 < 0) return;  // no work in this slot
+  // Fused: the norm weight row goes to LDS once; every piece's prologue reads it there.
+  if constexpr (FUSED) {
+    if (tid < kDqk / 8)
+      *reinterpret_cast<uint4*>(smem + Lay::kWOff + tid * 16) = reinterpret_cast<const uint4*>(a.norm_w)[tid];
+    __syncthreads();
   }
   const int j0 = uni(sload(ms, 1)), b1 = uni(sload(ms, 2)), j1 = uni(sload(ms, 3)),
             nitems = uni(sload(ms, 5));
@@ -837,7 +886,7 @@ k_decode(DecodeArgs a) {
     b = uni(b); j = uni(j);
   };
   auto ids_slot = [&](int step) {
-    return reinterpret_cast<int32_t*>(smem + Lay::kIdsOff) + (step % kIdsSlots) * 64;
+    return reinterpret_cast<int32_t*>(smem + Lay::kIdsOff) + (step % ids_slots<KVF>()) * 64;
   };
   auto fetch_ids = [&](int b, int j, int h, int step) {
     if constexpr (SPARSE)
@@ -854,6 +903,11 @@ k_decode(DecodeArgs a) {
   // compiler wait on them, or on a spill of their register, also waits for
   // the KV loads it cannot see) would do.  The FP8 path, whose waits keep a
   // step of KV loads in flight, uses scalar loads when it needs the values.
+  // Indices are not trusted to stay inside the pool: a block_table entry
+  // outside [0, num_blocks) stages a zero page, a sparse id outside
+  // [0, num_blocks * 64) is masked like -1.  Nothing is read past the pool.
+  const int64_t ntok = a.num_blocks * kPage;
+  auto page_in_pool = [&](int64_t phys) { return phys >= 0 && phys < a.num_blocks; };
   constexpr bool kVecWalk = KVF == kKvBf16 && !SPARSE;
   int lb = b0, lj = j0, lh = 0;
   int lL = SPARSE ? 0 : uni(sload(a.seqlens, b0));
@@ -866,13 +920,15 @@ k_decode(DecodeArgs a) {
   auto fetch_word = [&](int w, const i32x4& rs, int byte_off) {
     if (lane == 0) dma_buf4(lds_off(walk + w), byte_off, rs);
   };
+  // lphys = -1 when the item has no block_table entry (past the sequence,
+  // or positions beyond max_blocks_per_seq pages): its page stages zeros.
   auto fetch_phys = [&]() {
-    const bool any = lb <= b1 && lj * kPage < lL;
+    const bool any = lb <= b1 && lj * kPage < lL && lj < a.max_blocks;
     if constexpr (kVecWalk) {
       lany = any;
       if (any) fetch_word(0, bt_rs, (lb * a.max_blocks + lj) * 4);
     } else if constexpr (!SPARSE) {
-      lphys = any ? uni(sload(a.block_table, (int64_t)lb * a.max_blocks + lj)) : 0;
+      lphys = any ? uni(sload(a.block_table, (int64_t)lb * a.max_blocks + lj)) : -1;
     }
   };
   auto fetch_next_len = [&]() {
@@ -880,7 +936,7 @@ k_decode(DecodeArgs a) {
   };
   auto land = [&]() {
     if constexpr (kVecWalk) {
-      lphys = lany ? uni(walk[0]) : 0;
+      lphys = lany ? uni(walk[0]) : -1;
       lnL = uni(walk[1]);
     }
   };
@@ -916,29 +972,30 @@ k_decode(DecodeArgs a) {
   auto issue_load = [&](int step) {
     const int rs = step % (KVF == kKvBf16 ? kTileRing : kRing);
     if constexpr (!SPARSE) {
-      const bool any = lj * kPage < lL;
+      const bool any = lj * kPage < lL && page_in_pool(lphys);
       const int valid = any ? min(kPage, lL - lj * kPage) : 0;
+      const int64_t phys = any ? lphys : 0;
       if constexpr (KVF == kKvBf16)
-        load_half_bf16_dense(smem + Lay::kTileOff + rs * kHalfBytes, a.kv, lphys, valid, lh, wave, lane);
+        load_half_bf16_dense(smem + Lay::kTileOff + rs * kHalfBytes, a.kv, phys, valid, lh, wave, lane);
       else
-        load_half_fp8_dense(smem + Lay::kRawOff + rs * kRawSlotBytes, a.kv, lphys, valid, lh, wave, lane);
+        load_half_fp8_dense(smem + Lay::kRawOff + rs * kRawSlotBytes, a.kv, phys, valid, lh, wave, lane);
     } else {
       const int nvalid = min(kHalfRows, a.topk - lj * kPage - lh * kHalfRows);
       if constexpr (KVF == kKvBf16)
-        load_half_bf16_sparse(smem + Lay::kTileOff + rs * kHalfBytes, a.kv, ids_slot(step), nvalid,
+        load_half_bf16_sparse(smem + Lay::kTileOff + rs * kHalfBytes, a.kv, ntok, ids_slot(step), nvalid,
                               wave, lane);
       else
-        load_half_fp8_sparse<KVF>(smem + Lay::kRawOff + rs * kRawSlotBytes, a.kv, ids_slot(step), nvalid,
-                             wave, lane);
+        load_half_fp8_sparse<KVF>(smem + Lay::kRawOff + rs * kRawSlotBytes, a.kv, ntok, ids_slot(step),
+                                  nvalid, wave, lane);
     }
   };
 
-  // bf16 path: the loads of step+3 are captured by prepare_load() at the
-  // start of step `step` and issued by emit_load(k), k < kLoadsPerHalf, after
-  // the walker's and the ids' word loads of that step.  Past the slot's last
-  // step the same instructions stage zeros into the free slot, so every step
-  // issues exactly kLoadsPerHalf tile loads, last.  (Spreading the nine instructions between the MFMAs was
-  // measured: no gain, the address unit's queue blocks the wave either way.)
+  // bf16 path: the loads of step+kDepth are captured by prepare_load() at
+  // the start of step `step` and issued by emit_load(k), k < kLoadsPerHalf,
+  // after the walker's and the ids' word loads of that step.  Past the
+  // slot's last step the same instructions stage zeros into the free slot,
+  // so every step issues exactly kLoadsPerHalf tile loads, last.  (Issuing
+  // the nine loads between the MFMAs, or after S^T, was measured: no gain.)
   int pl_step = 0, pl_valid = 0, pl_h = 0, pl_nvalid = 0;
   int64_t pl_phys = 0;
   auto prepare_load = [&](int st) {
@@ -946,7 +1003,7 @@ k_decode(DecodeArgs a) {
     pl_step = st;
     pl_h = lh;
     if constexpr (!SPARSE) {
-      const bool any = do_load && lj * kPage < lL;
+      const bool any = do_load && lj * kPage < lL && page_in_pool(lphys);
       pl_valid = any ? min(kPage, lL - lj * kPage) : 0;
       pl_phys = any ? lphys : 0;
     } else {
@@ -957,7 +1014,7 @@ k_decode(DecodeArgs a) {
   auto emit_load = [&](int k) {
     uint8_t* slot = smem + Lay::kTileOff + (pl_step % kTileRing) * kHalfBytes;
     if constexpr (!SPARSE) load_row_bf16_dense(slot, a.kv, pl_phys, pl_valid, pl_h, wave, k);
-    else load_row_bf16_sparse(slot, a.kv, ids_slot(pl_step), pl_nvalid, wave, k);
+    else load_row_bf16_sparse(slot, a.kv, ntok, ids_slot(pl_step), pl_nvalid, wave, k);
   };
 
   // loads of step+2 and (sparse) ids of step+4, issued at step `step`
@@ -997,15 +1054,15 @@ k_decode(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
   }
   auto issue_first_loads = [&]() {
-    for (int s = 0; s < min(KVF == kKvFp8V41 ? 3 : 2, nsteps); ++s) {
+    for (int s = 0; s < min(KVF == kKvFp8V41 ? 3 : KVF == kKvBf16 ? kDepth : 2, nsteps); ++s) {
       issue_load(s);
       advance_load();
     }
   };
   if constexpr (KVF != kKvBf16) issue_first_loads();
 
-  constexpr int kQR = q_reg_steps<KVF>();
-  uint8_t* qlds = smem + Lay::kQOff + wave * q_lds_wave_bytes<KVF>();
+  constexpr int kQR = q_reg_steps<KVF, FUSED>();
+  uint8_t* qlds = smem + Lay::kQOff + wave * q_lds_wave_bytes<KVF, FUSED>();
   // FP8: Q rows are 384 B apart (an 8-group shift): chunk c of row r at
   // c ^ ((r >> 1) & 7) puts the 16 rows of a read phase on distinct groups
   const int x = (r32 >> 1) & 7;
@@ -1037,10 +1094,9 @@ k_decode(DecodeArgs a) {
     // row factor commutes with it).  The fragments hold bf16(RoPE(q (.) w))
     // chunk by chunk and inv joins the row's softmax scale, applied to S in
     // fp32; no chunk has to wait for the whole row's statistic.
-    float srow = a.scale_log2;  // log2(e) * softmax scale (* inv when fused)
+    const float srow = a.scale_log2;  // log2(e) * softmax scale (the fused q-hat carries its RMSNorm factor)
     {
       const uint16_t* qrow = a.q + ((int64_t)cb * a.rows + (row_ok ? row : 0)) * dqk_of<KVF>();
-      float ss = 0.f;
       const double pos = (double)Lb - (double)a.s_q + (double)tok;
       // chunk ks (dims 16ks + 8half .. +7): q-hat chunk, then its home
       auto put_q = [&](int ks, bf16x8 v) {
@@ -1049,58 +1105,64 @@ k_decode(DecodeArgs a) {
           qf[ks] = v;
         } else {
           const int cq = 2 * (ks - kQR) + half;
-          *reinterpret_cast<bf16x8*>(qlds + r32 * q_lds_row_bytes<KVF>() + ((cq ^ x) << 4)) = v;
+          *reinterpret_cast<bf16x8*>(qlds + r32 * q_lds_row_bytes<KVF, FUSED>() + ((cq ^ x) << 4)) = v;
         }
       };
       if constexpr (!FUSED) {
 #pragma unroll
         for (int ks = 0; ks < ksteps<KVF>(); ++ks) put_q(ks, *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8));
       } else {
-        // Six batches of 6 chunks (the RoPE chunks 32..35 first), each
-        // batch's q and weight loads issued together: all 72 in flight at
-        // once would not fit in the registers beside the fragments.
-        constexpr int kBatch = 6;
-        const RopeRow rr = rope_row(pos, row_ok, a.rope_inv_freq, 1.0f);
+        // Fused prologue: q-hat = inv * RoPE(q (.) w), inv = 1/sqrt(mean(q^2)
+        // + eps) over the row's 576 dims (RMSNorm, then RoPE on dims
+        // 512..575 at position len - s_q + t; RoPE is linear, so the row
+        // factor may come first), rounded once to fp16 for the fp16 products.
+        // Pass 1 loads the row (all 36 chunks in flight at once, into the
+        // fragments' own registers) and its sum of squares; pass 2 forms
+        // q-hat chunk by chunk with the weight row staged in LDS.
+        constexpr int kQT = ksteps<KVF>() - kQR;  // chunks held in LDS
+        bf16x8 tq[kQT > 0 ? kQT : 1];
 #pragma unroll
-        for (int bt = 0; bt < 36 / kBatch; ++bt) {
-          bf16x8 vb[kBatch], wb[kBatch];
+        for (int ks = 0; ks < ksteps<KVF>(); ++ks) {
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
+          if (ks < kQR) qf[ks] = v;
+          else tq[ks - kQR] = v;
+        }
+        float ss = 0.f;
 #pragma unroll
-          for (int i = 0; i < kBatch; ++i) {
-            const int n = bt * kBatch + i, ks = n < 4 ? 32 + n : n - 4;
-            vb[i] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
-            wb[i] = *reinterpret_cast<const bf16x8*>(a.norm_w + (2 * ks + half) * 8);
-          }
+        for (int ks = 0; ks < ksteps<KVF>(); ++ks) {
+          const bf16x8 v = ks < kQR ? qf[ks < kQR ? ks : 0] : tq[ks < kQR ? 0 : ks - kQR];
 #pragma unroll
-          for (int i = 0; i < kBatch; ++i) {
-            const int n = bt * kBatch + i, ks = n < 4 ? 32 + n : n - 4;
-            float y[8];
+          for (int e = 0; e < 8; ++e) ss += (float)v[e] * (float)v[e];
+        }
+        ss = row_sum2(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
+        const RopeRow rr = rope_row(pos, row_ok, a.rope_log2_base, 1.0f);
+        const uint16_t* wl = reinterpret_cast<const uint16_t*>(smem + Lay::kWOff);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float qv = (float)vb[i][e];
-              ss += qv * qv;
-              y[e] = qv * (float)wb[i][e];
+        for (int ks = 0; ks < ksteps<KVF>(); ++ks) {
+          const bf16x8 v = ks < kQR ? qf[ks < kQR ? ks : 0] : tq[ks < kQR ? 0 : ks - kQR];
+          const bf16x8 wv = *reinterpret_cast<const bf16x8*>(wl + (2 * ks + half) * 8);
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = (float)v[e] * (float)wv[e] * inv;
+          if (ks >= 32) {
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+              float cs, sn;
+              rope_pair(rr, a.rope_log2_base, 1.0f, 8 * (ks - 32) + pp, 8 * (ks - 32) + 4 + pp, half, cs, sn);
+              const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
+              y[2 * pp] = x0 * cs - x1 * sn;
+              y[2 * pp + 1] = x0 * sn + x1 * cs;
             }
-            if (ks >= 32) {
-#pragma unroll
-              for (int pp = 0; pp < 4; ++pp) {
-                float cs, sn;
-                rope_pair(rr, a.rope_inv_freq, 1.0f, 8 * (ks - 32) + pp, 8 * (ks - 32) + 4 + pp, half, cs, sn);
-                const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
-                y[2 * pp] = x0 * cs - x1 * sn;
-                y[2 * pp + 1] = x0 * sn + x1 * cs;
-              }
-            }
-            bf16x8 v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (__bf16)y[e];
-            put_q(ks, v);
           }
+          bf16x8 h;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = to_op16<true>(y[e]);
+          put_q(ks, h);
+          // one chunk at a time: hoisting all 36 weight reads would take
+          // 144 more VGPRs beside the fragments
           __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      if constexpr (FUSED) {
-        ss = row_sum2(ss);
-        srow *= 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
       }
     }
     if constexpr (KVF == kKvBf16) {
@@ -1108,15 +1170,6 @@ k_decode(DecodeArgs a) {
     }
     wait_vmcnt<0>();
     lds_barrier();  // every wave's loads of the piece's first step (and Q in LDS) landed
-    if constexpr (KVF == kKvBf16) {
-      if (first_piece) {
-        // step 2: the drain above landed the walker's block of its item
-        land();
-        prepare_load(2);
-#pragma unroll
-        for (int k = 0; k < kLoadsPerHalf; ++k) emit_load(k);
-      }
-    }
     first_piece = false;
 
     // ======== building blocks of one 32-key step
@@ -1141,16 +1194,27 @@ k_decode(DecodeArgs a) {
         return *reinterpret_cast<const bf16x8*>(smem + kroff + ((((2 * (ks - 32)) | lh) ^ lfr) << 4));
       };
       constexpr int kKS = ksteps<KVF>();
-      bf16x8 kbuf[kLa];
+      // query k-steps kQR.. sit in the wave's LDS rows (384 B, chunk c of row
+      // r at c ^ ((r >> 1) & 7)), read kLa MFMAs ahead like K
+      const int lx = (lr >> 1) & 7;
+      const int qrow0 = Lay::kQOff + wave * q_lds_wave_bytes<KVF, FUSED>() + lr * q_lds_row_bytes<KVF, FUSED>();
+      auto read_q = [&](int ks) {
+        const int j = ks - kQR;
+        return *reinterpret_cast<const bf16x8*>(smem + qrow0 + ((j >> 2) << 7) + ((((2 * (j & 3)) | lh) ^ lx) << 4));
+      };
+      bf16x8 kbuf[kLa], qbuf[kLa];
 #pragma unroll
       for (int i = 0; i < kLa; ++i) kbuf[i] = read_k(i);
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
         const bf16x8 ka = kbuf[ks % kLa];
-        const bf16x8 qb = qf[ks < kQR ? ks : 0];
-        if (ks + kLa < kKS) kbuf[ks % kLa] = read_k(ks + kLa);
-        if (ks == 0) mfma_s_first(sc, ka, qb);
-        else mfma_s_acc(sc, ka, qb);
+        const bf16x8 qb = ks < kQR ? qf[ks < kQR ? ks : 0] : qbuf[ks % kLa];
+        if (ks + kLa < kKS) {
+          kbuf[ks % kLa] = read_k(ks + kLa);
+          if (ks + kLa >= kQR) qbuf[ks % kLa] = read_q(ks + kLa);
+        }
+        if (ks == 0) mfma_s_first<kF16>(sc, ka, qb);
+        else mfma_s_acc<kF16>(sc, ka, qb);
         hook(ks);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1180,7 +1244,7 @@ k_decode(DecodeArgs a) {
       for (int i = 0; i < 32; ++i) {
         const bf16x8 va = vbuf[i % kVa];
         if (i + kVa < 32) vbuf[i % kVa] = read_v(i + kVa);
-        mfma_o(o[i & 15], va, pf[i >> 4]);
+        mfma_o<kF16>(o[i & 15], va, pf[i >> 4]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -1194,7 +1258,7 @@ k_decode(DecodeArgs a) {
       const int lkey = key_of_row(lr), lfr = (lkey >> 1) & 7, lx = (lr >> 1) & 7;
       const int koff = tb + lkey * kMainStride + 16 * lh;
       const int kroff = tb + kRopeOff + lkey * kRopeStride;
-      const int qb = Lay::kQOff + wave * q_lds_wave_bytes<KVF>() + lr * q_lds_row_bytes<KVF>();
+      const int qb = Lay::kQOff + wave * q_lds_wave_bytes<KVF, FUSED>() + lr * q_lds_row_bytes<KVF, FUSED>();
       int qoff[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) qoff[e] = qb + ((((2 * e) | lh) ^ lx) << 4);
@@ -1232,8 +1296,8 @@ k_decode(DecodeArgs a) {
           if (ks + kLa >= kQRegStepsFp8) qbuf[ks % kLa] = read_q(ks + kLa);
         }
         const int t = ks >> 3, u = ks & 7;
-        if (u == 0) mfma_s_first(part[t & 1], ka, qb);
-        else mfma_s_acc(part[t & 1], ka, qb);
+        if (u == 0) mfma_s_first<kF16>(part[t & 1], ka, qb);
+        else mfma_s_acc<kF16>(part[t & 1], ka, qb);
         if (t >= 1) {
           const int tp = t - 1;
           if (u == 0) {
@@ -1275,7 +1339,7 @@ k_decode(DecodeArgs a) {
       // that half by tile t-1), settled after MFMA 7.
       auto scale_p = [&](bf16x8 (&dst)[2], int q, const f32x4& s4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[q >> 1][4 * (q & 1) + e] = (__bf16)(p[4 * q + e] * s4[e]);
+        for (int e = 0; e < 4; ++e) dst[q >> 1][4 * (q & 1) + e] = to_op16<kF16>(p[4 * q + e] * s4[e]);
       };
       auto v_index = [](int i) { return ((i & 7) >> 2) * 16 + 4 * (i >> 3) + (i & 3); };  // kq * 16 + mt
       bf16x8 pt[2][2];
@@ -1292,7 +1356,7 @@ k_decode(DecodeArgs a) {
         const int t = i >> 3, j = i & 7;
         const bf16x8 va = vbuf[i % kVa];
         if (i + kVa < 32) vbuf[i % kVa] = read_v(v_index(i + kVa));
-        mfma_o(o[4 * t + (j & 3)], va, pt[t & 1][j >> 2]);
+        mfma_o<kF16>(o[4 * t + (j & 3)], va, pt[t & 1][j >> 2]);
         if (t + 1 < 4) {
           if (j == 0) {
 #pragma unroll
@@ -1311,8 +1375,8 @@ k_decode(DecodeArgs a) {
       const int k0 = key0_of(ps);
       return SPARSE ? (k0 < a.topk) : (k0 < Lb);
     };
-    // Online softmax of one tile (log2 domain) in kSmSlices slices, so that
-    // it can be spread between the MFMAs of the next tile's S^T.  Register i
+    // Online softmax of one tile (log2 domain), written as kSmSlices slices
+    // run in order.  Register i
     // of the S^T accumulator holds key key0 + key_of_row(8*(i/4) + i%4) + half.
     //   0..3  scale, mask, max of registers 4k..4k+3
     //   4     row max over the lane pair
@@ -1335,7 +1399,8 @@ k_decode(DecodeArgs a) {
           if (k == 0) {
             const int ln = fresh_lane(), r = ln & 31;
             const int nvalid = min(kHalfRows, a.topk - key0);
-            const uint64_t bm = __builtin_amdgcn_ballot_w64(ln < 32 && r < nvalid && ids_slot(st_step)[r] >= 0);
+            const uint64_t bm =
+                __builtin_amdgcn_ballot_w64(ln < 32 && r < nvalid && id_in_pool(ids_slot(st_step)[r], ntok));
             st.vmask = row_ok ? (uint32_t)bm >> half : 0u;
           }
 #pragma unroll
@@ -1372,7 +1437,7 @@ k_decode(DecodeArgs a) {
         for (int i = 4 * (k - 6); i < 4 * (k - 6) + 4; ++i) {
           const float p = __builtin_amdgcn_exp2f(sc[i] - st.mref);
           st.psum += p;
-          st.pf[i >> 3][i & 7] = (__bf16)p;
+          st.pf[i >> 3][i & 7] = to_op16<kF16>(p);
           if constexpr (KVF != kKvBf16) sc[i] = p;
         }
       } else {
@@ -1380,8 +1445,6 @@ k_decode(DecodeArgs a) {
       }
     };
     constexpr int kSmSlices = 11;
-    // k-step of the next tile's S^T after whose MFMA slice k runs
-    auto slice_at = [](int k) { return k < 6 ? 2 * k : 12 + 3 * (k - 6); };
     // Rare: the running max moved by more than the threshold; scale O.
     // Rare: some row's running max moved by more than the threshold while O
     // already held keys; scale O by alpha.  The branch ends with a full vmcnt
@@ -1403,46 +1466,35 @@ k_decode(DecodeArgs a) {
     };
 
     if constexpr (KVF == kKvBf16) {
-      // ---- bf16: step ps computes S^T of tile ps+1 with the softmax of tile
-      // ps woven between its MFMAs, then O += P V of tile ps.  Tiles ps and
-      // ps+1 are resident; tiles ps+2 (issued a step ago) and ps+3 (issued
-      // now, into tile ps-1's slot) are in flight.
-      const int n = 2 * (piece_end - cj);
-      f32x16 sc_cur, sc_nxt;
-      bool cur_has = has_keys(0);
-      if (cur_has) qk(tile_off(step), sc_cur, [](int) {});
-      for (int ps = 0; ps < n; ++ps, ++step) {
-        const bool has_next = ps + 1 < n;
-        const bool nxt_has = has_next && has_keys(ps + 1);
-        // Tile ps+1 (issued two steps ago) and the word loads of the last step
-        // landed: only that step's kLoadsPerHalf tile loads, issued after its
-        // word loads, may still be in flight (vector loads complete in order).
-        wait_vmcnt<kLoadsPerHalf>();
+      // ---- bf16: step ps waits for its tile (issued kDepth steps ago),
+      // issues the loads of step+kDepth into the slot tile ps-1 left free,
+      // then runs S^T, the online softmax and O += P V on its tile.  Within
+      // one wave the softmax VALU work does not overlap the MFMAs (measured),
+      // so the three phases run back to back on one resident tile.
+      for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
+        // Only the loads of the newest kDepth-1 steps (kLoadsPerHalf each,
+        // issued after those steps' walker words) may still be in flight.
+        wait_vmcnt<kLoadsPerHalf * (kDepth - 1)>();
         lds_barrier();  // ... for every wave; tile ps-1's slot is free
         land();
-        prepare_load(step + 3);
+        prepare_load(step + kDepth);
         fetch_next_ids(step);
 #pragma unroll
         for (int k = 0; k < kLoadsPerHalf; ++k) emit_load(k);
-        SmState st;
-        const int key0 = key0_of(ps);
-        if (nxt_has) {
-          qk(tile_off(step + 1), sc_nxt, [&](int ks) {
-#pragma unroll
-            for (int k = 0; k < kSmSlices; ++k)
-              if (ks == slice_at(k)) sm_slice(k, sc_cur, st, key0, step);
-          });
-        } else {
-#pragma unroll
-          for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc_cur, st, key0, step);
+        if constexpr (kF16) {  // fused: the landed bf16 tile becomes fp16 in place
+          tile_to_f16(smem + tile_off(step), tid);
+          lds_barrier();
         }
-        if (cur_has) {
+        if (has_keys(ps)) {
+          f32x16 sc;
+          SmState st;
+          qk(tile_off(step), sc, [](int) {});
+#pragma unroll
+          for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc, st, key0_of(ps), step);
           rescale_o(st);
           valu_to_mfma_settle(st.pf[0], st.pf[1]);
           pv(tile_off(step), st.pf);
         }
-        sc_cur = sc_nxt;
-        cur_has = nxt_has;
       }
     } else if constexpr (KVF == kKvFp8V41) {
       // ---- V4.1: two bf16 tiles.  Step s runs S^T, softmax and P.V on tile
@@ -1503,7 +1555,7 @@ k_decode(DecodeArgs a) {
           else wait_vmcnt<Lay::kVmPerStep>();
           lds_barrier();  // every wave's loads of this step landed
         }
-        dequant_codes(smem + Lay::kTileOff, reinterpret_cast<float*>(smem + Lay::kSclOff),
+        dequant_codes<kF16>(smem + Lay::kTileOff, reinterpret_cast<float*>(smem + Lay::kSclOff),
                       smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
         lds_barrier();  // the tile is staged; raw slot (step+2)%3 (dequantised last step) is free
         const bool hk = has_keys(ps);
@@ -1555,7 +1607,7 @@ k_decode(DecodeArgs a) {
           // move the 256 accumulators into VGPRs).  amax(O/l) = amax(O)/l
           // exactly, since scaling by a positive constant keeps the order.
           const double pos = (double)Lb - (double)a.s_q + (double)tok;
-          const RopeRow rr = rope_row(pos, row_ok, a.rope_inv_freq, -1.0f);
+          const RopeRow rr = rope_row(pos, row_ok, a.rope_log2_base, -1.0f);
           float rot[2][16];
 #pragma unroll
           for (int t = 0; t < 2; ++t)
@@ -1565,7 +1617,7 @@ k_decode(DecodeArgs a) {
               for (int pp = 0; pp < 2; ++pp) {
                 const int k0 = 16 * t + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * half
                 float cs, sn;
-                rope_pair(rr, a.rope_inv_freq, -1.0f, k0, k0 + 2, half, cs, sn);
+                rope_pair(rr, a.rope_log2_base, -1.0f, k0, k0 + 2, half, cs, sn);
                 const float x0 = o[14 + t][4 * qd + 2 * pp] * inv, x1 = o[14 + t][4 * qd + 2 * pp + 1] * inv;
                 rot[t][4 * qd + 2 * pp] = x0 * cs - x1 * sn;
                 rot[t][4 * qd + 2 * pp + 1] = x0 * sn + x1 * cs;
@@ -1615,7 +1667,6 @@ k_decode(DecodeArgs a) {
       } else {
         // partial of split `split_k` of sequence cb, row group g: O/l rounded
         // to bf16, stored in register order [wave][d-tile][quad pair][lane][8]
-        // (coherent stores: the in-kernel combine may read them from another XCD)
         const int64_t pidx = (int64_t)uni(sload(a.num_splits, cb) + split_k) * a.groups + g;
         const __amdgpu_buffer_rsrc_t prs = buf_rsrc(uni_ptr(a.part_o + pidx * kPartialOElems), kPartialOElems * 2);
         const int vbase = (wave * (16 * 2 * 64 * 8) + lane * 8) * 2;
@@ -1629,19 +1680,12 @@ k_decode(DecodeArgs a) {
               const __bf16 lo = (__bf16)(o[mt][8 * q2 + 2 * e] * inv), hi = (__bf16)(o[mt][8 * q2 + 2 * e + 1] * inv);
               w[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(w, prs, vbase + (mt * 2 + q2) * 64 * 8 * 2, 0, kCoherent);
+            __builtin_amdgcn_raw_buffer_store_b128(w, prs, vbase + (mt * 2 + q2) * 64 * 8 * 2, 0, kPastL2);
           }
         if (half == 0)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2 * kLn2),
                                                 buf_rsrc(uni_ptr(a.part_lse + pidx * kPartialLseFloats), kPartialLseFloats * 4),
-                                                (wave * 32 + r32) * 4, 0, kCoherent);
-        if (!FUSED && a.ctl) {
-          // every wave's stores completed (and are visible device-wide);
-          // then the piece counts itself in
-          wait_vmcnt<0>();
-          __syncthreads();
-          if (tid == 0) __hip_atomic_fetch_add(&a.ctl[3 + a.batch + 2 * cb + g], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+                                                (wave * 32 + r32) * 4, 0, kPastL2);
       }
     }
     // next piece: first item of the following sequence
@@ -1650,22 +1694,16 @@ k_decode(DecodeArgs a) {
     split_k = 0;
   }
   wait_vmcnt<0>();  // no tile load (zeros past the end) outlives the workgroup's LDS
-  // (the fused decode merges in a separate launch: its main loop has no
-  // registers to spare for the merge code)
-  if constexpr (!FUSED) {
-    if (a.ctl) combine_phase<FUSED>(a, smem);
-  }
 }
 
 // ---------------------------------------------------------------------------
-// LSE combine of the 32 rows wt*32.. of row group g of sequence b: wave
-// `sub` (lanes `lane`) merges d-tiles 4*sub .. 4*sub+3; thread (sub, lane)
-// holds lane's row and 16 of the 64 (d-tile, quad) float4s.  Plain output
-// needs one wave per sub; fused output needs all four subs of the rows in
-// one workgroup (amax_s: 1 KB of LDS for the row amax across them).
+// Fused LSE combine of the 32 rows wt*32.. of row group g of sequence b:
+// wave `sub` (lanes `lane`) merges d-tiles 4*sub .. 4*sub+3; thread (sub,
+// lane) holds lane's row and 16 of the 64 (d-tile, quad) float4s.  The
+// epilogue needs each row's amax over all 512 dims, so all four subs of the
+// rows sit in one workgroup (amax_s: 1 KB of LDS).
 // ---------------------------------------------------------------------------
-template <bool FUSED, bool COHERENT>
-__device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub, int lane,
+__device__ void combine_rows_fused(const DecodeArgs& a, int b, int g, int wt, int sub, int lane,
                              float (*amax_s)[64]) {
   const int s0 = a.num_splits[b], ns = a.num_splits[b + 1] - s0;
   if (ns <= 1) return;
@@ -1676,31 +1714,12 @@ __device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub,
   // this lane's LSE of split s: lsep[s * lstride]
   const int64_t lstride = (int64_t)a.groups * kPartialLseFloats;
   const float* lsep = a.part_lse + (int64_t)s0 * lstride + (int64_t)g * kPartialLseFloats + wt * 32 + r32;
-  // COHERENT (in-kernel combine): partials read past L1 and L2, as stored
-  auto lse_of = [&](int s) -> float {
-    if constexpr (COHERENT)
-      return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          buf_rsrc(uni_ptr(a.part_lse + ((int64_t)(s0 + s) * a.groups + g) * kPartialLseFloats), kPartialLseFloats * 4),
-          (wt * 32 + r32) * 4, 0, kCoherent));
-    else
-      return lsep[s * lstride];
-  };
+  auto lse_of = [&](int s) -> float { return lsep[s * lstride]; };
   auto load_split = [&](int s, uint4 (&v)[8]) {
-    if constexpr (COHERENT) {
-      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
-          uni_ptr(a.part_o + ((int64_t)(s0 + s) * a.groups + g) * kPartialOElems), kPartialOElems * 2);
-      const int vb = (wt * (16 * 2 * 64 * 8) + ((sub * 8) * 64 + lane) * 8) * 2;
+    const uint16_t* pb = a.part_o + ((int64_t)(s0 + s) * a.groups + g) * kPartialOElems +
+                         (size_t)wt * (16 * 2 * 64 * 8) + (size_t)((sub * 8) * 64 + lane) * 8;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, vb + k * 64 * 8 * 2, 0, kCoherent);
-        v[k] = make_uint4(t[0], t[1], t[2], t[3]);
-      }
-    } else {
-      const uint16_t* pb = a.part_o + ((int64_t)(s0 + s) * a.groups + g) * kPartialOElems +
-                           (size_t)wt * (16 * 2 * 64 * 8) + (size_t)((sub * 8) * 64 + lane) * 8;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const uint4*>(pb + k * 64 * 8);
-    }
+    for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const uint4*>(pb + k * 64 * 8);
   };
   // LSE = log sum_s exp(lse_s): running max and rescaled sum, eight splits'
   // loads in flight at a time
@@ -1766,28 +1785,12 @@ __device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub,
     }
   }
   const int64_t orow = (int64_t)b * a.rows + row;
-  if constexpr (!FUSED) {
-    if (row_ok) {
-      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + orow * kDv;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int e = sub * 16 + k, mt = e >> 2, qd = e & 3;
-        const int d = 32 * mt + 8 * qd + 4 * half;
-        uint2 pk;
-        pk.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[k][0]) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[k][1]) << 16);
-        pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[k][2]) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[k][3]) << 16);
-        *reinterpret_cast<uint2*>(op + d) = pk;
-      }
-      if (half == 0 && sub == 0) a.lse[orow] = lse;
-    }
-  } else {
+  {
     // conjugate RoPE on dims 448..511 (sub 3 holds d-tiles 12..15)
     const int Lb = a.seqlens[b];
     const int tok = row_ok ? row / a.h_q : 0;
     const double pos = (double)Lb - (double)a.s_q + (double)tok;
-    const RopeRow rr = rope_row(pos, row_ok, a.rope_inv_freq, -1.0f);
+    const RopeRow rr = rope_row(pos, row_ok, a.rope_log2_base, -1.0f);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int e = sub * 16 + k, mt = e >> 2, qd = e & 3;
@@ -1796,7 +1799,7 @@ __device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub,
       for (int pp = 0; pp < 2; ++pp) {
         const int k0 = 16 * (mt - 14) + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * half
         float cs, sn;
-        rope_pair(rr, a.rope_inv_freq, -1.0f, k0, k0 + 2, half, cs, sn);
+        rope_pair(rr, a.rope_log2_base, -1.0f, k0, k0 + 2, half, cs, sn);
         const float x0 = acc[k][2 * pp], x1 = acc[k][2 * pp + 1];
         acc[k][2 * pp] = x0 * cs - x1 * sn;
         acc[k][2 * pp + 1] = x0 * sn + x1 * cs;
@@ -1834,86 +1837,94 @@ __device__ void combine_rows(const DecodeArgs& a, int b, int g, int wt, int sub,
   }
 }
 
-// The combine as its own launch, per (sequence, row group, 32-row tile).
-// Plain output: the tile's four d-tile quarters go to two workgroups of two
-// waves each (twice the workgroups in flight on a streaming kernel).  Fused:
-// one workgroup of four waves, which share the row amax.
-template <bool FUSED>
-__global__ void __launch_bounds__(FUSED ? 256 : 128) k_combine(DecodeArgs a) {
+// The fused combine as its own launch: one workgroup of four waves per
+// (sequence, row group, 32-row tile), which share the row amax.
+__global__ void __launch_bounds__(256) k_combine_fused(DecodeArgs a) {
   __shared__ float amax_s[4][64];
-  if constexpr (FUSED) {
-    const int wt = blockIdx.x & 3;
-    const int g = (blockIdx.x >> 2) % a.groups;
-    const int b = (blockIdx.x >> 2) / a.groups;
-    combine_rows<FUSED, false>(a, b, g, wt, threadIdx.x >> 6, threadIdx.x & 63, amax_s);
-  } else {
-    const int u = blockIdx.x >> 1;
-    const int wt = u & 3;
-    const int g = (u >> 2) % a.groups;
-    const int b = (u >> 2) / a.groups;
-    combine_rows<FUSED, false>(a, b, g, wt, 2 * (blockIdx.x & 1) + (threadIdx.x >> 6), threadIdx.x & 63,
-                               amax_s);
-  }
+  const int wt = blockIdx.x & 3;
+  const int g = (blockIdx.x >> 2) % a.groups;
+  const int b = (blockIdx.x >> 2) / a.groups;
+  combine_rows_fused(a, b, g, wt, threadIdx.x >> 6, threadIdx.x & 63, amax_s);
 }
 
-// ---------------------------------------------------------------------------
-// In-kernel combine (decode launched cooperatively, so every workgroup is
-// resident; plain output only).  Each split piece, once its partial is
-// stored (coherently) and complete, counts itself in arrived[b][g].  A wave
-// out of decode work claims combine tasks (b, g, 32-row tile, d-quarter) in
-// sequence order from one counter, 16 per (b, g) -- as many as the waves of
-// the launch for 64 split sequences, so a task seldom waits for a claimer --
-// and waits until every piece of (b, g) has arrived.  The last of the 16
-// tasks of (b, g) clears its counters and the last claim clears the claim
-// counter, so the metadata is ready for the next decode call.  The wait is
-// bounded in time: past it the task is skipped and an error word is set.
-// Control area ctl (after the split prefix, written by the scheduler):
-//   [0] tasks T   [1] claim counter   [2] error word
-//   [3 .. 3+B) split sequences in order   then arrived[B][2], done[B][2]
-// ---------------------------------------------------------------------------
-constexpr int kCombineTasksPerGroup = 16;
-template <bool FUSED>
-__device__ void combine_phase(const DecodeArgs& a, uint8_t* /*lds*/) {
-  static_assert(!FUSED, "the fused output merges in its own launch");
-  int32_t* ctl = a.ctl;
-  const int B = a.batch, G = a.groups;
-  int32_t* list = ctl + 3;
-  int32_t* arrived = ctl + 3 + B;
-  int32_t* done = arrived + 2 * B;
-  const int lane = fresh_lane();
-  const int T = uni(ctl[0]);
-  const int claimers = (int)gridDim.x * kWaves;
-  for (;;) {
-    int t = 0;
-    if (lane == 0) t = atomicAdd(&ctl[1], 1);
-    t = uni(t);
-    if (t >= T) {
-      if (lane == 0 && t == T + claimers - 1)
-        __hip_atomic_store(&ctl[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
+// The plain combine: one 64-lane workgroup per (sequence b, row group g,
+// 32-row tile wt, 32-dim tile mt), so that even one sequence with many
+// splits spreads over many CUs.  Lane l takes the place of the decode's
+// lane l: row 32wt + l%32 and the 16 values of d-tile mt it held, two
+// 16-byte chunks per split (the partials are stored in that order).
+//   lse = ln sum_s e^{lse_s};  O = sum_s e^{lse_s - lse} O_s,
+// splits in ascending order, -inf partials with weight 0.
+__global__ void __launch_bounds__(64) k_combine_plain(DecodeArgs a) {
+  const int mt = blockIdx.x & 15, wt = (blockIdx.x >> 4) & 3;
+  const int g = (blockIdx.x >> 6) % a.groups, b = (blockIdx.x >> 6) / a.groups;
+  const int s0 = a.num_splits[b], ns = a.num_splits[b + 1] - s0;
+  if (ns <= 1) return;
+  const int lane = threadIdx.x, half = lane >> 5, r32 = lane & 31;
+  const int row = g * kRowsPerWg + wt * 32 + r32;
+  const int64_t lstride = (int64_t)a.groups * kPartialLseFloats;
+  const float* lsep = a.part_lse + (int64_t)s0 * lstride + (int64_t)g * kPartialLseFloats + wt * 32 + r32;
+  float m = -INFINITY, tot = 0.f;
+  for (int s = 0; s < ns; s += 8) {
+    float l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l[i] = s + i < ns ? lsep[(s + i) * lstride] : -INFINITY;
+    float mc = m;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mc = fmaxf(mc, l[i]);
+    if (mc != -INFINITY) {
+      float t = m == -INFINITY ? 0.f : tot * expf(m - mc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t += l[i] == -INFINITY ? 0.f : expf(l[i] - mc);
+      tot = t;
+      m = mc;
     }
-    const int i = t / (kCombineTasksPerGroup * G), g = (t / kCombineTasksPerGroup) % G;
-    const int wt = (t >> 2) & 3, sub = t & 3;
-    const int b = uni(list[i]);
-    const int ns = uni(a.num_splits[b + 1] - a.num_splits[b]);
-    int ok = 1;
-    if (lane == 0) {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (__hip_atomic_load(&arrived[2 * b + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < ns) {
-        __builtin_amdgcn_s_sleep(32);  // ~2k cycles between polls: a thousand waiting waves stay light on memory
-        if (__builtin_amdgcn_s_memrealtime() - t0 > 100000000ull) {  // 1 s at 100 MHz
-          ok = 0;
-          __hip_atomic_store(&ctl[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
+  }
+  const float lse = m == -INFINITY ? -INFINITY : m + logf(tot);
+  const int64_t pstride = (int64_t)a.groups * kPartialOElems;
+  const uint16_t* pb = a.part_o + (int64_t)s0 * pstride + (int64_t)g * kPartialOElems +
+                       (size_t)((wt * 16 + mt) * 2) * 64 * 8 + (size_t)lane * 8;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < ns; s += 4) {
+      uint4 v[4][2];
+      float w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = s + j < ns;
+        const float l = ok ? lsep[(s + j) * lstride] : -INFINITY;
+        w[j] = l == -INFINITY ? 0.f : expf(l - lse);
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+          v[j][q2] = ok ? *reinterpret_cast<const uint4*>(pb + (s + j) * pstride + q2 * 64 * 8) : make_uint4(0, 0, 0, 0);
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const uint32_t u[4] = {v[j][q2].x, v[j][q2].y, v[j][q2].z, v[j][q2].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[8 * q2 + 2 * e] += w[j] * __uint_as_float(u[e] << 16);
+            acc[8 * q2 + 2 * e + 1] += w[j] * __uint_as_float(u[e] & 0xffff0000u);
+          }
+        }
     }
-    if (uni(ok)) combine_rows<false, true>(a, b, g, wt, sub, lane, nullptr);
-    wait_vmcnt<0>();  // this task's output is written before it counts as done
-    if (lane == 0 && atomicAdd(&done[2 * b + g], 1) == kCombineTasksPerGroup - 1) {
-      __hip_atomic_store(&arrived[2 * b + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&done[2 * b + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (row < a.rows) {
+    const int64_t orow = (int64_t)b * a.rows + row;
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + orow * kDv;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {  // value i = 4qd + c sits at d = 32mt + 8qd + 4half + c
+      uint2 pk;
+      pk.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[4 * qd]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[4 * qd + 1]) << 16);
+      pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[4 * qd + 2]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[4 * qd + 3]) << 16);
+      *reinterpret_cast<uint2*>(op + 32 * mt + 8 * qd + 4 * half) = pk;
     }
+    if (mt == 0 && half == 0) a.lse[orow] = lse;
   }
 }
 
@@ -1936,13 +1947,15 @@ __global__ void __launch_bounds__(kThreads) k_debug_gather(DecodeArgs a, int b, 
       fetch_ids_dma(ids, a.indices, ((int64_t)b * a.s_q + t) * a.topk, a.topk, j, h);
       __builtin_amdgcn_s_waitcnt(0);
       const int nvalid = min(kHalfRows, a.topk - j * kPage - h * kHalfRows);
-      if constexpr (KVF == kKvBf16) load_half_bf16_sparse(tile, a.kv, ids, nvalid, wave, lane);
-      else load_half_fp8_sparse(raw, a.kv, ids, nvalid, wave, lane);
+      if constexpr (KVF == kKvBf16) load_half_bf16_sparse(tile, a.kv, a.num_blocks * kPage, ids, nvalid, wave, lane);
+      else load_half_fp8_sparse(raw, a.kv, a.num_blocks * kPage, ids, nvalid, wave, lane);
     } else {
       const int L = a.seqlens[b];
       const bool any = j * kPage < L;
-      const int64_t phys = any ? a.block_table[(int64_t)b * a.max_blocks + j] : 0;
-      const int valid = any ? min(kPage, L - j * kPage) : 0;
+      const int64_t bt = any ? a.block_table[(int64_t)b * a.max_blocks + j] : 0;
+      const bool in_pool = bt >= 0 && bt < a.num_blocks;
+      const int64_t phys = in_pool ? bt : 0;
+      const int valid = any && in_pool ? min(kPage, L - j * kPage) : 0;
       if constexpr (KVF == kKvBf16) load_half_bf16_dense(tile, a.kv, phys, valid, h, wave, lane);
       else load_half_fp8_dense(raw, a.kv, phys, valid, h, wave, lane);
     }
@@ -1979,23 +1992,6 @@ template <int KVF, bool SPARSE, bool FUSED>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
                                   hipEvent_t stop) {
   const int grid = a.num_slots * a.groups;
-  if (a.ctl) {
-    // every workgroup must be resident: the combine tasks wait on other
-    // workgroups' pieces
-    if (start) {
-      const hipError_t e = hipEventRecord(start, stream);
-      if (e != hipSuccess) return e;
-    }
-    DecodeArgs ac = a;
-    void* args[] = {&ac};
-    const hipError_t e = hipLaunchCooperativeKernel((const void*)k_decode<KVF, SPARSE, FUSED>, dim3(grid),
-                                                    dim3(kThreads), args, 0, stream);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();  // clear it: the caller falls back to the separate combine
-      return e;
-    }
-    return stop ? hipEventRecord(stop, stream) : hipSuccess;
-  }
   if (start || stop)
     hipExtLaunchKernelGGL((k_decode<KVF, SPARSE, FUSED>), dim3(grid), dim3(kThreads), 0, stream, start,
                           stop, 0, a);
@@ -2025,8 +2021,8 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool f
 hipError_t launch_combine(const DecodeArgs& a, bool fused, hipStream_t stream) {
   const int grid = a.batch * a.groups * 4;
   if (grid == 0) return hipSuccess;
-  if (fused) hipLaunchKernelGGL(k_combine<true>, dim3(grid), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(k_combine<false>, dim3(2 * grid), dim3(128), 0, stream, a);
+  if (fused) hipLaunchKernelGGL(k_combine_fused, dim3(grid), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(k_combine_plain, dim3(16 * grid), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
 """Helpers shared by the GPU tests: upload a workloads.Problem, run the HIP
 path through the C-ABI binding, and compare with the oracle at the
 tolerances the parity bar sets (bf16 O: max-abs 2e-2 and relative RMS
-5e-3; LSE: max-abs 1e-3; FP8 O: one e4m3 step after dequantisation)."""
+5e-3 over the tensor, and every row's own relative RMS within 1e-2; LSE:
+max-abs 1e-3; FP8 O: one e4m3 step after dequantisation)."""
 import math
 import sys
 
@@ -10,6 +11,9 @@ import torch
 
 O_MAX_ABS = 2e-2
 O_REL_RMS = 5e-3
+# One broken row barely moves the tensor's relative RMS, so every row is
+# also held to its own bound (twice the tensor bar).
+O_ROW_REL_RMS = 1e-2
 LSE_MAX_ABS = 1e-3
 
 
@@ -62,6 +66,16 @@ def run(p, t=None, num_slots=None):
     return out
 
 
+def row_rel_rms(o, ref_o):
+    """Relative RMS error of every output row (last axis), 0 for rows whose
+    reference is exactly zero and whose output is too."""
+    d = (o - ref_o).reshape(-1, o.shape[-1])
+    r = ref_o.reshape(-1, o.shape[-1])
+    num = np.sqrt((d * d).sum(axis=1))
+    den = np.sqrt((r * r).sum(axis=1))
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
 def check_o_lse(o, lse, ref_o, ref_lse, what=""):
     """bf16 O and fp32 LSE against fp64 references."""
     assert o.shape == ref_o.shape, (o.shape, ref_o.shape)
@@ -71,8 +85,11 @@ def check_o_lse(o, lse, ref_o, ref_lse, what=""):
     num = math.sqrt(float((d * d).sum()))
     den = math.sqrt(float((ref_o * ref_o).sum()))
     rel = num / den if den > 0 else num
+    rows = row_rel_rms(o, ref_o) if o.size else np.zeros(1)
+    worst = int(np.argmax(rows))
     assert max_abs <= O_MAX_ABS, f"{what}: O max-abs {max_abs:.3e}"
     assert rel <= O_REL_RMS, f"{what}: O rel-RMS {rel:.3e}"
+    assert rows[worst] <= O_ROW_REL_RMS, f"{what}: row {worst} rel-RMS {rows[worst]:.3e}"
     empty = np.isneginf(ref_lse)
     assert np.array_equal(np.isneginf(lse), empty), f"{what}: -inf LSE pattern differs"
     if (~empty).any():
@@ -82,7 +99,7 @@ def check_o_lse(o, lse, ref_o, ref_lse, what=""):
         assert np.all(o[empty] == 0), f"{what}: empty rows must be exactly 0"
     le = float(np.abs(lse[~empty] - ref_lse[~empty]).max()) if (~empty).any() else 0.0
     say(f"{what}: O max-abs {max_abs:.2e} (bar {O_MAX_ABS:.0e}), rel-RMS {rel:.2e} (bar {O_REL_RMS:.0e}), "
-        f"LSE max-abs {le:.2e} (bar {LSE_MAX_ABS:.0e})")
+        f"worst row rel-RMS {rows[worst]:.2e} (bar {O_ROW_REL_RMS:.0e}), LSE max-abs {le:.2e} (bar {LSE_MAX_ABS:.0e})")
     return max_abs, rel
 
 
@@ -96,30 +113,69 @@ def e4m3_step(a):
     return np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 1e-300))) - 3))
 
 
-def check_fp8(codes, scale, ref_o, ref_scale, what=""):
-    """FP8 output parity: each GPU code, with the GPU's row scale, must be
-    within one e4m3 step of the rounding of some O' that meets the bf16-O
-    bar against the oracle's fp64 O.  Per element, e = distance from O_ref to
-    [(c - step(c)) * scale, (c + step(c)) * scale]; max e <= 2e-2 and
-    ||e|| / ||O_ref|| <= 5e-3.  A per-element step at the element's own binade
-    (2^-9 * scale near zero) is finer than the accuracy any bf16 P.V path has
-    for small elements, so the step is taken around the GPU's code and the O
-    error is held to the same bar as the bf16 output.  The row scale must
-    equal amax/448 of such an O' (|amax_gpu - amax_ref| <= 2e-2) and each
-    row's largest element must encode as +-448."""
-    v = e4m3_value(codes)
-    st = e4m3_step(np.abs(v))
-    lo = (v - st) * scale[..., None]
-    hi = (v + st) * scale[..., None]
-    e = np.where(ref_o < lo, lo - ref_o, np.where(ref_o > hi, ref_o - hi, 0.0))
-    max_e = float(e.max()) if e.size else 0.0
-    den = math.sqrt(float((ref_o * ref_o).sum()))
-    rel = math.sqrt(float((e * e).sum())) / den if den > 0 else 0.0
-    assert max_e <= O_MAX_ABS, f"{what}: fp8 max distance {max_e:.3e}"
-    assert rel <= O_REL_RMS, f"{what}: fp8 rel-RMS distance {rel:.3e}"
-    assert np.all(np.abs(scale - ref_scale) * 448.0 <= O_MAX_ABS), f"{what}: row scale mismatch"
-    nz = ref_scale > 0
+# FP8 output bar ("within one e4m3 step after dequantisation"): the GPU's
+# codes against the oracle's own codes, element by element, with the row
+# scales compared on their own.
+#  - Row scale: |scale_gpu / scale_ref - 1| <= FP8_SCALE_REL, and each row's
+#    largest element encodes as +-448.  The scale is the row's largest |O|
+#    over 448, so it carries that element's relative error and is held to
+#    O's own relative bar (O_REL_RMS); that moves the largest dequantised
+#    element by under 448 * 5e-3 / 32 = 0.07 of its e4m3 step (32 at 256..448).
+#  - Elements of at least amax/16: the two codes are equal or adjacent
+#    e4m3 values (code distance <= 1 in the ordered list of e4m3 values).
+#    An O that sits near a rounding midpoint legitimately rounds either way.
+#  - Smaller elements: their e4m3 step is finer than what a P.V with 16-bit
+#    operands resolves (its error is a fraction of the row's RMS, not of the
+#    element), so the dequantised values must agree to max(one step of the
+#    reference binade, 2^-8 * amax) plus what the scale difference itself
+#    moves them by: c_g s_g - c_r s_r = (c_g - c_r) s_r + c_g (s_g - s_r), so
+#    that term is |s_g - s_r| |c_g|.  Their code distances are reported.
+#  - Bias: among elements of at least amax/16, at most FP8_FLIP_SHARE sit one
+#    code apart and their signed mean code difference is within
+#    FP8_MEAN_SHIFT.  Unbiased 16-bit rounding flips only the few elements
+#    near a rounding midpoint, in both directions; a systematic half-step
+#    shift flips about half of them one way.
+FP8_BIG_FRACTION = 1.0 / 16
+FP8_FLIP_SHARE = 1.0 / 8
+FP8_MEAN_SHIFT = 1e-2
+FP8_SMALL_FLOOR = 2.0 ** -8
+FP8_SCALE_REL = O_REL_RMS
+
+
+def e4m3_order(codes):
+    """Position of each e4m3 code in the ordered list of e4m3 values
+    (+0 and -0 both at 0): adjacent values differ by 1."""
+    c = np.asarray(codes, dtype=np.int64)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def check_fp8(codes, scale, ref_codes, ref_scale, ref_o, what=""):
+    cdist = np.abs(e4m3_order(codes) - e4m3_order(ref_codes))
+    v = e4m3_value(codes) * scale[..., None]
+    rvv = e4m3_value(ref_codes)
+    rv = rvv * ref_scale[..., None]
+    step = e4m3_step(np.abs(rvv)) * ref_scale[..., None]
+    amax = np.abs(ref_o).max(axis=-1, keepdims=True)
+    big = np.abs(ref_o) >= FP8_BIG_FRACTION * amax
+    srel = np.abs(scale / ref_scale - 1.0)
+    gvv = e4m3_value(codes)
+    allow = np.maximum(step, FP8_SMALL_FLOOR * amax) + np.abs(scale - ref_scale)[..., None] * np.abs(gvv)
+    small_bad = ~big & (np.abs(v - rv) > allow * (1 + 1e-9))
+    signed = (e4m3_order(codes) - e4m3_order(ref_codes))[big]
+    flip = float((signed != 0).mean()) if signed.size else 0.0
+    shift = float(signed.mean()) if signed.size else 0.0
+    hist = {k: int((cdist == k).sum()) for k in range(3)}
+    hist[">2"] = int((cdist > 2).sum())
+    say(f"{what}: FP8 code distance {hist} over {cdist.size} elements; >= amax/16: "
+        f"{int((big & (cdist > 1)).sum())} beyond 1 of {int(big.sum())}; exempt share {float((~big).mean()):.3f}; "
+        f"row scale rel err max {float(srel.max()) if srel.size else 0:.2e} (bar {FP8_SCALE_REL:.0e}); "
+        f">= amax/16 one code apart {flip:.4f} (bar {FP8_FLIP_SHARE}), mean code shift {shift:+.2e}")
+    assert int((big & (cdist > 1)).sum()) == 0, f"{what}: elements >= amax/16 more than one e4m3 step apart"
+    assert flip <= FP8_FLIP_SHARE, f"{what}: {flip:.3f} of elements >= amax/16 one code apart"
+    assert abs(shift) <= FP8_MEAN_SHIFT, f"{what}: mean code shift {shift:+.3e}"
+    assert int(small_bad.sum()) == 0, f"{what}: {int(small_bad.sum())} small elements beyond max(step, 2^-8 amax)"
+    assert np.all(srel <= FP8_SCALE_REL), f"{what}: row scale rel err {float(srel.max()):.2e}"
     top = (np.asarray(codes) & 0x7F).max(axis=-1)
-    assert np.all(top[np.abs(ref_o).max(axis=-1) > 0] == 0x7E), f"{what}: row max does not encode as 448"
-    say(f"{what}: FP8 distance max {max_e:.2e} (bar {O_MAX_ABS:.0e}), rel-RMS {rel:.2e} (bar {O_REL_RMS:.0e})")
-    return max_e, rel
+    assert np.all(top[amax[..., 0] > 0] == 0x7E), f"{what}: row max does not encode as 448"
+    return int(cdist.max()) if cdist.size else 0

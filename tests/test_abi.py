@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 def test_size_queries():
     lib = B.load_library()
     assert lib.mla_sched_meta_ints(256) == 2048
-    assert lib.mla_num_splits_ints(64) == 6 * 64 + 4
+    assert lib.mla_num_splits_ints(64) == 65
     # (batch + slots) partials x row groups x (128*512 + 128) fp32
     assert lib.mla_workspace_bytes(64, 1, 128, 256) == 320 * (128 * 512 * 2 + 128 * 4)
     assert lib.mla_workspace_bytes(128, 2, 128, 128) == 256 * 2 * (128 * 512 * 2 + 128 * 4)

@@ -21,7 +21,7 @@ def _torch_cuda():
     return torch
 
 
-def _parity(p, num_slots=None, what="", fused_lse_tol=1e-3):
+def _parity(p, num_slots=None, what=""):
     _torch_cuda()
     say(f"{what} {p.name} b={p.batch} s_q={p.s_q} h_q={p.h_q} L={list(p.seqlens[:8])} "
         f"causal={p.causal} fmt={p.kv_format} sparse={p.indices is not None} fused={p.fused} "
@@ -29,11 +29,12 @@ def _parity(p, num_slots=None, what="", fused_lse_tol=1e-3):
     g = run(p, num_slots=num_slots)
     r = oracle.decode(p)
     if p.fused:
-        check_fp8(g["codes"], g["oscale"], r["o"], r["oscale"], what)
+        check_fp8(g["codes"], g["oscale"], r["codes"], r["oscale"], r["o"], what)
         fin = np.isfinite(r["lse"])
         assert np.array_equal(np.isfinite(g["lse"]), fin)
-        err = np.abs(g["lse"][fin] - r["lse"][fin]).max()
-        assert err <= fused_lse_tol, f"{what}: LSE max-abs {err:.3e}"
+        err = float(np.abs(g["lse"][fin] - r["lse"][fin]).max()) if fin.any() else 0.0
+        say(f"{what}: LSE max-abs {err:.2e} (bar {LSE_MAX_ABS:.0e})")
+        assert err <= LSE_MAX_ABS, f"{what}: LSE max-abs {err:.3e}"
     else:
         check_o_lse(g["o"], g["lse"], r["o"], r["lse"], what)
     return g, r
@@ -83,14 +84,6 @@ def test_sparse_fp8_v41(slots, s_q):
     _parity(p, num_slots=slots, what=f"sparse-fp8-v41 s_q={s_q}")
 
 
-# The fused path rounds q-hat = RoPE(RMSNorm(q)) to bf16 before the MFMA; on
-# this workload that rounding alone moves the LSE by 3.35e-3 in exact
-# arithmetic (the kernel adds ~1e-7 on top).  The O / FP8 output meets its
-# bar; the LSE is held here to 4e-3 and the 1e-3 bar is the strict xfail
-# below until q-hat is carried past bf16 precision into QK^T.
-FUSED_BF16_QHAT_LSE = 4e-3
-
-
 @gpu
 @pytest.mark.parametrize("causal,s_q,slots", [(False, 1, None), (True, 2, 16)])
 def test_dense_fp8(causal, s_q, slots):
@@ -108,22 +101,21 @@ def test_fused_fp8(sparse):
     base = W.make_dense("ff8", [70, 1500, 5, 700], s_q=1, h_q=128, seed=19, fused=True)
     if sparse:
         base = W.make_sparse_bf16_from_dense(base, topk=300, seed=7)
-    _parity(W.with_fp8v32(base, seed=8), num_slots=8, what=f"fused-fp8 sparse={sparse}",
-            fused_lse_tol=FUSED_BF16_QHAT_LSE)
+    _parity(W.with_fp8v32(base, seed=8), num_slots=8, what=f"fused-fp8 sparse={sparse}")
 
 
 @gpu
 def test_fused_sparse_bf16():
     base = W.make_dense("fsp", [90, 400, 3, 1000], s_q=1, h_q=128, seed=20, fused=True)
     p = W.make_sparse_bf16_from_dense(base, topk=200, seed=9)
-    _parity(p, num_slots=16, what="fused-sparse-bf16", fused_lse_tol=FUSED_BF16_QHAT_LSE)
+    _parity(p, num_slots=16, what="fused-sparse-bf16")
 
 
 @gpu
 @pytest.mark.parametrize("slots", [None, 8])
 def test_fused(slots):
     p = W.make_dense("fused", [70, 2048, 5, 700], s_q=1, h_q=128, seed=15, fused=True)
-    _parity(p, num_slots=slots, what="fused", fused_lse_tol=FUSED_BF16_QHAT_LSE)
+    _parity(p, num_slots=slots, what="fused")
 
 
 @gpu
@@ -133,14 +125,15 @@ def test_fused_multi_token(h_q):
     tokens (RoPE angles per lane), with h_q 64 each wave has one token but
     the workgroup two (angles shared across the wave)."""
     p = W.make_dense("fused_mt", [70, 1500, 3, 400], s_q=2, h_q=h_q, seed=17, fused=True)
-    _parity(p, num_slots=16, what=f"fused s_q=2 h{h_q}", fused_lse_tol=FUSED_BF16_QHAT_LSE)
+    _parity(p, num_slots=16, what=f"fused s_q=2 h{h_q}")
 
 
 @gpu
-@pytest.mark.xfail(strict=True, reason="q-hat is rounded to bf16 before QK^T: LSE error 3.3e-3 > 1e-3")
-def test_fused_lse_1e3():
-    p = W.make_dense("fused", [70, 2048, 5, 700], s_q=1, h_q=128, seed=15, fused=True)
-    _parity(p, what="fused-lse-1e-3", fused_lse_tol=1e-3)
+def test_fused_lse_short_rows():
+    """Rows with a few keys: the LSE is then about one score, so it shows
+    the rounding of q-hat directly; it must meet the 1e-3 bar."""
+    p = W.make_dense("fused_short", [1, 2, 5, 9, 33, 70], s_q=1, h_q=128, seed=29, fused=True)
+    _parity(p, what="fused short rows")
 
 
 @gpu
@@ -160,17 +153,7 @@ def test_metadata_bit_exact():
         torch.cuda.synchronize()
         rm, rn = oracle.sched_plan(np.array(sl, dtype=np.int32), rows, topk, S)
         assert np.array_equal(meta.cpu().numpy(), rm)
-        g = ns.cpu().numpy()
-        B = len(sl)
-        assert np.array_equal(g[:B + 1], rn)
-        # control area of the in-kernel combine: task count, cleared
-        # counters, the split sequences in order
-        split = [b for b in range(B) if rn[b + 1] - rn[b] > 1]
-        G = (rows + 127) // 128
-        ctl = g[B + 1:]
-        assert ctl[0] == len(split) * (G if G <= 2 else 0) * 16 and ctl[1] == 0 and ctl[2] == 0
-        assert list(ctl[3:3 + len(split)]) == split
-        assert not ctl[3 + B:3 + 5 * B].any()
+        assert np.array_equal(ns.cpu().numpy(), rn)
 
 
 def _bf16_round_f32(x):
@@ -302,10 +285,8 @@ def test_full_config5_sampled(batch):
     for (b, t, h) in rows:
         r = oracle.decode_row(p, b, t, h)
         what = f"config5 b={batch} row {(b, t, h)}"
-        check_fp8(g["codes"][b, t, h][None], g["oscale"][b, t, h][None], r["o"][None],
-                  np.array([r["oscale"]]), what)
-        # 2K-16K keys per row: the bf16 rounding of q-hat averages out and the
-        # LSE meets the full 1e-3 bar (only rows with a few keys miss it)
+        check_fp8(g["codes"][b, t, h][None], g["oscale"][b, t, h][None], r["codes"][None],
+                  np.array([r["oscale"]]), r["o"][None], what)
         err = abs(g["lse"][b, t, h] - r["lse"])
         say(f"{what}: LSE max-abs {err:.2e} (bar {LSE_MAX_ABS:.0e})")
         assert err <= LSE_MAX_ABS, f"{what}: LSE {err:.3e}"
@@ -352,3 +333,119 @@ def test_decode_timed_matches_decode():
     hip.hipEventDestroy(e1)
     assert 0.0 < ms.value < 1000.0
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+# ------------------------------------------------ every row at full size
+def _cores():
+    import os
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def _all_rows(p, what):
+    """Full-size workload at its real shape and launch configuration: every
+    output row against the oracle's full decode."""
+    _torch_cuda()
+    say(f"full-size all rows {what} {p.name} b={p.batch} s_q={p.s_q} (oracle on {_cores()} threads)")
+    g = run(p)
+    r = oracle.decode(p, nthreads=_cores())
+    if p.fused:
+        check_fp8(g["codes"], g["oscale"], r["codes"], r["oscale"], r["o"], what)
+        fin = np.isfinite(r["lse"])
+        assert np.array_equal(np.isfinite(g["lse"]), fin)
+        err = float(np.abs(g["lse"][fin] - r["lse"][fin]).max())
+        say(f"{what}: LSE max-abs {err:.2e} (bar {LSE_MAX_ABS:.0e})")
+        assert err <= LSE_MAX_ABS, f"{what}: LSE max-abs {err:.3e}"
+    else:
+        check_o_lse(g["o"], g["lse"], r["o"], r["lse"], what)
+
+
+@gpu
+def test_all_rows_config2():
+    _all_rows(W.config2(), "config2")
+
+
+@gpu
+def test_all_rows_config3():
+    _all_rows(W.config3(), "config3")
+
+
+@gpu
+def test_all_rows_config4():
+    _all_rows(W.config4(), "config4")
+
+
+@gpu
+def test_all_rows_config_v41():
+    _all_rows(W.config_v41(), "config-v41")
+
+
+@gpu
+@pytest.mark.parametrize("batch", [32, 1])
+def test_all_rows_config5(batch):
+    _all_rows(W.config5(batch=batch), f"config5 b={batch}")
+
+
+# -------------------------------------------- indices outside the pool
+# A block_table entry outside [0, num_blocks) stages a zero page and a
+# sparse id outside [0, num_blocks * 64) is masked like -1 (the oracle
+# implements the same reading); nothing is read past the pool.
+@gpu
+@pytest.mark.parametrize("fmt", ["bf16", "fp8v32"])
+def test_out_of_pool_block_table(fmt):
+    import dataclasses
+    p = W.make_dense("oob", [300, 1000, 70, 129], s_q=1, h_q=128, seed=23)
+    bt = p.block_table.copy()
+    bt[0, 1] = p.num_blocks + 7
+    bt[1, 3] = -5
+    bt[1, 9] = 2 ** 31 - 1
+    bt[3, 2] = p.num_blocks
+    p = dataclasses.replace(p, block_table=bt)
+    if fmt == "fp8v32":
+        p = W.with_fp8v32(p, seed=4)
+    _parity(p, num_slots=16, what=f"out-of-pool block_table {fmt}")
+
+
+@gpu
+@pytest.mark.parametrize("fmt", ["bf16", "fp8v32", "fp8v41"])
+def test_out_of_pool_sparse_ids(fmt):
+    import dataclasses
+    if fmt == "bf16":
+        p = W.make_sparse_bf16_from_dense(W.make_dense("oobs", [90, 400, 3, 1000], s_q=1, h_q=128, seed=24),
+                                          topk=200, seed=6)
+    elif fmt == "fp8v32":
+        p = W.make_sparse_fp8("oobs8", batch=4, s_q=1, h_q=128, cache_len=1024, topk=300, seed=25, pad_frac=0.5)
+    else:
+        p = W.make_sparse_fp8_v41("oobs41", batch=4, s_q=1, h_q=128, cache_len=1024, topk=300, seed=26,
+                                  pad_frac=0.5)
+    ntok = p.num_blocks * 64
+    rng = np.random.default_rng(8)
+    sel = rng.random(p.indices.shape) < 0.2
+    repl = rng.choice(np.array([ntok, ntok + 1, 2 ** 31 - 1, -2, -1000], dtype=np.int64),
+                      size=p.indices.shape).astype(np.int32)
+    idx = p.indices.copy()
+    idx[sel] = repl[sel]
+    _parity(dataclasses.replace(p, indices=idx), num_slots=8, what=f"out-of-pool sparse ids {fmt}")
+
+
+@gpu
+def test_positions_past_block_table():
+    """Sequences longer than max_blocks_per_seq pages: the positions with no
+    block_table entry read as zero keys."""
+    import dataclasses
+    p = W.make_dense("short_bt", [300, 1000, 70], s_q=1, h_q=128, seed=27)
+    p = dataclasses.replace(p, block_table=np.ascontiguousarray(p.block_table[:, :3]))
+    _parity(p, num_slots=16, what="positions past the block table")
+
+
+# ----------------------------------------- one sequence over many slots
+@gpu
+@pytest.mark.parametrize("fused", [False, True])
+def test_batch1_many_splits(fused):
+    """A small total spreads one item per slot: one sequence of 3000 keys
+    splits 47 ways, and the combine merges all of them."""
+    p = W.make_dense("b1", [3000], s_q=1, h_q=128, seed=28, fused=fused)
+    g, r = _parity(p, what=f"batch 1 fused={fused}")
+    assert int(np.diff(g["num_splits"])[0]) == 47
