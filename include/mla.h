@@ -172,6 +172,24 @@ mla_status mla_decode(const mla_decode_params* params, void* stream);
 mla_status mla_decode_timed(const mla_decode_params* params, void* stream, void* start_event,
                             void* stop_event);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): mla_decode without a
+ * workspace.  The split partials go to a static device array of
+ * MLA_NOALLOC_SCRATCH_BYTES per GPU (allocated with the library's code
+ * object on each device it runs on, held until the process ends); its
+ * device address is looked up on the first call on a device, which must be
+ * the current device.  params->workspace and workspace_bytes are ignored;
+ * flags must be 0 (decode and merge in one call).  Every call on a GPU
+ * shares that GPU's array, so calls that overlap on one GPU (on different
+ * streams, or from several threads without ordering) race; calls ordered on
+ * one stream do not.  Nothing in the array needs to start at zero: the
+ * combine reads only partials the decode launch of the same call wrote.
+ * Calls no hipMalloc, hipFree or allocating routine.  Errors as mla_decode;
+ * MLA_ERR_WORKSPACE when mla_workspace_bytes() for the call exceeds
+ * MLA_NOALLOC_SCRATCH_BYTES. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+mla_status mla_decode_noalloc(const mla_decode_params* params, void* stream);
+
 /* The LSE merge of split partials ("FlashMLA" Ampere-adaptation README,
  * section "Usage": the decode returns (o, lse) over the whole KV length).
  * For every sequence the schedule split, every row: lse = ln sum_s e^{lse_s},

@@ -76,7 +76,7 @@ MLA_FLAG_DEFER_COMBINE = 1
 
 
 EXPORTED = ["mla_num_sched_slots", "mla_sched_meta_ints", "mla_num_splits_ints", "mla_get_metadata",
-            "mla_workspace_bytes", "mla_decode", "mla_decode_timed", "mla_combine", "mla_debug_gather",
+            "mla_workspace_bytes", "mla_decode", "mla_decode_timed", "mla_decode_noalloc", "mla_combine", "mla_debug_gather",
             "mla_status_string", "mla_last_error"]
 
 _lib = None
@@ -107,6 +107,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode.argtypes = [c.POINTER(DecodeParams), c.c_void_p]
     lib.mla_decode_timed.restype = c.c_int
     lib.mla_decode_timed.argtypes = [c.POINTER(DecodeParams), c.c_void_p, c.c_void_p, c.c_void_p]
+    lib.mla_decode_noalloc.restype = c.c_int
+    lib.mla_decode_noalloc.argtypes = [c.POINTER(DecodeParams), c.c_void_p]
     lib.mla_combine.restype = c.c_int
     lib.mla_combine.argtypes = [c.POINTER(DecodeParams), c.c_void_p]
     lib.mla_debug_gather.restype = c.c_int
@@ -219,7 +221,8 @@ def _params(q, kvcache, block_table, cache_seqlens, sched_meta, num_splits, caus
     _need(num_splits, "num_splits", torch.int32, device=dev)
     if num_splits.numel() < int(load_library().mla_num_splits_ints(b)):
         raise ValueError(f"num_splits holds {num_splits.numel()} ints, fewer than batch + 1")
-    _need(workspace, "workspace", torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, device=dev)
     _need(out, "out", torch.uint8 if fused is not None else torch.bfloat16, (b, s_q, h_q, D_V), dev)
     _need(lse, "lse", torch.float32, (b, s_q, h_q), dev)
     if fused is not None:
@@ -245,8 +248,9 @@ def _params(q, kvcache, block_table, cache_seqlens, sched_meta, num_splits, caus
     p.sched_meta = sched_meta.data_ptr()
     p.num_splits = num_splits.data_ptr()
     p.num_slots = sched_meta.shape[0]
-    p.workspace = workspace.data_ptr()
-    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
     p.out = out.data_ptr()
     p.lse = lse.data_ptr()
     if fused is not None:
@@ -294,6 +298,28 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
     _check(load_library().mla_decode(ctypes.byref(p), _stream(dev)))
     if fz is not None:
         return out, lse, fz["out_scale"]
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def mla_decode_noalloc(q: torch.Tensor, kvcache: torch.Tensor, block_table: Optional[torch.Tensor],
+                       cache_seqlens: torch.Tensor, dv: int, sched_meta: torch.Tensor,
+                       num_splits: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                       causal: bool = False, indices: Optional[torch.Tensor] = None,
+                       softmax_scale: Optional[float] = None, kv_format: str = "bf16",
+                       fused: Optional[dict] = None):
+    """mla_decode_with_kvcache through the library's allocation-free entry
+    point: the caller passes every output (out, lse, and fused["out_scale"]
+    when fused) and no workspace; the split partials use the library's
+    static per-GPU scratch array.  Calls that overlap on one GPU race."""
+    assert dv == D_V, "d_v must be 512"
+    p = _params(q, kvcache, block_table, cache_seqlens, sched_meta, num_splits, causal, indices,
+                softmax_scale, kv_format, None, out, lse, fused)
+    _check(load_library().mla_decode_noalloc(ctypes.byref(p), _stream(q.device)))
+    if fused is not None:
+        return out, lse, fused["out_scale"]
     return out, lse
 
 

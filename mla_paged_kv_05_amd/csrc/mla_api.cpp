@@ -213,6 +213,25 @@ mla_status mla_decode_timed(const mla_decode_params* p, void* stream, void* star
   return decode_impl(p, stream, (hipEvent_t)start_event, (hipEvent_t)stop_event);
 }
 
+mla_status mla_decode_noalloc(const mla_decode_params* p, void* stream) {
+  if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+  if (p->flags != 0)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_noalloc takes no flags (got 0x%x)", p->flags);
+  const size_t need = mla_workspace_bytes(p->batch, p->s_q, p->h_q, p->num_slots);
+  if (need > mla::kNoAllocScratchBytes)
+    return fail(MLA_ERR_WORKSPACE,
+                "mla_decode_noalloc: the call needs %zu bytes of scratch, the static array holds %zu "
+                "(batch + num_slots split partials per 128-row group); use mla_decode with a workspace",
+                need, (size_t)mla::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = mla::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "scratch symbol lookup");
+  mla_decode_params q = *p;
+  q.workspace = scratch;
+  q.workspace_bytes = mla::kNoAllocScratchBytes;
+  return decode_impl(&q, stream, nullptr, nullptr);
+}
+
 mla_status mla_combine(const mla_decode_params* p, void* stream) {
   mla::DecodeArgs a{};
   bool sparse = false;

@@ -59,6 +59,12 @@ struct DecodeArgs {
 enum KvFormat { kKvBf16 = 0, kKvFp8V32 = 1, kKvFp8V41 = 2 };
 constexpr int kFp8V41TokenBytes = 528;  // 512 e4m3 codes (all dims) + 16 e8m0 scales
 
+// Size of the static scratch array behind mla_decode_noalloc: the partials
+// of up to 510 (split, row group) pairs.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// Device address of the current device's scratch array (looked up once).
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_sched(const int32_t* seqlens, int batch, int rows, int topk, int num_slots,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool fused,

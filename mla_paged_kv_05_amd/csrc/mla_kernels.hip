@@ -34,6 +34,8 @@
 #include <hip/hip_ext.h>
 #include <cstdint>
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "mla_internal.h"
 
@@ -2036,6 +2038,35 @@ hipError_t launch_debug_gather(const DecodeArgs& a, int kv_format, bool sparse, 
     else hipLaunchKernelGGL((k_debug_gather<kKvFp8V32, false>), dim3(1), dim3(kThreads), 0, stream, a, b, t, j, dst);
   }
   return hipGetLastError();
+}
+
+// Workspace of the allocation-free decode entry point: one copy per GPU the
+// library runs on, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it passes the device address hipGetSymbolAddress returns for the
+// current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device; null until looked up
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace mla

@@ -155,3 +155,21 @@ def test_zero_batch_is_a_noop():
     assert st == 1
     st, _ = status(good_params(batch=1, workspace_bytes=ws0, q=None))
     assert st == 1
+
+
+def test_noalloc_rejects_before_touching_the_device():
+    """The allocation-free entry point refuses flags and any call whose
+    partials exceed its static scratch array, before any HIP call."""
+    lib = B.load_library()
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    m = re.search(r"#define MLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
+    p = good_params(flags=1)
+    assert lib.mla_decode_noalloc(ctypes.byref(p), None) == 1
+    assert "flags" in B.load_library().mla_last_error().decode()
+    # 16384 sequences + 256 slots, one row group: 16640 partials of 128.5 KiB
+    big = good_params(batch=16384, num_slots=256)
+    assert lib.mla_workspace_bytes(16384, 1, 128, 256) > B.NOALLOC_SCRATCH_BYTES
+    assert lib.mla_decode_noalloc(ctypes.byref(big), None) == 3
+    assert "static array" in B.load_library().mla_last_error().decode()
+    assert lib.mla_decode_noalloc(None, None) == 1
