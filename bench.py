@@ -96,9 +96,19 @@ def cpu_baseline(p, nbytes):
     t0 = time.perf_counter()
     oracle.decode(p, nthreads=cores)
     dt = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"whole workload ({p.batch} sequences), fp64, {dt:.2f} s",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3), "cpu_model": model, "threads": cores,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
 
 
 def main():
@@ -231,22 +241,31 @@ def main():
                 step(first + i)
 
     # Timed region: the steps only, bracketed by two events on the stream.
+    # With eager launches every decode launch also records the kernel's own
+    # start and end (mla_decode_timed: HIP events at the dispatch, on the
+    # launch stream), so the kernel durations come from the timed steps
+    # themselves: the GPU's clock drifts over a run, and a separate pass
+    # would time the kernel at another clock.
     stream = torch.cuda.current_stream(dev)
+    kevs = [(hip_event(), hip_event()) for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
-    run_steps(args.warmup)
+    if graphs is not None:
+        run_steps(args.warmup)
+    else:
+        for i in range(args.steps):
+            step(args.warmup + i, kevs[i])
     end.record(stream)
     host = time.perf_counter() - wall0  # host time to enqueue the steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = start.elapsed_time(end) / args.steps
 
-    # Second pass, outside the timed region: the decode kernel's own duration
-    # (mla_decode_timed records HIP events at its dispatch, on the launch
-    # stream), and the metadata call's, per step.
-    kevs = [(hip_event(), hip_event()) for _ in range(args.steps)]
+    # Second pass, outside the timed region: the metadata call's duration
+    # per step, and under --graph (events cannot be recorded at a dispatch
+    # inside a captured graph) the decode kernel's.
     mevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for i in range(args.steps):
         mevs[i][0].record(stream)
@@ -255,11 +274,13 @@ def main():
         mevs[i][1].record(stream)
         if st != 0:
             raise RuntimeError(lib.mla_last_error().decode())
-        pr = params[(args.warmup + i) % R]
-        st = lib.mla_decode_timed(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream), kevs[i][0], kevs[i][1])
-        st |= lib.mla_combine(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream))
-        if st != 0:
-            raise RuntimeError(lib.mla_last_error().decode())
+        if graphs is not None:
+            pr = params[(args.warmup + i) % R]
+            st = lib.mla_decode_timed(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream), kevs[i][0],
+                                      kevs[i][1])
+            st |= lib.mla_combine(ctypes.byref(pr), ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(lib.mla_last_error().decode())
     torch.cuda.synchronize()
     dec_ms = []
     for k0, k1 in kevs:
@@ -309,6 +330,11 @@ def main():
             "traffic": traffic,
             "kernel": "k_decode",
             "kernel_avg_us": round(dec_avg * 1e3, 2),
+            "kernel_median_us": round(float(np.median(dec_ms)) * 1e3, 2),
+            "kernel_p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+            "kernel_p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
+            "kernel_timing": ("HIP events at each decode dispatch in the timed steps" if graphs is None
+                              else "HIP events at the decode dispatch, second eager pass"),
             "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
             "intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
             "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),

@@ -1118,51 +1118,68 @@ k_decode(DecodeArgs a) {
         // + eps) over the row's 576 dims (RMSNorm, then RoPE on dims
         // 512..575 at position len - s_q + t; RoPE is linear, so the row
         // factor may come first), rounded once to fp16 for the fp16 products.
-        // Pass 1 loads the row (all 36 chunks in flight at once, into the
-        // fragments' own registers) and its sum of squares; pass 2 forms
-        // q-hat chunk by chunk with the weight row staged in LDS.
-        constexpr int kQT = ksteps<KVF>() - kQR;  // chunks held in LDS
-        bf16x8 tq[kQT > 0 ? kQT : 1];
-#pragma unroll
-        for (int ks = 0; ks < ksteps<KVF>(); ++ks) {
-          const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
-          if (ks < kQR) qf[ks] = v;
-          else tq[ks - kQR] = v;
-        }
+        // Pass 1 reads the row for its sum of squares only (all 36 chunks in
+        // flight, none kept); pass 2 reads it again (from L2 now) in groups
+        // of four chunks, one group ahead, and forms q-hat chunk by chunk
+        // with the weight row staged in LDS.  Keeping the row in registers
+        // from pass 1 to pass 2 instead would need 144 VGPRs beside the
+        // fragments and spills them.
+        const RopeRow rr = rope_row(pos, row_ok, a.rope_log2_base, 1.0f);
         float ss = 0.f;
+        {
+          bf16x8 v[ksteps<KVF>()];
 #pragma unroll
-        for (int ks = 0; ks < ksteps<KVF>(); ++ks) {
-          const bf16x8 v = ks < kQR ? qf[ks < kQR ? ks : 0] : tq[ks < kQR ? 0 : ks - kQR];
+          for (int ks = 0; ks < ksteps<KVF>(); ++ks) v[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ss += (float)v[e] * (float)v[e];
+          for (int ks = 0; ks < ksteps<KVF>(); ++ks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += (float)v[ks][e] * (float)v[ks][e];
+          }
         }
         ss = row_sum2(ss);
         const float inv = 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
-        const RopeRow rr = rope_row(pos, row_ok, a.rope_log2_base, 1.0f);
         const uint16_t* wl = reinterpret_cast<const uint16_t*>(smem + Lay::kWOff);
+        // the second read must not reuse the first one's registers
+        const uint16_t* qrow2 = qrow + opaque(0);
+        constexpr int kG = 4, kNG = ksteps<KVF>() / kG;
+        static_assert(ksteps<KVF>() % kG == 0, "whole groups");
+        bf16x8 cur[kG], nxt[kG];
 #pragma unroll
-        for (int ks = 0; ks < ksteps<KVF>(); ++ks) {
-          const bf16x8 v = ks < kQR ? qf[ks < kQR ? ks : 0] : tq[ks < kQR ? 0 : ks - kQR];
-          const bf16x8 wv = *reinterpret_cast<const bf16x8*>(wl + (2 * ks + half) * 8);
-          float y[8];
+        for (int i = 0; i < kG; ++i) cur[i] = *reinterpret_cast<const bf16x8*>(qrow2 + (2 * i + half) * 8);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = (float)v[e] * (float)wv[e] * inv;
-          if (ks >= 32) {
+        for (int g = 0; g < kNG; ++g) {
+          if (g + 1 < kNG) {
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-              float cs, sn;
-              rope_pair(rr, a.rope_log2_base, 1.0f, 8 * (ks - 32) + pp, 8 * (ks - 32) + 4 + pp, half, cs, sn);
-              const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
-              y[2 * pp] = x0 * cs - x1 * sn;
-              y[2 * pp + 1] = x0 * sn + x1 * cs;
-            }
+            for (int i = 0; i < kG; ++i)
+              nxt[i] = *reinterpret_cast<const bf16x8*>(qrow2 + (2 * ((g + 1) * kG + i) + half) * 8);
           }
-          bf16x8 h;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) h[e] = to_op16<true>(y[e]);
-          put_q(ks, h);
-          // one chunk at a time: hoisting all 36 weight reads would take
-          // 144 more VGPRs beside the fragments
+          for (int i = 0; i < kG; ++i) {
+            const int ks = g * kG + i;
+            const bf16x8 v = cur[i];
+            const bf16x8 wv = *reinterpret_cast<const bf16x8*>(wl + (2 * ks + half) * 8);
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (float)v[e] * (float)wv[e] * inv;
+            if (ks >= 32) {
+#pragma unroll
+              for (int pp = 0; pp < 4; ++pp) {
+                float cs, sn;
+                rope_pair(rr, a.rope_log2_base, 1.0f, 8 * (ks - 32) + pp, 8 * (ks - 32) + 4 + pp, half, cs, sn);
+                const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
+                y[2 * pp] = x0 * cs - x1 * sn;
+                y[2 * pp + 1] = x0 * sn + x1 * cs;
+              }
+            }
+            bf16x8 h;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = to_op16<true>(y[e]);
+            put_q(ks, h);
+          }
+#pragma unroll
+          for (int i = 0; i < kG; ++i) cur[i] = nxt[i];
+          // one group at a time: the next group's reads are in flight, the
+          // weight reads are not hoisted past it
           __builtin_amdgcn_sched_barrier(0);
         }
       }
