@@ -151,8 +151,8 @@ __device__ __forceinline__ int fresh_lane() {
 // every MFMA accumulator to AGPRs, and the 256 AGPRs are exactly the O
 // accumulator of a 32-row wave tile; S then overflows and spills.  The asm is
 // not volatile, so the scheduler still hoists the LDS reads feeding it.
-// F16 selects the fp16 operand form (the fused path), otherwise bf16; the
-// operands are eight 16-bit values either way.
+// F16 selects the fp16 operand form (the fused path over an FP8 cache),
+// otherwise bf16; the operands are eight 16-bit values either way.
 template <bool F16>
 __device__ __forceinline__ void mfma_s_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
   if constexpr (F16) asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
@@ -172,7 +172,8 @@ __device__ __forceinline__ void mfma_o(f32x16& c, const bf16x8& a, const bf16x8&
   if constexpr (F16) asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
   else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
-// One fp32 value as the 16-bit MFMA operand element: fp16 or bf16, RNE.
+// One fp32 value as the 16-bit MFMA operand element, round to nearest even:
+// bf16, or fp16 (F16).
 template <bool F16>
 __device__ __forceinline__ __bf16 to_op16(float x) {
   if constexpr (F16) return __builtin_bit_cast(__bf16, (_Float16)x);
@@ -519,8 +520,9 @@ __device__ __forceinline__ int scale_slot(int key) {  // key -> h*16 + i
 
 // 32 raw records -> the half tile with the e4m3 codes of dims < 512
 // converted exactly (every e4m3 value is a bf16 value and an fp16 value),
-// dims 512..575 copied (bf16) or converted to fp16 (F16, the fused path),
-// and the fp32 tile scales moved to `scl`.  The decode applies the scales in
+// dims 512..575 copied (bf16) or converted to fp16 (F16: exact for
+// magnitudes in [2^-14, 65504], 2^-24 absolute resolution below), and the
+// fp32 tile scales moved to `scl`.  The decode applies the scales in
 // fp32: to each tile's partial scores in QK^T and to P in P.V, so no product
 // code*scale is ever rounded to 16 bits.  An all-zero record gives a zero row
 // with zero scales.
@@ -573,35 +575,6 @@ __device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const u
   if (tid < 4 * kHalfRows) {
     const int r = tid >> 2, t = tid & 3;
     scl[t * 32 + scale_slot(r)] = *reinterpret_cast<const float*>(raw + r * kFp8TokenBytes + 512 + 4 * t);
-  }
-}
-
-// A staged bf16 half tile (main and RoPE parts) converted in place to fp16,
-// for the fused path's fp16 products.  Exact for |x| in fp16's normal range
-// [2^-14, 65504]; smaller magnitudes keep 2^-24 absolute resolution.  Each
-// thread converts every 256th 16-byte chunk of the tile (pad included), in
-// two batches whose reads all go out before their writes.
-__device__ __forceinline__ void tile_to_f16(uint8_t* tile, int tid) {
-  tid = (tid & ~63) | fresh_lane();
-  constexpr int kChunks = kHalfBytes / 16;                       // 2336
-  constexpr int kPer = (kChunks + kThreads - 1) / kThreads;      // 10, the last partly
-  constexpr int kBatch = kPer / 2;
-  static_assert(kPer == 2 * kBatch, "two equal batches");
-#pragma unroll
-  for (int bt = 0; bt < 2; ++bt) {
-    uint4 v[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int c = (bt * kBatch + i) * kThreads + tid;
-      if (c < kChunks) v[i] = *reinterpret_cast<const uint4*>(tile + c * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int c = (bt * kBatch + i) * kThreads + tid;
-      if (c < kChunks)
-        *reinterpret_cast<uint4*>(tile + c * 16) =
-            make_uint4(bf16x2_to_f16x2(v[i].x), bf16x2_to_f16x2(v[i].y), bf16x2_to_f16x2(v[i].z), bf16x2_to_f16x2(v[i].w));
-    }
   }
 }
 
@@ -833,7 +806,10 @@ template <int KVF, bool SPARSE, bool FUSED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_decode(DecodeArgs a) {
   using Lay = DecodeLayout<KVF, SPARSE, FUSED>;
-  constexpr bool kF16 = FUSED;  // the fused path runs both products in fp16
+  // The fused path over a V3.2 FP8 cache runs both products on fp16
+  // operands: its codes are exact in fp16 as in bf16, the bf16-rounded q-hat
+  // converts to fp16 exactly, and P (scaled per 128 dims) keeps 3 more bits.
+  constexpr bool kF16 = FUSED && KVF == kKvFp8V32;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Lay::kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
@@ -1090,12 +1066,8 @@ k_decode(DecodeArgs a) {
     // ---- piece prologue: the query fragments, then a drain.  The loads of
     // the piece's first steps (and the previous piece's stores) are older
     // than the query loads, so their latencies overlap.
-    // Query fragments of this piece.  Fused: q^ = inv * RoPE(q (.) w) with
-    // inv = 1 / sqrt(mean(q^2) + eps) (RMSNorm over the row's 576 dims, then
-    // RoPE on dims 512..575 at position len - s_q + t; RoPE is linear, so the
-    // row factor commutes with it).  The fragments hold bf16(RoPE(q (.) w))
-    // chunk by chunk and inv joins the row's softmax scale, applied to S in
-    // fp32; no chunk has to wait for the whole row's statistic.
+    // Query fragments of this piece: the bf16 q rows, or (fused) q-hat
+    // formed from them below.
     const float srow = a.scale_log2;  // log2(e) * softmax scale (the fused q-hat carries its RMSNorm factor)
     {
       const uint16_t* qrow = a.q + ((int64_t)cb * a.rows + (row_ok ? row : 0)) * dqk_of<KVF>();
@@ -1117,7 +1089,10 @@ k_decode(DecodeArgs a) {
         // Fused prologue: q-hat = inv * RoPE(q (.) w), inv = 1/sqrt(mean(q^2)
         // + eps) over the row's 576 dims (RMSNorm, then RoPE on dims
         // 512..575 at position len - s_q + t; RoPE is linear, so the row
-        // factor may come first), rounded once to fp16 for the fp16 products.
+        // factor may come first), rounded once to bf16: the attention takes
+        // q-hat as its bf16 operand, as it would take the q input of an
+        // unfused pipeline, so the fusion leaves the attention arithmetic as
+        // it is.
         // Pass 1 reads the row for its sum of squares only (all 36 chunks in
         // flight, none kept); pass 2 reads it again (from L2 now) in groups
         // of four chunks, one group ahead, and forms q-hat chunk by chunk
@@ -1173,7 +1148,7 @@ k_decode(DecodeArgs a) {
             }
             bf16x8 h;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = to_op16<true>(y[e]);
+            for (int e = 0; e < 8; ++e) h[e] = to_op16<kF16>((float)(__bf16)y[e]);  // bf16, then (exactly) fp16 if F16
             put_q(ks, h);
           }
 #pragma unroll
@@ -1500,10 +1475,6 @@ k_decode(DecodeArgs a) {
         fetch_next_ids(step);
 #pragma unroll
         for (int k = 0; k < kLoadsPerHalf; ++k) emit_load(k);
-        if constexpr (kF16) {  // fused: the landed bf16 tile becomes fp16 in place
-          tile_to_f16(smem + tile_off(step), tid);
-          lds_barrier();
-        }
         if (has_keys(ps)) {
           f32x16 sc;
           SmState st;

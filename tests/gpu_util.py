@@ -131,13 +131,15 @@ def e4m3_step(a):
 #    moves them by: c_g s_g - c_r s_r = (c_g - c_r) s_r + c_g (s_g - s_r), so
 #    that term is |s_g - s_r| |c_g|.  Their code distances are reported.
 #  - Bias: among elements of at least amax/16, at most FP8_FLIP_SHARE sit one
-#    code apart and their signed mean code difference is within
-#    FP8_MEAN_SHIFT.  Unbiased 16-bit rounding flips only the few elements
-#    near a rounding midpoint, in both directions; a systematic half-step
-#    shift flips about half of them one way.
+#    code apart, and the signed sum of their code differences is within
+#    FP8_SHIFT_SIGMAS standard deviations of a symmetric +-1 walk over the
+#    n elements that differ (|sum| <= 4 sqrt(n)).  Unbiased 16-bit rounding
+#    flips only the few elements near a rounding midpoint, in both
+#    directions; a one-step bias moves all n the same way (sum = n, which
+#    fails once n > 16), a half-step shift about half of them.
 FP8_BIG_FRACTION = 1.0 / 16
 FP8_FLIP_SHARE = 1.0 / 8
-FP8_MEAN_SHIFT = 1e-2
+FP8_SHIFT_SIGMAS = 4.0
 FP8_SMALL_FLOOR = 2.0 ** -8
 FP8_SCALE_REL = O_REL_RMS
 
@@ -164,16 +166,18 @@ def check_fp8(codes, scale, ref_codes, ref_scale, ref_o, what=""):
     small_bad = ~big & (np.abs(v - rv) > allow * (1 + 1e-9))
     signed = (e4m3_order(codes) - e4m3_order(ref_codes))[big]
     flip = float((signed != 0).mean()) if signed.size else 0.0
-    shift = float(signed.mean()) if signed.size else 0.0
+    moved = int((signed != 0).sum())
+    zshift = float(signed.sum()) / math.sqrt(max(moved, 1))
     hist = {k: int((cdist == k).sum()) for k in range(3)}
     hist[">2"] = int((cdist > 2).sum())
     say(f"{what}: FP8 code distance {hist} over {cdist.size} elements; >= amax/16: "
         f"{int((big & (cdist > 1)).sum())} beyond 1 of {int(big.sum())}; exempt share {float((~big).mean()):.3f}; "
         f"row scale rel err max {float(srel.max()) if srel.size else 0:.2e} (bar {FP8_SCALE_REL:.0e}); "
-        f">= amax/16 one code apart {flip:.4f} (bar {FP8_FLIP_SHARE}), mean code shift {shift:+.2e}")
+        f">= amax/16 one code apart {flip:.4f} (bar {FP8_FLIP_SHARE}), signed shift {zshift:+.2f} sigma "
+        f"(bar {FP8_SHIFT_SIGMAS:.0f})")
     assert int((big & (cdist > 1)).sum()) == 0, f"{what}: elements >= amax/16 more than one e4m3 step apart"
     assert flip <= FP8_FLIP_SHARE, f"{what}: {flip:.3f} of elements >= amax/16 one code apart"
-    assert abs(shift) <= FP8_MEAN_SHIFT, f"{what}: mean code shift {shift:+.3e}"
+    assert abs(zshift) <= FP8_SHIFT_SIGMAS, f"{what}: code shift {zshift:+.2f} sigma over {moved} moved codes"
     assert int(small_bad.sum()) == 0, f"{what}: {int(small_bad.sum())} small elements beyond max(step, 2^-8 amax)"
     assert np.all(srel <= FP8_SCALE_REL), f"{what}: row scale rel err {float(srel.max()):.2e}"
     top = (np.asarray(codes) & 0x7F).max(axis=-1)
