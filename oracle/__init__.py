@@ -62,8 +62,6 @@ def _load():
     lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
     lib.orc_e8m0_decode.restype = ctypes.c_double
     lib.orc_e8m0_decode.argtypes = [ctypes.c_uint8]
-    lib.orc_bf16_round.restype = ctypes.c_double
-    lib.orc_bf16_round.argtypes = [ctypes.c_double]
     lib.orc_e4m3_encode_rne.restype = ctypes.c_uint8
     lib.orc_e4m3_encode_rne.argtypes = [ctypes.c_double]
     lib.orc_rmsnorm.restype = None
@@ -122,13 +120,6 @@ def e8m0_decode(codes) -> np.ndarray:
     lib = _load()
     c = np.asarray(codes, dtype=np.uint8).ravel()
     return np.array([lib.orc_e8m0_decode(int(x)) for x in c], dtype=np.float64)
-
-
-def bf16_round(x) -> np.ndarray:
-    """Nearest bf16 value of each element (fp64 in, fp64 out), ties to even."""
-    lib = _load()
-    v = np.asarray(x, dtype=np.float64)
-    return np.array([lib.orc_bf16_round(float(a)) for a in v.ravel()], dtype=np.float64).reshape(v.shape)
 
 
 def e4m3_encode(x) -> np.ndarray:

@@ -32,10 +32,7 @@
  *  - "FlashMLA fused norm-RoPE-attention-RoPE-cast kernel" (inference-
  *    research card), section "Arithmetic intensity": the fused kernel runs
  *    Q-norm, Q-RoPE, attention, conjugate O-RoPE and the cast to FP8 in
- *    that order without changing the attention arithmetic.  Reading: the
- *    attention takes the normalised, rotated query in its own operand
- *    precision, bf16 (round to nearest even), exactly as it takes the bf16
- *    q of the unfused path; everything after that is fp64 as elsewhere.
+ *    that order without changing the attention arithmetic.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *  - LSE is the natural log of the sum of exp of the *scaled* scores.
@@ -94,22 +91,6 @@ double orc_e4m3_decode(uint8_t code) {
   else
     v = ldexp(1.0 + (double)m / 8.0, e - 7);
   return s ? -v : v;
-}
-
-/* Nearest bfloat16 value (8 significant bits, binary32's exponent range),
- * ties to even; beyond the largest finite value by half a step or more it
- * is +-inf.  Below 2^-126 the step stays 2^-133 (subnormals). */
-double orc_bf16_round(double x) {
-  if (isnan(x) || isinf(x) || x == 0.0) return x;
-  double a = fabs(x);
-  int e2;
-  (void)frexp(a, &e2);           /* a = f * 2^e2, f in [0.5, 1) */
-  int e = e2 - 1;                 /* a in [2^e, 2^(e+1)) */
-  if (e < -126) e = -126;         /* subnormal range: fixed step */
-  double step = ldexp(1.0, e - 7);
-  double r = nearbyint(a / step) * step; /* default mode: ties to even */
-  if (r > ldexp(255.0, 120)) r = INFINITY; /* largest finite bf16 is (2 - 2^-7) * 2^127 */
-  return copysign(r, x);
 }
 
 /* OCP E8M0 (a scale): an 8-bit biased exponent, value 2^(e - 127); the
@@ -290,8 +271,7 @@ static int64_t visible_tokens(const orc_problem* p, int b, int t, int64_t* ids) 
   return n;
 }
 
-/* Query row (b, t, h) after the optional fused prologue (RMSNorm and RoPE
- * in fp64, then rounded to bf16 as the attention's operand). */
+/* Query row (b, t, h) after the optional fused prologue, in fp64. */
 static void query_row(const orc_problem* p, int b, int t, int h, double* q) {
   const uint16_t* src = p->q + (((int64_t)b * p->s_q + t) * p->h_q + h) * p->d_qk;
   for (int d = 0; d < p->d_qk; ++d) q[d] = orc_bf16_to_f64(src[d]);
@@ -302,7 +282,6 @@ static void query_row(const orc_problem* p, int b, int t, int h, double* q) {
     for (int d = 0; d < p->d_qk; ++d) q[d] = y[d];
     double pos = (double)p->seqlens[b] - (double)p->s_q + (double)t;
     orc_rope(q + 512, (p->d_qk - 512) / 2, pos, p->rope_base, +1.0);
-    for (int d = 0; d < p->d_qk; ++d) q[d] = orc_bf16_round(q[d]); /* the attention's operand */
   }
 }
 
