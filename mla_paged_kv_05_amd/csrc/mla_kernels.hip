@@ -526,10 +526,35 @@ __device__ __forceinline__ int scale_slot(int key) {  // key -> h*16 + i
 // fp32: to each tile's partial scores in QK^T and to P in P.V, so no product
 // code*scale is ever rounded to 16 bits.  An all-zero record gives a zero row
 // with zero scales.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two bf16 values -> two fp16 values, round to nearest even (one
+// v_cvt_pk_f16_f32 after widening): exact for magnitudes in [2^-14, 65504].
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-  const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+  const f32x2_t f = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+}
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
+  return make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w));
+}
+// The fused path over a bf16 cache runs its products on fp16: each wave
+// converts in place exactly the chunks its own loads staged in a half tile
+// (main rows wave + 4k, k < 8, and its 1 KB of RoPE rows), right after its
+// own load wait, so the conversion needs no barrier of its own: the step's
+// barrier that follows publishes it to the other waves.
+__device__ __forceinline__ void own_chunks_to_f16(uint8_t* slot, int wave) {
+  const int l16 = fresh_lane() << 4;
+  uint4 v[kLoadsPerHalf];
+#pragma unroll
+  for (int k = 0; k < kLoadsPerHalf; ++k) {
+    const int off = k < kHalfRows / kWaves ? (wave + kWaves * k) * kMainStride : kRopeOff + wave * 1024;
+    v[k] = *reinterpret_cast<const uint4*>(slot + off + l16);
+  }
+#pragma unroll
+  for (int k = 0; k < kLoadsPerHalf; ++k) {
+    const int off = k < kHalfRows / kWaves ? (wave + kWaves * k) * kMainStride : kRopeOff + wave * 1024;
+    *reinterpret_cast<uint4*>(slot + off + l16) = bf16x8_to_f16x8(v[k]);
+  }
 }
 template <bool F16>
 __device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const uint8_t* raw, int tid) {
@@ -567,9 +592,7 @@ __device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const u
   }
   {
     const int r = tid >> 3, c = tid & 7;
-    if constexpr (F16)
-      rope = make_uint4(bf16x2_to_f16x2(rope.x), bf16x2_to_f16x2(rope.y), bf16x2_to_f16x2(rope.z),
-                        bf16x2_to_f16x2(rope.w));
+    if constexpr (F16) rope = bf16x8_to_f16x8(rope);
     *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = rope;
   }
   if (tid < 4 * kHalfRows) {
@@ -806,10 +829,11 @@ template <int KVF, bool SPARSE, bool FUSED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_decode(DecodeArgs a) {
   using Lay = DecodeLayout<KVF, SPARSE, FUSED>;
-  // The fused path over a V3.2 FP8 cache runs both products on fp16
-  // operands: its codes are exact in fp16 as in bf16, the bf16-rounded q-hat
-  // converts to fp16 exactly, and P (scaled per 128 dims) keeps 3 more bits.
-  constexpr bool kF16 = FUSED && KVF == kKvFp8V32;
+  // The fused path runs both products on fp16 operands: q-hat is formed in
+  // fp32 and rounded once, to fp16 (3 more bits than bf16), so QK^T meets
+  // the LSE bar even on rows of a few keys; bf16 K/V and e4m3 codes convert
+  // to fp16 exactly, and P keeps 3 more bits too.
+  constexpr bool kF16 = FUSED;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Lay::kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
@@ -1089,10 +1113,7 @@ k_decode(DecodeArgs a) {
         // Fused prologue: q-hat = inv * RoPE(q (.) w), inv = 1/sqrt(mean(q^2)
         // + eps) over the row's 576 dims (RMSNorm, then RoPE on dims
         // 512..575 at position len - s_q + t; RoPE is linear, so the row
-        // factor may come first), rounded once to bf16: the attention takes
-        // q-hat as its bf16 operand, as it would take the q input of an
-        // unfused pipeline, so the fusion leaves the attention arithmetic as
-        // it is.
+        // factor may come first), rounded once to fp16 for the fp16 products.
         // Pass 1 reads the row for its sum of squares only (all 36 chunks in
         // flight, none kept); pass 2 reads it again (from L2 now) in groups
         // of four chunks, one group ahead, and forms q-hat chunk by chunk
@@ -1148,7 +1169,7 @@ k_decode(DecodeArgs a) {
             }
             bf16x8 h;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = to_op16<kF16>((float)(__bf16)y[e]);  // bf16, then (exactly) fp16 if F16
+            for (int e = 0; e < 8; ++e) h[e] = to_op16<kF16>(y[e]);
             put_q(ks, h);
           }
 #pragma unroll
@@ -1469,6 +1490,7 @@ k_decode(DecodeArgs a) {
         // Only the loads of the newest kDepth-1 steps (kLoadsPerHalf each,
         // issued after those steps' walker words) may still be in flight.
         wait_vmcnt<kLoadsPerHalf * (kDepth - 1)>();
+        if constexpr (FUSED) own_chunks_to_f16(smem + tile_off(step), wave);  // this wave's rows -> fp16
         lds_barrier();  // ... for every wave; tile ps-1's slot is free
         land();
         prepare_load(step + kDepth);
