@@ -94,7 +94,9 @@ size_t mla_num_splits_ints(int32_t batch);      /* = batch + 1      */
  *                     num_splits[b+1] - num_splits[b] of them)
  * The split rule: a sequence has n_b = ceil(len/64) work items (ceil(topk/64)
  * when sparse; an empty sequence keeps one item with no KV); with
- * F = max(1, ceil(min(rows,128)/32)), the items are laid on a line where
+ * F = max(1, ceil(min(rows,128)/64)) (a piece's fixed cost -- query load,
+ * pipeline fill and finalize -- in items: about two for 128 rows), the
+ * items are laid on a line where
  * sequence b starts at U_b = sum_{b'<b}(F + n_b') and its item j sits at
  * U_b + F + j; with cap = ceil((U_batch+1)/S), slot s takes the items at
  * positions [s*cap, (s+1)*cap).  A small total (U_batch < S) thus gives

@@ -17,10 +17,11 @@ constexpr int kFp8TokenBytes = 656;
 constexpr int kMaxBatch = 16384;
 constexpr int kMaxRows = 65536;
 
-// Piece cost F of the split rule (in KV-block units).
+// Piece cost F of the split rule (in KV-block units): a piece's query load,
+// pipeline fill and finalize cost about two 64-key items at 128 rows.
 inline int sched_piece_cost(int rows) {
   int m = rows < kRowsPerWg ? rows : kRowsPerWg;
-  int f = (m + 31) / 32;
+  int f = (m + 63) / 64;
   return f < 1 ? 1 : f;
 }
 

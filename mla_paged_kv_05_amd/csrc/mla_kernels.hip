@@ -262,7 +262,7 @@ k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
   const int tid = threadIdx.x;
   const int F = [&] {
     int m = rows < kRowsPerWg ? rows : kRowsPerWg;
-    int f = (m + 31) / 32;
+    int f = (m + 63) / 64;
     return f < 1 ? 1 : f;
   }();
   const int per = (B + kSchedThreads - 1) / kSchedThreads;

@@ -378,7 +378,7 @@ int orc_decode_row_subset(const orc_problem* p, int b, int t, int h, int64_t n,
 /* ------------------------------------------------------------------ */
 /*
  * n_b   = ceil(topk/64) if topk > 0 else ceil(seqlens[b]/64)   (work items)
- * F     = max(1, ceil(min(M,128)/32))                            (piece cost)
+ * F     = max(1, ceil(min(M,128)/64))                            (piece cost)
  * U_0 = 0, U_{b+1} = U_b + F + n_b, T = U_B
  * cap   = ceil((T+1)/S)
  * Batch b has max(n_b,1) items; item j sits at P(b,j) = U_b + F + j and
@@ -393,7 +393,7 @@ int orc_sched_plan(const int32_t* seqlens, int B, int M, int topk, int S, int32_
                    int32_t* num_splits) {
   if (B < 0 || S < 1 || M < 1) return 1;
   int mm = M < 128 ? M : 128;
-  int64_t F = (mm + 31) / 32;
+  int64_t F = (mm + 63) / 64;
   if (F < 1) F = 1;
   int64_t* U = (int64_t*)malloc(sizeof(int64_t) * (size_t)(B + 1));
   int64_t* nb = (int64_t*)malloc(sizeof(int64_t) * (size_t)(B > 0 ? B : 1));

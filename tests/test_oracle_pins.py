@@ -467,7 +467,7 @@ def sched_check(seqlens, rows, topk, S):
     B = len(seqlens)
     nb = [(-(-topk // 64)) if topk else -(-max(int(L), 0) // 64) for L in seqlens]
     items = [max(n, 1) for n in nb]
-    F = max(1, -(-min(rows, 128) // 32))
+    F = max(1, -(-min(rows, 128) // 64))
     # walk the slots: every (b, item) exactly once, in order, contiguous
     seen = []
     for s in range(S):
