@@ -861,12 +861,6 @@ k_decode(DecodeArgs a) {
   const int32_t* ms = a.meta + 8 * slot;
   const int b0 = uni(sload(ms, 0));
   if (b0 < 0) return;  // no work in this slot
-  // Fused: the norm weight row goes to LDS once; every piece's prologue reads it there.
-  if constexpr (FUSED) {
-    if (tid < kDqk / 8)
-      *reinterpret_cast<uint4*>(smem + Lay::kWOff + tid * 16) = reinterpret_cast<const uint4*>(a.norm_w)[tid];
-    __syncthreads();
-  }
   const int j0 = uni(sload(ms, 1)), b1 = uni(sload(ms, 2)), j1 = uni(sload(ms, 3)),
             nitems = uni(sload(ms, 5));
   int split_k = uni(sload(ms, 4));
@@ -1116,16 +1110,24 @@ k_decode(DecodeArgs a) {
         // factor may come first), rounded once to fp16 for the fp16 products.
         // Pass 1 reads the row for its sum of squares only (all 36 chunks in
         // flight, none kept); pass 2 reads it again (from L2 now) in groups
-        // of four chunks, one group ahead, and forms q-hat chunk by chunk
+        // of four chunks, two groups ahead, and forms q-hat chunk by chunk
         // with the weight row staged in LDS.  Keeping the row in registers
         // from pass 1 to pass 2 instead would need 144 VGPRs beside the
         // fragments and spills them.
         const RopeRow rr = rope_row(pos, row_ok, a.rope_log2_base, 1.0f);
+        // The first piece also reads the norm weight row beside the query
+        // (stored to LDS after pass 1, for every later piece too) and issues
+        // its first KV loads here, so that they land during the prologue.
+        uint4 wrow = make_uint4(0, 0, 0, 0);
+        if (first_piece && tid < kDqk / 8) wrow = reinterpret_cast<const uint4*>(a.norm_w)[tid];
         float ss = 0.f;
         {
           bf16x8 v[ksteps<KVF>()];
 #pragma unroll
           for (int ks = 0; ks < ksteps<KVF>(); ++ks) v[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
+          if constexpr (KVF == kKvBf16) {
+            if (first_piece) issue_first_loads();
+          }
 #pragma unroll
           for (int ks = 0; ks < ksteps<KVF>(); ++ks) {
 #pragma unroll
@@ -1134,20 +1136,26 @@ k_decode(DecodeArgs a) {
         }
         ss = row_sum2(ss);
         const float inv = 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
+        if (first_piece) {
+          if (tid < kDqk / 8) *reinterpret_cast<uint4*>(smem + Lay::kWOff + tid * 16) = wrow;
+          lds_barrier();
+        }
         const uint16_t* wl = reinterpret_cast<const uint16_t*>(smem + Lay::kWOff);
         // the second read must not reuse the first one's registers
         const uint16_t* qrow2 = qrow + opaque(0);
         constexpr int kG = 4, kNG = ksteps<KVF>() / kG;
         static_assert(ksteps<KVF>() % kG == 0, "whole groups");
-        bf16x8 cur[kG], nxt[kG];
+        bf16x8 cur[kG], nxt[kG], nx2[kG];
 #pragma unroll
         for (int i = 0; i < kG; ++i) cur[i] = *reinterpret_cast<const bf16x8*>(qrow2 + (2 * i + half) * 8);
 #pragma unroll
+        for (int i = 0; i < kG; ++i) nxt[i] = *reinterpret_cast<const bf16x8*>(qrow2 + (2 * (kG + i) + half) * 8);
+#pragma unroll
         for (int g = 0; g < kNG; ++g) {
-          if (g + 1 < kNG) {
+          if (g + 2 < kNG) {
 #pragma unroll
             for (int i = 0; i < kG; ++i)
-              nxt[i] = *reinterpret_cast<const bf16x8*>(qrow2 + (2 * ((g + 1) * kG + i) + half) * 8);
+              nx2[i] = *reinterpret_cast<const bf16x8*>(qrow2 + (2 * ((g + 2) * kG + i) + half) * 8);
           }
 #pragma unroll
           for (int i = 0; i < kG; ++i) {
@@ -1173,14 +1181,17 @@ k_decode(DecodeArgs a) {
             put_q(ks, h);
           }
 #pragma unroll
-          for (int i = 0; i < kG; ++i) cur[i] = nxt[i];
-          // one group at a time: the next group's reads are in flight, the
-          // weight reads are not hoisted past it
+          for (int i = 0; i < kG; ++i) {
+            cur[i] = nxt[i];
+            nxt[i] = nx2[i];
+          }
+          // one group at a time: the next two groups' reads are in flight,
+          // the weight reads are not hoisted past it
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-    if constexpr (KVF == kKvBf16) {
+    if constexpr (KVF == kKvBf16 && !FUSED) {
       if (first_piece) issue_first_loads();  // after the query loads: latencies overlap
     }
     wait_vmcnt<0>();
