@@ -162,6 +162,15 @@ typedef struct mla_decode_params {
  * batch = 0 is a no-op that launches nothing; q, kv, block_table,
  * cache_seqlens, out and lse may then be NULL (sched_meta, num_splits and
  * the workspace may not).
+ * Pool bounds: nothing outside the pool [0, num_blocks) is ever read.  A
+ * sparse id outside [0, num_blocks*64) is masked like -1.  A block_table
+ * entry outside [0, num_blocks) names no page: its 64 positions stay
+ * visible and read as all-zero keys (score 0), and so do positions past
+ * max_blocks_per_seq pages.  Entries past ceil(len/64) are never read.
+ * Fused arithmetic: q-hat is rounded to fp16 and both products run on fp16
+ * operands (bf16 KV and e4m3 codes convert exactly), so the fused path
+ * needs |K|, |q-hat| and, over an FP8 cache, |P * tile scale| below 65504;
+ * magnitudes under 2^-14 keep 2^-24 absolute resolution.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP (launch failure). */
 mla_status mla_decode(const mla_decode_params* params, void* stream);
 
