@@ -1720,164 +1720,105 @@ k_decode(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Fused LSE combine of the 32 rows wt*32.. of row group g of sequence b:
-// wave `sub` (lanes `lane`) merges d-tiles 4*sub .. 4*sub+3; thread (sub,
-// lane) holds lane's row and 16 of the 64 (d-tile, quad) float4s.  The
-// epilogue needs each row's amax over all 512 dims, so all four subs of the
-// rows sit in one workgroup (amax_s: 1 KB of LDS).
+// Fused combine, second launch: the epilogue of the 32 rows wt*32.. of row
+// group g of sequence b, once k_combine<true> has merged them.  That merge
+// leaves each (32-row tile, 32-dim tile mt)'s fp32 O in the slices of the
+// tile that splits s0 and s0+1 held (every lane's 16 values in the four
+// 16-byte chunks it read there).  Wave `sub` (lanes `lane`) takes d-tiles
+// 4*sub .. 4*sub+3; acc[4*i + qd] holds quad qd of d-tile 4*sub + i.  The
+// row amax spans all 512 dims, so the four waves of the rows share it
+// through LDS (amax_s: 1 KB).
 // ---------------------------------------------------------------------------
-__device__ void combine_rows_fused(const DecodeArgs& a, int b, int g, int wt, int sub, int lane,
-                             float (*amax_s)[64]) {
-  const int s0 = a.num_splits[b], ns = a.num_splits[b + 1] - s0;
-  if (ns <= 1) return;
-  const int half = lane >> 5, r32 = lane & 31;
-  const int row = g * kRowsPerWg + wt * 32 + r32;
-  const bool row_ok = row < a.rows;
-
-  // this lane's LSE of split s: lsep[s * lstride]
-  const int64_t lstride = (int64_t)a.groups * kPartialLseFloats;
-  const float* lsep = a.part_lse + (int64_t)s0 * lstride + (int64_t)g * kPartialLseFloats + wt * 32 + r32;
-  auto lse_of = [&](int s) -> float { return lsep[s * lstride]; };
-  auto load_split = [&](int s, uint4 (&v)[8]) {
-    const uint16_t* pb = a.part_o + ((int64_t)(s0 + s) * a.groups + g) * kPartialOElems +
-                         (size_t)wt * (16 * 2 * 64 * 8) + (size_t)((sub * 8) * 64 + lane) * 8;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const uint4*>(pb + k * 64 * 8);
-  };
-  // LSE = log sum_s exp(lse_s): running max and rescaled sum, eight splits'
-  // loads in flight at a time
-  // The first eight splits' LSEs and the first four splits' partials are
-  // loaded together (one round trip for the common case ns <= 4).
-  float l8[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) l8[i] = i < ns ? lse_of(i) : -INFINITY;
-  uint4 v[4][8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (j < ns) load_split(j, v[j]);
-  float m = -INFINITY, tot = 0.f;
-  for (int s = 0; s < ns; s += 8) {
-    float l[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) l[i] = s == 0 ? l8[i] : (s + i < ns ? lse_of(s + i) : -INFINITY);
-    float mc = m;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) mc = fmaxf(mc, l[i]);
-    if (mc != -INFINITY) {
-      float t = m == -INFINITY ? 0.f : tot * expf(m - mc);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) t += l[i] == -INFINITY ? 0.f : expf(l[i] - mc);
-      tot = t;
-      m = mc;
-    }
-  }
-  const float lse = m == -INFINITY ? -INFINITY : m + logf(tot);
-  // thread (sub, lane) owns d-tiles 4*sub .. 4*sub+3 of its row: acc[4*i + qd]
-  // holds quad qd of d-tile 4*sub + i (8 stored quad pairs)
-  f32x4 acc[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) acc[k] = f32x4{};
-  // O = sum_s exp(lse_s - LSE) O_s, four splits' partials in flight at a
-  // time (a split without keys for the row has lse_s = -inf and weight 0)
-  auto add_split = [&](const uint4 (&v)[8], float w) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t u[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-      // load k = (d-tile 4*sub + k/2, quad pair k%2); u[e] holds elements
-      // 2e, 2e+1 of the pair, i.e. quad 2*(k%2) + e/2, lanes (2e)%4, (2e+1)%4
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f32x4& t = acc[4 * (k >> 1) + 2 * (k & 1) + (e >> 1)];
-        t[(2 * e) & 3] += w * __uint_as_float(u[e] << 16);
-        t[(2 * e + 1) & 3] += w * __uint_as_float(u[e] & 0xffff0000u);
-      }
-    }
-  };
-  auto weight = [&](float l) { return l == -INFINITY ? 0.f : expf(l - lse); };
-  if (m != -INFINITY) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (j < ns) add_split(v[j], weight(l8[j]));
-    for (int s = 4; s < ns; s += 4) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (s + j < ns) load_split(s + j, v[j]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (s + j < ns) add_split(v[j], weight(s + j < 8 ? l8[s + j] : lse_of(s + j)));
-    }
-  }
-  const int64_t orow = (int64_t)b * a.rows + row;
-  {
-    // conjugate RoPE on dims 448..511 (sub 3 holds d-tiles 12..15)
-    const int Lb = a.seqlens[b];
-    const int tok = row_ok ? row / a.h_q : 0;
-    const double pos = (double)Lb - (double)a.s_q + (double)tok;
-    const RopeRow rr = rope_row(pos, row_ok, a.rope_log2_base, -1.0f);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int e = sub * 16 + k, mt = e >> 2, qd = e & 3;
-      if (mt < 14) continue;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const int k0 = 16 * (mt - 14) + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * half
-        float cs, sn;
-        rope_pair(rr, a.rope_log2_base, -1.0f, k0, k0 + 2, half, cs, sn);
-        const float x0 = acc[k][2 * pp], x1 = acc[k][2 * pp + 1];
-        acc[k][2 * pp] = x0 * cs - x1 * sn;
-        acc[k][2 * pp + 1] = x0 * sn + x1 * cs;
-      }
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(acc[k][e]));
-    amax = row_max2(amax);
-    amax_s[sub][lane] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(amax_s[0][lane], amax_s[1][lane]), fmaxf(amax_s[2][lane], amax_s[3][lane]));
-    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-    const float rs = amax > 0.f ? 448.0f / amax : 1.0f;
-    if (row_ok) {
-      uint8_t* op = reinterpret_cast<uint8_t*>(a.out) + orow * kDv;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int e = sub * 16 + k, mt = e >> 2, qd = e & 3;
-        const int d = 32 * mt + 8 * qd + 4 * half;
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = fminf(fmaxf(acc[k][i] * rs, -448.f), 448.f);
-        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], pk, true);
-        *reinterpret_cast<int*>(op + d) = pk;
-      }
-      if (half == 0 && sub == 0) {
-        a.lse[orow] = lse;
-        a.out_scale[orow] = sc;
-      }
-    }
-  }
+__device__ __forceinline__ float* merged_chunk(const DecodeArgs& a, int b, int g, int wt, int mt, int lane,
+                                               int k) {
+  // chunk k (0..3) of lane `lane`: split s0 + (k & 1), 16-byte chunk k >> 1
+  const int64_t pstride = (int64_t)a.groups * kPartialOElems;
+  uint16_t* pb = a.part_o + (int64_t)(a.num_splits[b] + (k & 1)) * pstride + (int64_t)g * kPartialOElems +
+                 (size_t)((wt * 16 + mt) * 2 + (k >> 1)) * 64 * 8 + (size_t)lane * 8;
+  return reinterpret_cast<float*>(pb);
 }
 
-// The fused combine as its own launch: one workgroup of four waves per
-// (sequence, row group, 32-row tile), which share the row amax.
-__global__ void __launch_bounds__(256) k_combine_fused(DecodeArgs a) {
+__global__ void __launch_bounds__(256) k_fused_epilogue(DecodeArgs a) {
   __shared__ float amax_s[4][64];
   const int wt = blockIdx.x & 3;
   const int g = (blockIdx.x >> 2) % a.groups;
   const int b = (blockIdx.x >> 2) / a.groups;
-  combine_rows_fused(a, b, g, wt, threadIdx.x >> 6, threadIdx.x & 63, amax_s);
+  const int sub = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int s0 = a.num_splits[b], ns = a.num_splits[b + 1] - s0;
+  if (ns <= 1) return;  // the decode wrote these rows itself (uniform over the workgroup)
+  const int half = lane >> 5, r32 = lane & 31;
+  const int row = g * kRowsPerWg + wt * 32 + r32;
+  const bool row_ok = row < a.rows;
+  f32x4 acc[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // the merge's chunk k holds its values 4k .. 4k+3, i.e. quad k of d-tile mt
+      const float4 v = *reinterpret_cast<const float4*>(merged_chunk(a, b, g, wt, 4 * sub + i, lane, k));
+      acc[4 * i + k] = f32x4{v.x, v.y, v.z, v.w};
+    }
+  const int64_t orow = (int64_t)b * a.rows + row;
+  // conjugate RoPE on dims 448..511 (sub 3 holds d-tiles 12..15)
+  const int Lb = a.seqlens[b];
+  const int tok = row_ok ? row / a.h_q : 0;
+  const double pos = (double)Lb - (double)a.s_q + (double)tok;
+  const RopeRow rr = rope_row(pos, row_ok, a.rope_log2_base, -1.0f);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int e = sub * 16 + k, mt = e >> 2, qd = e & 3;
+    if (mt < 14) continue;
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const int k0 = 16 * (mt - 14) + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * half
+      float cs, sn;
+      rope_pair(rr, a.rope_log2_base, -1.0f, k0, k0 + 2, half, cs, sn);
+      const float x0 = acc[k][2 * pp], x1 = acc[k][2 * pp + 1];
+      acc[k][2 * pp] = x0 * cs - x1 * sn;
+      acc[k][2 * pp + 1] = x0 * sn + x1 * cs;
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(acc[k][e]));
+  amax = row_max2(amax);
+  amax_s[sub][lane] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(amax_s[0][lane], amax_s[1][lane]), fmaxf(amax_s[2][lane], amax_s[3][lane]));
+  const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+  const float rs = amax > 0.f ? 448.0f / amax : 1.0f;
+  if (row_ok) {
+    uint8_t* op = reinterpret_cast<uint8_t*>(a.out) + orow * kDv;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int e = sub * 16 + k, mt = e >> 2, qd = e & 3;
+      const int d = 32 * mt + 8 * qd + 4 * half;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = fminf(fmaxf(acc[k][i] * rs, -448.f), 448.f);
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], pk, true);
+      *reinterpret_cast<int*>(op + d) = pk;
+    }
+    if (half == 0 && sub == 0) a.out_scale[orow] = sc;
+  }
 }
 
-// The plain combine: one 64-lane workgroup per (sequence b, row group g,
+// The combine: one 64-lane workgroup per (sequence b, row group g,
 // 32-row tile wt, 32-dim tile mt), so that even one sequence with many
 // splits spreads over many CUs.  Lane l takes the place of the decode's
 // lane l: row 32wt + l%32 and the 16 values of d-tile mt it held, two
 // 16-byte chunks per split (the partials are stored in that order).
 //   lse = ln sum_s e^{lse_s};  O = sum_s e^{lse_s - lse} O_s,
 // splits in ascending order, -inf partials with weight 0.
-__global__ void __launch_bounds__(64) k_combine_plain(DecodeArgs a) {
+// FP32OUT (the fused path's first launch) writes the merged fp32 values
+// over the tile's own slices of splits s0 and s0+1, which no other
+// workgroup reads (lane l rewrites exactly the four chunks it read there),
+// for k_fused_epilogue; the LSE is written either way.
+template <bool FP32OUT>
+__global__ void __launch_bounds__(64) k_combine(DecodeArgs a) {
   const int mt = blockIdx.x & 15, wt = (blockIdx.x >> 4) & 3;
   const int g = (blockIdx.x >> 6) % a.groups, b = (blockIdx.x >> 6) / a.groups;
   const int s0 = a.num_splits[b], ns = a.num_splits[b + 1] - s0;
@@ -1910,11 +1851,14 @@ __global__ void __launch_bounds__(64) k_combine_plain(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   if (m != -INFINITY) {
-    for (int s = 0; s < ns; s += 4) {
-      uint4 v[4][2];
-      float w[4];
+    // kInFlight splits' chunks in flight at a time: a sequence split over
+    // the whole machine (batch 1) has dozens of splits
+    constexpr int kInFlight = 8;
+    for (int s = 0; s < ns; s += kInFlight) {
+      uint4 v[kInFlight][2];
+      float w[kInFlight];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kInFlight; ++j) {
         const bool ok = s + j < ns;
         const float l = ok ? lsep[(s + j) * lstride] : -INFINITY;
         w[j] = l == -INFINITY ? 0.f : expf(l - lse);
@@ -1923,7 +1867,7 @@ __global__ void __launch_bounds__(64) k_combine_plain(DecodeArgs a) {
           v[j][q2] = ok ? *reinterpret_cast<const uint4*>(pb + (s + j) * pstride + q2 * 64 * 8) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kInFlight; ++j)
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
           const uint32_t u[4] = {v[j][q2].x, v[j][q2].y, v[j][q2].z, v[j][q2].w};
@@ -1935,7 +1879,15 @@ __global__ void __launch_bounds__(64) k_combine_plain(DecodeArgs a) {
         }
     }
   }
-  if (row < a.rows) {
+  if constexpr (FP32OUT) {
+    // chunk k (split s0 + (k & 1), 16-byte chunk k >> 1) takes values 4k .. 4k+3
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint16_t* dst = const_cast<uint16_t*>(pb) + (k & 1) * pstride + (k >> 1) * 64 * 8;
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]);
+    }
+    if (row < a.rows && mt == 0 && half == 0) a.lse[(int64_t)b * a.rows + row] = lse;
+  } else if (row < a.rows) {
     const int64_t orow = (int64_t)b * a.rows + row;
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + orow * kDv;
 #pragma unroll
@@ -2044,8 +1996,14 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool f
 hipError_t launch_combine(const DecodeArgs& a, bool fused, hipStream_t stream) {
   const int grid = a.batch * a.groups * 4;
   if (grid == 0) return hipSuccess;
-  if (fused) hipLaunchKernelGGL(k_combine_fused, dim3(grid), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(k_combine_plain, dim3(16 * grid), dim3(64), 0, stream, a);
+  if (fused) {
+    hipLaunchKernelGGL(k_combine<true>, dim3(16 * grid), dim3(64), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_fused_epilogue, dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(k_combine<false>, dim3(16 * grid), dim3(64), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
