@@ -70,9 +70,7 @@ WORKLOADS = ("dense_b64_h128_L1k-8k", "splitkv_b128_sq2_causal", "sparse_fp8_b64
 
 def make_workload(name):
     from mla_paged_kv_05_amd import workloads as W
-    return {"dense_b64_h128_L1k-8k": W.config2, "splitkv_b128_sq2_causal": W.config3,
-            "sparse_fp8_b64_top2048": W.config4, "fused_b32_h128": lambda: W.config5(32),
-            "fused_b1_h128": lambda: W.config5(1), "sparse_fp8v41_b64_top2048": W.config_v41}[name]()
+    return W.by_name(name)
 
 
 def traffic_record(kernel_src, workload):

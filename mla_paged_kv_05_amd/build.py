@@ -198,6 +198,34 @@ def build(strict: bool = False, verbose: bool = False) -> str:
     return LIB
 
 
+TRACE_LIB = os.path.join(HERE, "libmla_phase_trace.so")
+
+
+def build_phase_trace() -> str:
+    """The measurement library: the same sources with -DMLA_PHASE_TRACE, so
+    each decode workgroup records its phase timeline (read back by
+    mla_phase_trace_copy; see phase_trace.py).  Not the product library."""
+    build_dir = os.path.join(ROOT, "_build", "phase_trace")
+    os.makedirs(build_dir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(build_dir, src + ".o")
+        r = subprocess.run([HIPCC, *COMMON, "-DMLA_PHASE_TRACE", "-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc failed on {src} (phase trace build)")
+        objs.append(obj)
+    tmp = TRACE_LIB + f".tmp{os.getpid()}"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link failed (phase trace build)")
+    os.replace(tmp, TRACE_LIB)
+    return TRACE_LIB
+
+
 if __name__ == "__main__":
     build(strict="--strict" in sys.argv, verbose=True)
     print(LIB)

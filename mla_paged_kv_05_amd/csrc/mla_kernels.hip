@@ -41,6 +41,44 @@
 
 namespace mla {
 
+// ---------------------------------------------------------------------------
+// Phase timeline, compiled only into the measurement library that
+// build.build_phase_trace() makes (-DMLA_PHASE_TRACE); the product library
+// has none of it.  Lane 0 of wave 0 of each workgroup records the 100 MHz
+// s_memrealtime clock at kernel start, at each piece's start, after its
+// prologue, after its main loop and at its end (up to kTrPieces pieces), and
+// at kernel end, with vector stores into a static array that
+// mla_phase_trace_copy() returns.
+// ---------------------------------------------------------------------------
+#ifdef MLA_PHASE_TRACE
+constexpr int kTrPieces = 7, kTrPer = 32, kTrWgs = 4096;
+__device__ uint64_t g_phase_t[kTrWgs * kTrPer];
+__device__ int g_phase_items[kTrWgs * kTrPieces];
+#define MLA_TR_KERNEL_START const uint64_t tr_t0 = __builtin_amdgcn_s_memrealtime(); int tr_p = 0;
+#define MLA_TR_WG_ACTIVE \
+  if (threadIdx.x == 0 && blockIdx.x < kTrWgs) g_phase_t[blockIdx.x * kTrPer] = tr_t0;
+#define MLA_TR(k)                                                                              \
+  do {                                                                                         \
+    if (threadIdx.x == 0 && blockIdx.x < kTrWgs && tr_p < kTrPieces)                          \
+      g_phase_t[blockIdx.x * kTrPer + 4 * tr_p + (k)] = __builtin_amdgcn_s_memrealtime();    \
+  } while (0)
+#define MLA_TR_ITEMS(n)                                                                        \
+  do {                                                                                         \
+    if (threadIdx.x == 0 && blockIdx.x < kTrWgs && tr_p < kTrPieces)                          \
+      g_phase_items[blockIdx.x * kTrPieces + tr_p] = (n);                                      \
+  } while (0)
+#define MLA_TR_NEXT_PIECE ++tr_p;
+#define MLA_TR_KERNEL_END \
+  if (threadIdx.x == 0 && blockIdx.x < kTrWgs) g_phase_t[blockIdx.x * kTrPer + kTrPer - 1] = __builtin_amdgcn_s_memrealtime();
+#else
+#define MLA_TR_KERNEL_START
+#define MLA_TR_WG_ACTIVE
+#define MLA_TR(k) do {} while (0)
+#define MLA_TR_ITEMS(n) do {} while (0)
+#define MLA_TR_NEXT_PIECE
+#define MLA_TR_KERNEL_END
+#endif
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -828,6 +866,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int KVF, bool SPARSE, bool FUSED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_decode(DecodeArgs a) {
+  MLA_TR_KERNEL_START
   using Lay = DecodeLayout<KVF, SPARSE, FUSED>;
   // The fused path runs both products on fp16 operands: q-hat is formed in
   // fp32 and rounded once, to fp16 (3 more bits than bf16), so QK^T meets
@@ -861,6 +900,7 @@ k_decode(DecodeArgs a) {
   const int32_t* ms = a.meta + 8 * slot;
   const int b0 = uni(sload(ms, 0));
   if (b0 < 0) return;  // no work in this slot
+  MLA_TR_WG_ACTIVE
   const int j0 = uni(sload(ms, 1)), b1 = uni(sload(ms, 2)), j1 = uni(sload(ms, 3)),
             nitems = uni(sload(ms, 5));
   int split_k = uni(sload(ms, 4));
@@ -1069,6 +1109,7 @@ k_decode(DecodeArgs a) {
   int cb = b0, cj = j0, step = 0;
   while (step < nsteps) {
     // ======== one piece: sequence cb, items cj .. piece_end-1
+    MLA_TR(1);
     const int Lb = uni(sload(a.seqlens, cb));
     const int piece_end = item_end(cb);
     float m_used = -INFINITY, lsum = 0.f;
@@ -1197,6 +1238,7 @@ k_decode(DecodeArgs a) {
     wait_vmcnt<0>();
     lds_barrier();  // every wave's loads of the piece's first step (and Q in LDS) landed
     first_piece = false;
+    MLA_TR(2);
 
     // ======== building blocks of one 32-key step
     auto tile_off = [&](int st) -> int {
@@ -1597,6 +1639,8 @@ k_decode(DecodeArgs a) {
       }
     }
 
+    MLA_TR(3);
+    MLA_TR_ITEMS(piece_end - cj);
     // ======== finalize the piece: O / l and LSE; direct output or partial
     o_settle(o);
     {
@@ -1711,12 +1755,15 @@ k_decode(DecodeArgs a) {
                                                 (wave * 32 + r32) * 4, 0, kPastL2);
       }
     }
+    MLA_TR(4);
+    MLA_TR_NEXT_PIECE
     // next piece: first item of the following sequence
     cb = uni(cb + 1);
     cj = 0;
     split_k = 0;
   }
   wait_vmcnt<0>();  // no tile load (zeros past the end) outlives the workgroup's LDS
+  MLA_TR_KERNEL_END
 }
 
 // ---------------------------------------------------------------------------
@@ -2049,3 +2096,22 @@ hipError_t noalloc_scratch(void** ptr) {
 }
 
 }  // namespace mla
+
+#ifdef MLA_PHASE_TRACE
+// Measurement library only: the phase timeline of the last decode launches
+// (see the phase-timeline note at the top of this file).
+extern "C" int mla_phase_trace_copy(void* times, void* items, int nwg) {
+  if (nwg < 0 || nwg > mla::kTrWgs) return -1;
+  if (hipMemcpyFromSymbol(times, HIP_SYMBOL(mla::g_phase_t), sizeof(uint64_t) * mla::kTrPer * nwg) != hipSuccess)
+    return -2;
+  if (hipMemcpyFromSymbol(items, HIP_SYMBOL(mla::g_phase_items), sizeof(int) * mla::kTrPieces * nwg) != hipSuccess)
+    return -3;
+  return 0;
+}
+extern "C" int mla_phase_trace_clear(void) {
+  static uint64_t zt[mla::kTrWgs * mla::kTrPer];
+  static int zi[mla::kTrWgs * mla::kTrPieces];
+  if (hipMemcpyToSymbol(HIP_SYMBOL(mla::g_phase_t), zt, sizeof zt) != hipSuccess) return -1;
+  return hipMemcpyToSymbol(HIP_SYMBOL(mla::g_phase_items), zi, sizeof zi) == hipSuccess ? 0 : -2;
+}
+#endif

@@ -332,3 +332,18 @@ def config5(batch=32, seed=None) -> Problem:
     seqlens = rng.integers(2048, 16384 + 1, size=batch).astype(np.int32)
     return _dense_from_lengths(f"fused_b{batch}_h128", rng, seqlens, 1, 128, False, 1.2, True,
                                None, 0)
+
+
+# The standard workloads by the names bench.py and the profiles use.
+WORKLOADS = {
+    "dense_b64_h128_L1k-8k": config2,
+    "splitkv_b128_sq2_causal": config3,
+    "sparse_fp8_b64_top2048": config4,
+    "fused_b32_h128": lambda: config5(32),
+    "fused_b1_h128": lambda: config5(1),
+    "sparse_fp8v41_b64_top2048": config_v41,
+}
+
+
+def by_name(name: str) -> Problem:
+    return WORKLOADS[name]()
