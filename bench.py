@@ -85,15 +85,47 @@ def traffic_record(kernel_src, workload):
     return rec if rec.get("kernel_sha") == h and rec.get("workload") == workload else None
 
 
-def cpu_baseline(p, nbytes):
+def measured_peaks(dev):
+    """The box's own ceilings, a second denominator beside the published
+    peaks: a 1 GiB device-to-device copy (bytes read + written per second)
+    and a large bf16 GEMM on the vendor library (flop/s), best of 5 each."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    c = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
+
+    def best(fn):
+        ts = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts[1:])
+    copy_s = best(lambda: dst.copy_(src))
+    gemm_s = best(lambda: torch.mm(a, b, out=c))
+    del src, dst, a, b, c
+    return {"copy_gbs": round(2 * n / copy_s / 1e9, 1), "gemm_bf16_tflops": round(2 * 8192 ** 3 / gemm_s / 1e12, 1),
+            "copy": "1 GiB device-to-device copy, read + written bytes", "gemm": "8192^3 bf16 torch.mm"}
+
+
+def cpu_baseline(p, nbytes, flops):
     import oracle
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    oracle.decode(p, nthreads=cores)
-    dt = time.perf_counter() - t0
+    runs = []
+    for _ in range(3):  # the median of three runs
+        t0 = time.perf_counter()
+        oracle.decode(p, nthreads=cores)
+        runs.append(time.perf_counter() - t0)
+    dt = float(np.median(runs))
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -104,8 +136,8 @@ def cpu_baseline(p, nbytes):
     except OSError:
         pass
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"whole workload ({p.batch} sequences), fp64, {dt:.2f} s",
-            "seconds": round(dt, 3), "cpu_model": model, "threads": cores,
+            "sample": f"whole workload ({p.batch} sequences), fp64, median of 3 runs, {dt:.2f} s",
+            "seconds": round(dt, 3), "gflops": round(flops / dt / 1e9, 2), "cpu_model": model, "threads": cores,
             "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
 
 
@@ -338,9 +370,14 @@ def main():
             "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
             "mfma_tflops": round(mfma_tflops, 1), "mfma_frac": round(mfma_tflops / BF16_PEAK_TFLOPS, 4)}),
     }
+    # the box's own ceilings beside the published peaks (outside the timed region)
+    pk = measured_peaks(dev)
+    pk["hbm_frac_of_copy"] = round(hbm_gbs / pk["copy_gbs"], 4)
+    pk["mfma_frac_of_gemm"] = round(mfma_tflops / pk["gemm_bf16_tflops"], 4)
+    res["roofline"]["measured_peaks"] = pk
     if not args.no_cpu:
         log("timing the CPU oracle on the same workload ...")
-        res["cpu_baseline"] = cpu_baseline(p, nbytes)
+        res["cpu_baseline"] = cpu_baseline(p, nbytes, flops)
     print(json.dumps(res), flush=True)
 
 
