@@ -30,6 +30,16 @@
 //    when a new block max exceeds it by more than 2^8, so the 256-register
 //    O accumulator is almost never rescaled ("skip scale", AI Wiki, section
 //    "The Ascend kernel deep-dive"); exact up to rounding.
+//  * The fused variant (q RMSNorm + RoPE in the piece prologue, conjugate
+//    RoPE + amax + e4m3 cast in the epilogue, "FlashMLA fused norm-RoPE-
+//    attention-RoPE-cast kernel" card) runs both products on fp16 operands
+//    (v_mfma_f32_32x32x16_f16): q-hat is rounded once to fp16, each wave
+//    converts the bf16 rows it staged to fp16 in place, FP8 codes
+//    dequantise to fp16 exactly.
+//  * Split rows: the decode stores bf16 partial O and fp32 partial LSE; the
+//    combine (k_combine) merges them on one 64-lane workgroup per 32x32 tile
+//    of O; in the fused path it leaves fp32 tiles that k_fused_epilogue
+//    turns into the rotated, scaled e4m3 output.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 #include <cstdint>
