@@ -167,10 +167,12 @@ typedef struct mla_decode_params {
  * entry outside [0, num_blocks) names no page: its 64 positions stay
  * visible and read as all-zero keys (score 0), and so do positions past
  * max_blocks_per_seq pages.  Entries past ceil(len/64) are never read.
- * Fused arithmetic: q-hat is rounded to fp16 and both products run on fp16
- * operands (bf16 KV and e4m3 codes convert exactly), so the fused path
- * needs |K|, |q-hat| and, over an FP8 cache, |P * tile scale| below 65504;
- * magnitudes under 2^-14 keep 2^-24 absolute resolution.
+ * 16-bit arithmetic: the fused path and every decode over a V3.2 FP8 cache
+ * run both products on fp16 operands.  Fused: q-hat is rounded once to
+ * fp16, bf16 KV converts exactly.  V3.2 FP8: each key value is
+ * fp16(fp32(code) * fp32 scale), rounded once; q converts exactly.  These
+ * paths need |q|, |q-hat| and |K| below 65504; magnitudes under 2^-14
+ * keep 2^-24 absolute resolution.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP (launch failure). */
 mla_status mla_decode(const mla_decode_params* params, void* stream);
 
@@ -210,10 +212,12 @@ mla_status mla_decode_noalloc(const mla_decode_params* params, void* stream);
  * stream.  Errors as mla_decode. */
 mla_status mla_combine(const mla_decode_params* params, void* stream);
 
-/* Test hook: the 64 x 576 bf16 tile the KV loader stages for work item j
- * of sequence b (query token t when sparse), written un-swizzled to
- * dst [64][576] bf16: gathered rows, dequantised when FP8, zero rows past
- * the sequence or for -1 indices.  Not available for MLA_KV_FP8_V41
+/* Test hook: the 64 x 576 tile of 16-bit values the KV loader stages for
+ * work item j of sequence b (query token t when sparse), written
+ * un-swizzled to dst [64][576]: the bf16 rows of a bf16 cache; for a V3.2
+ * FP8 cache the fp16 rows both products read, fp16(fp32(code) * fp32
+ * scale) for dims < 512 and the bf16 RoPE dims in fp16; zero rows past the
+ * sequence or for -1 indices.  Not available for MLA_KV_FP8_V41
  * (MLA_ERR_UNSUPPORTED). */
 mla_status mla_debug_gather(const mla_decode_params* params, int32_t b, int32_t t, int32_t j,
                             void* dst, void* stream);

@@ -33,9 +33,12 @@
 //  * The fused variant (q RMSNorm + RoPE in the piece prologue, conjugate
 //    RoPE + amax + e4m3 cast in the epilogue, "FlashMLA fused norm-RoPE-
 //    attention-RoPE-cast kernel" card) runs both products on fp16 operands
-//    (v_mfma_f32_32x32x16_f16): q-hat is rounded once to fp16, each wave
-//    converts the bf16 rows it staged to fp16 in place, FP8 codes
-//    dequantise to fp16 exactly.
+//    (v_mfma_f32_32x32x16_f16): q-hat is rounded once to fp16, and each
+//    wave converts the bf16 rows it staged to fp16 in place.
+//  * FP8 caches: V3.2 records (e4m3 codes with an fp32 scale per 128 dims)
+//    dequantise to fp16 tiles, code * scale rounded once, and run on fp16
+//    MFMA with q converted to fp16; V4.1 records (power-of-two scales)
+//    dequantise exactly to bf16.
 //  * Split rows: the decode stores bf16 partial O and fp32 partial LSE; the
 //    combine (k_combine) merges them on one 64-lane workgroup per 32x32 tile
 //    of O; in the fused path it leaves fp32 tiles that k_fused_epilogue
@@ -560,20 +563,7 @@ __device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t
 // Scales of an FP8 half tile in LDS, in the register order of the S^T
 // accumulator: [tile t][lane half h][i] holds the scale of dims 128t.. of
 // key key_of_row(8*(i/4) + i%4) + h.
-constexpr int kScaleBytes = 4 * 2 * 16 * 4;
-__device__ __forceinline__ int scale_slot(int key) {  // key -> h*16 + i
-  const int h = key & 1, kc = key - h, rem = kc & 15;
-  return h * 16 + 8 * (kc >> 4) + 4 * ((rem >> 1) & 1) + (rem >> 2);
-}
 
-// 32 raw records -> the half tile with the e4m3 codes of dims < 512
-// converted exactly (every e4m3 value is a bf16 value and an fp16 value),
-// dims 512..575 copied (bf16) or converted to fp16 (F16: exact for
-// magnitudes in [2^-14, 65504], 2^-24 absolute resolution below), and the
-// fp32 tile scales moved to `scl`.  The decode applies the scales in
-// fp32: to each tile's partial scores in QK^T and to P in P.V, so no product
-// code*scale is ever rounded to 16 bits.  An all-zero record gives a zero row
-// with zero scales.
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // Two bf16 values -> two fp16 values, round to nearest even (one
@@ -604,48 +594,50 @@ __device__ __forceinline__ void own_chunks_to_f16(uint8_t* slot, int wave) {
     *reinterpret_cast<uint4*>(slot + off + l16) = bf16x8_to_f16x8(v[k]);
   }
 }
-template <bool F16>
-__device__ __forceinline__ void dequant_codes(uint8_t* tile, float* scl, const uint8_t* raw, int tid) {
+// 32 raw V3.2 records -> the fp16 half tile both products read: dims < 512
+// as fp16(fp32(code) * scale) (the e4m3 code widened exactly to fp32, one
+// fp32 product with the record's fp32 scale of that 128-dim block, rounded
+// once to fp16 (relative error below 2^-11); the hardware's scaled
+// conversion uses only the scale's exponent, so the product is formed
+// here), dims 512..575 converted from bf16 (exact for magnitudes in
+// [2^-14, 65504]).  An all-zero record gives a zero row.  Used by the
+// decode and, unchanged, by the gather test hook.
+__device__ __forceinline__ void dequant_codes(uint8_t* tile, const uint8_t* raw, int tid) {
   tid = (tid & ~63) | fresh_lane();  // keep the per-thread addresses out of the loop's live set
-  // All code reads first, then the conversions and writes: the compiler
-  // cannot move a read of the raw slot above a write to the tile (same LDS
-  // array), so interleaved they would each wait out a full LDS latency.
+  // All code and scale reads first, then the conversions and writes: the
+  // compiler cannot move a read of the raw slot above a write to the tile
+  // (same LDS array), so interleaved they would each wait out an LDS latency.
   constexpr int kPer = kHalfRows * 64 / kThreads;
+  const int blk = (tid & 63) >> 4;  // chunk k = kk*256 + tid: every one in 128-dim block blk
   uint2 codes[kPer];
+  float scl[kPer];
 #pragma unroll
   for (int kk = 0; kk < kPer; ++kk) {
     const int k = kk * kThreads + tid;
-    codes[kk] = *reinterpret_cast<const uint2*>(raw + (k >> 6) * kFp8TokenBytes + (k & 63) * 8);
+    const uint8_t* rec = raw + (k >> 6) * kFp8TokenBytes;
+    codes[kk] = *reinterpret_cast<const uint2*>(rec + (k & 63) * 8);
+    scl[kk] = *reinterpret_cast<const float*>(rec + 512 + 4 * blk);
   }
   uint4 rope = *reinterpret_cast<const uint4*>(raw + (tid >> 3) * kFp8TokenBytes + 528 + (tid & 7) * 16);
 #pragma unroll
   for (int kk = 0; kk < kPer; ++kk) {
     const int k = kk * kThreads + tid;
     const int r = k >> 6, c = k & 63;
-    const uint2 code = codes[kk];
-    const uint32_t cw[2] = {code.x, code.y};
+    const uint32_t cw[2] = {codes[kk].x, codes[kk].y};
+    const float sc = scl[kk];
     uint32_t w[4];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      // two codes -> two 16-bit values in one instruction; with scale 1 exact
-      if constexpr (F16) {
-        w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[hh], 1.0f, false));
-        w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[hh], 1.0f, true));
-      } else {
-        w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], 1.0f, false));
-        w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], 1.0f, true));
-      }
+      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], false);
+      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], true);
+      w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo * sc, f16x2_t));
+      w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi * sc, f16x2_t));
     }
     *reinterpret_cast<uint4*>(tile + r * kMainStride + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
   {
     const int r = tid >> 3, c = tid & 7;
-    if constexpr (F16) rope = bf16x8_to_f16x8(rope);
-    *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = rope;
-  }
-  if (tid < 4 * kHalfRows) {
-    const int r = tid >> 2, t = tid & 3;
-    scl[t * 32 + scale_slot(r)] = *reinterpret_cast<const float*>(raw + r * kFp8TokenBytes + 512 + 4 * t);
+    *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = bf16x8_to_f16x8(rope);
   }
 }
 
@@ -708,42 +700,6 @@ __device__ __forceinline__ void v41_write(uint8_t* tile, int wave_base, int kk, 
     w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], scale, true));
   }
   *reinterpret_cast<uint4*>(tile + (k >> 6) * kMainStride + (k & 63) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// Dequantise 32 raw records into the bf16 half tile: dims < 512 are
-// e4m3 * fp32 tile scale computed in fp32 and rounded once to bf16 (RNE);
-// dims 512..575 are copied.  An all-zero record gives a zero row.  (The
-// staged rows as the cache defines them; the decode itself keeps the codes
-// and the scales apart, see dequant_codes.)
-__device__ __forceinline__ void dequant_half_scaled(uint8_t* tile, const uint8_t* raw, int tid) {
-#pragma unroll
-  for (int kk = 0; kk < kHalfRows * 64 / kThreads; ++kk) {
-    const int k = kk * kThreads + tid;
-    const int r = k >> 6, c = k & 63;
-    const uint8_t* rec = raw + r * kFp8TokenBytes;
-    const uint2 code = *reinterpret_cast<const uint2*>(rec + c * 8);
-    const float sc = *reinterpret_cast<const float*>(rec + 512 + (c >> 4) * 4);
-    const uint32_t cw[2] = {code.x, code.y};
-    uint32_t w[4];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      typedef __attribute__((ext_vector_type(2))) float f2;
-      f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], false);
-      f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], true);
-      __bf16 b0 = (__bf16)(lo[0] * sc), b1 = (__bf16)(lo[1] * sc);
-      __bf16 b2 = (__bf16)(hi[0] * sc), b3 = (__bf16)(hi[1] * sc);
-      w[2 * hh] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-      w[2 * hh + 1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-    }
-    *reinterpret_cast<uint4*>(tile + r * kMainStride + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  {
-    const int r = tid >> 3, c = tid & 7;
-    const uint4 v = *reinterpret_cast<const uint4*>(raw + r * kFp8TokenBytes + 528 + c * 16);
-    *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = v;
-  }
 }
 
 // The 32 sparse ids of half `h` of work item j of (sequence b, query token
@@ -853,7 +809,7 @@ struct DecodeLayout {
   static constexpr int kIdsOff = kQOff + kWaves * q_lds_wave_bytes<KVF, FUSED>();
   static constexpr int kWalkOff = kIdsOff + (SPARSE ? ids_slots<KVF>() * 256 : 0);  // 2 words per wave
   static constexpr int kSclOff = kWalkOff + (KVF == kKvBf16 && !SPARSE ? kWaves * 8 : 0);
-  static constexpr int kWOff = kSclOff + (KVF == kKvFp8V32 ? kScaleBytes : 0);  // fused: norm weight row
+  static constexpr int kWOff = kSclOff;  // fused: norm weight row
   static constexpr int kSmem = kWOff + (FUSED ? kDqk * 2 : 0);
   // per-step VMEM instructions issued by every wave (loads + id fetch)
   static constexpr int kVmPerStep =
@@ -882,7 +838,7 @@ k_decode(DecodeArgs a) {
   // fp32 and rounded once, to fp16 (3 more bits than bf16), so QK^T meets
   // the LSE bar even on rows of a few keys; bf16 K/V and e4m3 codes convert
   // to fp16 exactly, and P keeps 3 more bits too.
-  constexpr bool kF16 = FUSED;
+  constexpr bool kF16 = FUSED || KVF == kKvFp8V32;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Lay::kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
@@ -1153,7 +1109,13 @@ k_decode(DecodeArgs a) {
       };
       if constexpr (!FUSED) {
 #pragma unroll
-        for (int ks = 0; ks < ksteps<KVF>(); ++ks) put_q(ks, *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8));
+        for (int ks = 0; ks < ksteps<KVF>(); ++ks) {
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
+          // fp16 products (the V3.2 FP8 cache): bf16 q converts exactly
+          // (magnitudes in [2^-14, 65504])
+          if constexpr (kF16) put_q(ks, __builtin_bit_cast(bf16x8, bf16x8_to_f16x8(__builtin_bit_cast(uint4, v))));
+          else put_q(ks, v);
+        }
       } else {
         // Fused prologue: q-hat = inv * RoPE(q (.) w), inv = 1/sqrt(mean(q^2)
         // + eps) over the row's 576 dims (RMSNorm, then RoPE on dims
@@ -1326,128 +1288,6 @@ k_decode(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // FP8: S^T from the exact codes, one 128-dim tile at a time, each tile's
-    // partial scores scaled by its per-key fp32 scale before they are summed;
-    // the RoPE block (bf16 in the cache) adds unscaled.
-    const float* scl = reinterpret_cast<const float*>(smem + Lay::kSclOff);
-    auto qk_fp8 = [&](int tb, f32x16& sc) {
-      constexpr int kLa = 2;  // the tile accumulator costs 16 VGPRs: shorter lookahead
-      const int ln = fresh_lane(), lr = ln & 31, lh = ln >> 5;
-      const int lkey = key_of_row(lr), lfr = (lkey >> 1) & 7, lx = (lr >> 1) & 7;
-      const int koff = tb + lkey * kMainStride + 16 * lh;
-      const int kroff = tb + kRopeOff + lkey * kRopeStride;
-      const int qb = Lay::kQOff + wave * q_lds_wave_bytes<KVF, FUSED>() + lr * q_lds_row_bytes<KVF, FUSED>();
-      int qoff[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qoff[e] = qb + ((((2 * e) | lh) ^ lx) << 4);
-      auto read_k = [&](int ks) {
-        if (ks < 32) return *reinterpret_cast<const bf16x8*>(smem + koff + 32 * ks);
-        return *reinterpret_cast<const bf16x8*>(smem + kroff + ((((2 * (ks - 32)) | lh) ^ lfr) << 4));
-      };
-      auto read_q = [&](int ks) {
-        return *reinterpret_cast<const bf16x8*>(smem + qoff[(ks - kQRegStepsFp8) & 3] +
-                                                ((ks - kQRegStepsFp8) >> 2) * 128);
-      };
-      const f32x4* sv = reinterpret_cast<const f32x4*>(scl + lh * 16);
-      bf16x8 kbuf[kLa], qbuf[kLa];
-      // Two partial accumulators alternate between the 128-dim tiles: tile
-      // t's fold (sc += part * scale) runs between the first MFMAs of tile
-      // t+1, so the MFMA pipe does not wait for it.  Fold of tile tp: settle
-      // and scale reads after MFMA 8(tp+1), quarter q after MFMA 8(tp+1)+1+q
-      // (tile 3's last quarter after the loop).  The RoPE tile (ks 32..35)
-      // adds unscaled at the end.
-      f32x16 part[2];
-      f32x4 s4[4];
-      auto fold_quarter = [&](int tp, int q) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sc[4 * q + e] = (tp == 0 ? 0.f : sc[4 * q + e]) + part[tp & 1][4 * q + e] * s4[q][e];
-      };
-#pragma unroll
-      for (int i = 0; i < kLa; ++i) kbuf[i] = read_k(i);
-#pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
-        const bf16x8 ka = kbuf[ks % kLa];
-        const bf16x8 qb = ks < kQR ? qf[ks < kQR ? ks : 0] : qbuf[ks % kLa];
-        if (ks + kLa < 36) {
-          kbuf[ks % kLa] = read_k(ks + kLa);
-          if (ks + kLa >= kQRegStepsFp8) qbuf[ks % kLa] = read_q(ks + kLa);
-        }
-        const int t = ks >> 3, u = ks & 7;
-        if (u == 0) mfma_s_first<kF16>(part[t & 1], ka, qb);
-        else mfma_s_acc<kF16>(part[t & 1], ka, qb);
-        if (t >= 1) {
-          const int tp = t - 1;
-          if (u == 0) {
-            mfma_s_settle(part[tp & 1]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) s4[q] = sv[tp * 8 + q];
-          } else if (u <= 4) {
-            fold_quarter(tp, u - 1);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      fold_quarter(3, 3);
-      mfma_s_settle(part[0]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] += part[0][i];
-    };
-    // FP8: O^T += V^T P_t^T where V holds the exact codes and P_t = p * the
-    // keys' scale of tile t (d-tiles 4t..4t+3), rounded once to bf16.
-    auto pv_fp8 = [&](int tb, const f32x16& p) {
-      const int ln = fresh_lane(), lh = ln >> 5;
-      const f32x4* sv = reinterpret_cast<const f32x4*>(scl + lh * 16);
-      constexpr int kVa = 2;
-      const int voff = tb + (4 * ((ln & 15) >> 2) + lh) * kMainStride + 32 * ((ln >> 4) & 1) + 8 * (ln & 3);
-      auto read_v = [&](int i) {  // i = kq * 16 + mt
-        const int kq = i >> 4, mt = i & 15;
-        const uint8_t* pp = smem + voff + kq * 16 * kMainStride + mt * 64;
-        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(pp));
-        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(pp + 2 * kMainStride));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      // mt order: the four d-tiles of one scale tile, both key halves; one
-      // stream of 32 MFMAs, i = 8t + j.  The V reads run kVa MFMAs ahead
-      // across tile boundaries.  Tile t+1's scaled P goes to the other half
-      // of pt while tile t's MFMAs run: scale reads after MFMA j = 0, one
-      // quarter after each of MFMAs 3..6 (three MFMAs after the last read of
-      // that half by tile t-1), settled after MFMA 7.
-      auto scale_p = [&](bf16x8 (&dst)[2], int q, const f32x4& s4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[q >> 1][4 * (q & 1) + e] = to_op16<kF16>(p[4 * q + e] * s4[e]);
-      };
-      auto v_index = [](int i) { return ((i & 7) >> 2) * 16 + 4 * (i >> 3) + (i & 3); };  // kq * 16 + mt
-      bf16x8 pt[2][2];
-      f32x4 s4[4];
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int q = 0; q < 4; ++q) scale_p(pt[0], q, sv[q]);
-      valu_to_mfma_settle(pt[0][0], pt[0][1]);
-      bf16x8 vbuf[kVa];
-#pragma unroll
-      for (int i = 0; i < kVa; ++i) vbuf[i] = read_v(v_index(i));
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int t = i >> 3, j = i & 7;
-        const bf16x8 va = vbuf[i % kVa];
-        if (i + kVa < 32) vbuf[i % kVa] = read_v(v_index(i + kVa));
-        mfma_o<kF16>(o[4 * t + (j & 3)], va, pt[t & 1][j >> 2]);
-        if (t + 1 < 4) {
-          if (j == 0) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) s4[q] = sv[(t + 1) * 8 + q];
-          } else if (j >= 3 && j <= 6) {
-            scale_p(pt[(t + 1) & 1], j - 3, s4[j - 3]);
-          } else if (j == 7) {
-            valu_to_mfma_settle(pt[(t + 1) & 1][0], pt[(t + 1) & 1][1]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
     auto key0_of = [&](int ps) { return (cj + (ps >> 1)) * kPage + (ps & 1) * kHalfRows; };
     auto has_keys = [&](int ps) {
       const int k0 = key0_of(ps);
@@ -1516,7 +1356,6 @@ k_decode(DecodeArgs a) {
           const float p = __builtin_amdgcn_exp2f(sc[i] - st.mref);
           st.psum += p;
           st.pf[i >> 3][i & 7] = to_op16<kF16>(p);
-          if constexpr (KVF != kKvBf16) sc[i] = p;
         }
       } else {
         lsum = lsum * st.alpha + st.psum;
@@ -1618,7 +1457,8 @@ k_decode(DecodeArgs a) {
         }
       }
     } else {
-      // ---- FP8: one bf16 tile, dequantised from the raw ring each step
+      // ---- FP8 V3.2: one fp16 tile (code times scale, rounded once),
+      // dequantised from the raw ring each step; S^T and P.V as on bf16 KV
       for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
         if (ps > 0) {
           // This step's loads were issued two steps ago; the previous step
@@ -1630,13 +1470,12 @@ k_decode(DecodeArgs a) {
           else wait_vmcnt<Lay::kVmPerStep>();
           lds_barrier();  // every wave's loads of this step landed
         }
-        dequant_codes<kF16>(smem + Lay::kTileOff, reinterpret_cast<float*>(smem + Lay::kSclOff),
-                      smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
+        dequant_codes(smem + Lay::kTileOff, smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
         lds_barrier();  // the tile is staged; raw slot (step+2)%3 (dequantised last step) is free
         const bool hk = has_keys(ps);
         f32x16 sc;
         SmState st;
-        if (hk) qk_fp8(tile_off(step), sc);
+        if (hk) qk(tile_off(step), sc, [](int) {});
         // The loads of step+2 go out after S^T: the register reloads inside
         // S^T wait for every older load, and would otherwise wait for these.
         issue_next(step);
@@ -1644,7 +1483,8 @@ k_decode(DecodeArgs a) {
 #pragma unroll
           for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc, st, key0_of(ps), step);
           rescale_o(st);
-          pv_fp8(tile_off(step), sc);
+          valu_to_mfma_settle(st.pf[0], st.pf[1]);
+          pv(tile_off(step), st.pf);
         }
       }
     }
@@ -1994,7 +1834,7 @@ __global__ void __launch_bounds__(kThreads) k_debug_gather(DecodeArgs a, int b, 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if constexpr (KVF != kKvBf16) {
-      dequant_half_scaled(tile, raw, tid);
+      dequant_codes(tile, raw, tid);
       __syncthreads();
     }
     for (int k = tid; k < kHalfRows * kChunksPerRow; k += kThreads) {

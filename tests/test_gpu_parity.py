@@ -156,13 +156,6 @@ def test_metadata_bit_exact():
         assert np.array_equal(ns.cpu().numpy(), rn)
 
 
-def _bf16_round_f32(x):
-    """fp64 -> fp32 (RNE) -> bf16 (RNE), as the dequantiser rounds."""
-    import torch
-    return torch.from_numpy(np.asarray(x, dtype=np.float64).astype(np.float32)).to(torch.bfloat16).view(
-        torch.int16).numpy().view(np.uint16)
-
-
 @gpu
 def test_gather_bit_exact():
     torch = _torch_cuda()
@@ -180,7 +173,8 @@ def test_gather_bit_exact():
         exp = np.zeros((64, 576), dtype=np.uint16)
         exp[:n] = p.kv[p.block_table[b, j], :n]
         assert np.array_equal(g, exp)
-    # sparse fp8: dequantised rows = bf16(fp32(code) * fp32 scale), zero for -1 / past topk
+    # sparse fp8: the fp16 tile the decode stages, fp16(fp32(code) * fp32 scale) and the
+    # bf16 RoPE dims in fp16, zero for -1 / past topk
     p = W.make_sparse_fp8("gf", batch=2, s_q=1, h_q=128, cache_len=256, topk=100, seed=17, pad_frac=0.5)
     t = upload(p)
     meta, ns = mla.get_mla_metadata(t["seqlens"], 128, 1, topk=100)
@@ -199,8 +193,9 @@ def test_gather_bit_exact():
             sc = np.frombuffer(rec[512:528].tobytes(), dtype=np.float32)
             codes = torch.from_numpy(rec[:512].copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
             prod = (codes * np.repeat(sc, 128)).astype(np.float32)  # fp32 product, RNE
-            exp[r, :512] = _bf16_round_f32(prod)
-            exp[r, 512:] = np.frombuffer(rec[528:].tobytes(), dtype=np.uint16)
+            exp[r, :512] = prod.astype(np.float16).view(np.uint16)  # then RNE to fp16
+            rope = (np.frombuffer(rec[528:].tobytes(), dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+            exp[r, 512:] = rope.astype(np.float16).view(np.uint16)
         assert np.array_equal(g, exp)
 
 
