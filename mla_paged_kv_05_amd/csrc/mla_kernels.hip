@@ -602,6 +602,18 @@ __device__ __forceinline__ void own_chunks_to_f16(uint8_t* slot, int wave) {
 // here), dims 512..575 converted from bf16 (exact for magnitudes in
 // [2^-14, 65504]).  An all-zero record gives a zero row.  Used by the
 // decode and, unchanged, by the gather test hook.
+__device__ __forceinline__ uint4 codes_to_f16x8(uint32_t c0, uint32_t c1, float sc) {
+  const uint32_t cw[2] = {c0, c1};
+  uint32_t w[4];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], true);
+    w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo * sc, f16x2_t));
+    w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi * sc, f16x2_t));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
 __device__ __forceinline__ void dequant_codes(uint8_t* tile, const uint8_t* raw, int tid) {
   tid = (tid & ~63) | fresh_lane();  // keep the per-thread addresses out of the loop's live set
   // All code and scale reads first, then the conversions and writes: the
@@ -622,22 +634,40 @@ __device__ __forceinline__ void dequant_codes(uint8_t* tile, const uint8_t* raw,
 #pragma unroll
   for (int kk = 0; kk < kPer; ++kk) {
     const int k = kk * kThreads + tid;
-    const int r = k >> 6, c = k & 63;
-    const uint32_t cw[2] = {codes[kk].x, codes[kk].y};
-    const float sc = scl[kk];
-    uint32_t w[4];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], false);
-      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[hh], true);
-      w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo * sc, f16x2_t));
-      w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi * sc, f16x2_t));
-    }
-    *reinterpret_cast<uint4*>(tile + r * kMainStride + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(tile + (k >> 6) * kMainStride + (k & 63) * 16) =
+        codes_to_f16x8(codes[kk].x, codes[kk].y, scl[kk]);
   }
   {
     const int r = tid >> 3, c = tid & 7;
     *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = bf16x8_to_f16x8(rope);
+  }
+}
+
+// The same conversion one chunk at a time, for spreading it between the
+// MFMAs of another step's S^T: chunk kk < 8 is 8 codes of a record and
+// their block scale (the dequant_codes loop's chunk kk), chunk 8 the 8 RoPE
+// dims this thread converts.
+constexpr int kV32Chunks = kHalfRows * 64 / kThreads + 1;  // 9
+static_assert(4 * kV32Chunks == 36, "one V3.2 chunk per four S^T k-steps");
+__device__ __forceinline__ uint4 v32_read(const uint8_t* raw, int wave_base, int kk) {
+  const int t = wave_base | fresh_lane();
+  if (kk < kV32Chunks - 1) {
+    const int k = kk * kThreads + t;
+    const uint8_t* rec = raw + (k >> 6) * kFp8TokenBytes;
+    const uint2 c = *reinterpret_cast<const uint2*>(rec + (k & 63) * 8);
+    return make_uint4(c.x, c.y, *reinterpret_cast<const uint32_t*>(rec + 512 + 4 * ((k & 63) >> 4)), 0u);
+  }
+  return *reinterpret_cast<const uint4*>(raw + (t >> 3) * kFp8TokenBytes + 528 + (t & 7) * 16);
+}
+__device__ __forceinline__ void v32_write(uint8_t* tile, int wave_base, int kk, uint4 ch) {
+  const int t = wave_base | fresh_lane();
+  if (kk < kV32Chunks - 1) {
+    const int k = kk * kThreads + t;
+    *reinterpret_cast<uint4*>(tile + (k >> 6) * kMainStride + (k & 63) * 16) =
+        codes_to_f16x8(ch.x, ch.y, __uint_as_float(ch.z));
+  } else {
+    const int r = t >> 3, c = t & 7;
+    *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = bf16x8_to_f16x8(ch);
   }
 }
 
@@ -786,28 +816,37 @@ template <int KVF>
 constexpr int ksteps() { return KVF == kKvFp8V41 ? 32 : 36; }
 template <int KVF>
 constexpr int dqk_of() { return 16 * ksteps<KVF>(); }
-// FP8 KV and the fused bf16 path (whose prologue and epilogue need the
-// registers) keep k-steps 24..35 of the query in LDS.
+// The fused path (whose prologue and epilogue need the registers) keeps
+// k-steps 24..35 of the query in LDS; every other path holds all of it in
+// VGPRs.
 template <int KVF, bool FUSED>
-constexpr int q_reg_steps() { return KVF == kKvFp8V32 || (KVF == kKvBf16 && FUSED) ? 24 : ksteps<KVF>(); }
+constexpr int q_reg_steps() { return FUSED ? 24 : ksteps<KVF>(); }
 template <int KVF, bool FUSED>
 constexpr int q_lds_row_bytes() { return (ksteps<KVF>() - q_reg_steps<KVF, FUSED>()) * 2 * 16; }  // 384 or 0
 template <int KVF, bool FUSED>
 constexpr int q_lds_wave_bytes() { return 32 * q_lds_row_bytes<KVF, FUSED>(); }                 // 12288 or 0
-constexpr int kQRegStepsFp8 = q_reg_steps<kKvFp8V32, false>();
-// Sparse id slots: ids are fetched 4 steps ahead (5 for V4.1 records), and
-// a slot is rewritten only after the step that last read it.
-template <int KVF>
-constexpr int ids_slots() { return KVF == kKvFp8V41 ? 6 : 5; }
+// FP8 records: unfused, a step dequantises the next step's records into a
+// second tile between its own S^T MFMAs, and raw records go out three steps
+// ahead; the fused V3.2 path (its query half in LDS leaves room for one
+// tile only) dequantises each step's records before its S^T, two ahead.
+template <int KVF, bool FUSED>
+constexpr bool dq_ahead() { return KVF != kKvBf16 && !FUSED; }
+template <int KVF, bool FUSED>
+constexpr int raw_ahead() { return dq_ahead<KVF, FUSED>() ? 3 : 2; }
+// Sparse id slots: ids are fetched 4 steps ahead on bf16 KV and two steps
+// before the FP8 records that use them, and a slot is rewritten only after
+// the step that last read it.
+template <int KVF, bool FUSED>
+constexpr int ids_slots() { return KVF == kKvBf16 ? 5 : raw_ahead<KVF, FUSED>() + 3; }
 
 template <int KVF, bool SPARSE, bool FUSED>
 struct DecodeLayout {
   static constexpr int kTileOff = 0;                                   // bf16 half tiles
-  static constexpr int kTiles = KVF == kKvBf16 ? kTileRing : KVF == kKvFp8V41 ? 2 : 1;
+  static constexpr int kTiles = KVF == kKvBf16 ? kTileRing : dq_ahead<KVF, FUSED>() ? 2 : 1;
   static constexpr int kRawOff = kTiles * kHalfBytes;                  // fp8 raw slots
   static constexpr int kQOff = kRawOff + (KVF == kKvBf16 ? 0 : kRing * kRawSlotBytes);
   static constexpr int kIdsOff = kQOff + kWaves * q_lds_wave_bytes<KVF, FUSED>();
-  static constexpr int kWalkOff = kIdsOff + (SPARSE ? ids_slots<KVF>() * 256 : 0);  // 2 words per wave
+  static constexpr int kWalkOff = kIdsOff + (SPARSE ? ids_slots<KVF, FUSED>() * 256 : 0);  // 2 words per wave
   static constexpr int kSclOff = kWalkOff + (KVF == kKvBf16 && !SPARSE ? kWaves * 8 : 0);
   static constexpr int kWOff = kSclOff;  // fused: norm weight row
   static constexpr int kSmem = kWOff + (FUSED ? kDqk * 2 : 0);
@@ -888,7 +927,7 @@ k_decode(DecodeArgs a) {
     b = uni(b); j = uni(j);
   };
   auto ids_slot = [&](int step) {
-    return reinterpret_cast<int32_t*>(smem + Lay::kIdsOff) + (step % ids_slots<KVF>()) * 64;
+    return reinterpret_cast<int32_t*>(smem + Lay::kIdsOff) + (step % ids_slots<KVF, FUSED>()) * 64;
   };
   auto fetch_ids = [&](int b, int j, int h, int step) {
     if constexpr (SPARSE)
@@ -1029,9 +1068,8 @@ k_decode(DecodeArgs a) {
       }
     }
   };
-  // FP8 loads lead by kRawAhead steps, ids by kRawAhead + 2 (V4.1, whose
-  // step dequantises one step ahead, by one more)
-  constexpr int kRawAhead = KVF == kKvFp8V41 ? 3 : 2;
+  // FP8 loads lead by kRawAhead steps, ids by kRawAhead + 2
+  constexpr int kRawAhead = raw_ahead<KVF, FUSED>();
   auto issue_next = [&](int step) {
     if (step + kRawAhead < nsteps) {
       issue_load(step + kRawAhead);
@@ -1045,18 +1083,19 @@ k_decode(DecodeArgs a) {
     }
   };
 
-  // ---- prologue: ids of steps 0..3; the loads of steps 0..2 are issued in
-  // the first piece's prologue (bf16: steps 0 and 1 right after the query
-  // loads, step 2 once the walker has landed the block of its item)
+  // ---- prologue: the ids of the first steps (4 on bf16 KV, kRawAhead + 2
+  // on FP8); the loads of the first kDepth (bf16) or kRawAhead (FP8) steps
+  // are issued in the first piece's prologue (bf16: right after the query
+  // loads)
   if constexpr (SPARSE) {
-    for (int s = 0; s < min(KVF == kKvFp8V41 ? 5 : 4, nsteps); ++s) {
+    for (int s = 0; s < min(KVF == kKvBf16 ? 4 : kRawAhead + 2, nsteps); ++s) {
       fetch_ids(fb, fj, fh, s);
       advance(fb, fj, fh);
     }
     __builtin_amdgcn_s_waitcnt(0);
   }
   auto issue_first_loads = [&]() {
-    for (int s = 0; s < min(KVF == kKvFp8V41 ? 3 : KVF == kKvBf16 ? kDepth : 2, nsteps); ++s) {
+    for (int s = 0; s < min(KVF == kKvBf16 ? kDepth : kRawAhead, nsteps); ++s) {
       issue_load(s);
       advance_load();
     }
@@ -1215,7 +1254,7 @@ k_decode(DecodeArgs a) {
     // ======== building blocks of one 32-key step
     auto tile_off = [&](int st) -> int {
       if constexpr (KVF == kKvBf16) return Lay::kTileOff + (st % kTileRing) * kHalfBytes;
-      else if constexpr (KVF == kKvFp8V41) return Lay::kTileOff + (st & 1) * kHalfBytes;
+      else if constexpr (dq_ahead<KVF, FUSED>()) return Lay::kTileOff + (st & 1) * kHalfBytes;
       else return Lay::kTileOff;
     };
     // S^T (32 keys x 32 rows) of the tile at LDS offset tb into sc, with the
@@ -1410,25 +1449,31 @@ k_decode(DecodeArgs a) {
           pv(tile_off(step), st.pf);
         }
       }
-    } else if constexpr (KVF == kKvFp8V41) {
-      // ---- V4.1: two bf16 tiles.  Step s runs S^T, softmax and P.V on tile
-      // s%2 and meanwhile dequantises step s+1's records into the other tile,
-      // one chunk between every four MFMAs of S^T; one barrier per step.
-      // Raw records go out three steps ahead (into the slot of the records
-      // dequantised a step ago), ids five.
+    } else if constexpr (dq_ahead<KVF, FUSED>()) {
+      // ---- FP8 records, two tiles.  Step s runs S^T, softmax and P.V on
+      // tile s%2 and meanwhile dequantises step s+1's records into the other
+      // tile, one chunk between every four MFMAs of S^T (V3.2: 9 chunks over
+      // 36 k-steps; V4.1: 8 over 32); one barrier per step.  Raw records go
+      // out three steps ahead (into the slot of the records dequantised a
+      // step ago), ids five.
       const int wave_base = tid & ~63;
       auto dq_tile = [&](int st) { return smem + tile_off(st); };
       auto dq_raw = [&](int st) { return smem + Lay::kRawOff + (st % kRing) * kRawSlotBytes; };
+      auto dequant_all = [&](int st) {
+        if constexpr (KVF == kKvFp8V41) dequant_v41(dq_tile(st), dq_raw(st), tid);
+        else dequant_codes(dq_tile(st), dq_raw(st), tid);
+      };
       if (step == 0) {  // the first step's tile: the prologue drain landed its records
-        dequant_v41(dq_tile(0), dq_raw(0), tid);
+        dequant_all(0);
         lds_barrier();
       }
       for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
         if (ps > 0) {
-          // The previous step issued raw(step+2) (if any) and ids(step+4) (if
-          // any), after everything this step needs: raw(step+1), ids(step+3).
+          // The previous step issued raw(step+2) (if any) and, sparse,
+          // ids(step+4) (if any), after everything this step needs:
+          // raw(step+1) and ids(step+3).
           if (step + 2 >= nsteps) wait_vmcnt<0>();
-          else if (step + 4 >= nsteps) wait_vmcnt<Lay::kVmPerStep - 1>();
+          else if (SPARSE && step + 4 >= nsteps) wait_vmcnt<Lay::kVmPerStep - 1>();
           else wait_vmcnt<Lay::kVmPerStep>();
           lds_barrier();  // tile step%2 staged by every wave; P.V(step-1) done with the other
         }
@@ -1438,15 +1483,23 @@ k_decode(DecodeArgs a) {
         f32x16 sc;
         SmState st;
         if (hk && dq) {
-          V41Chunk ch;
-          qk(tile_off(step), sc, [&](int ks) {
-            if ((ks & 3) == 0) ch = v41_read(dq_raw(step + 1), wave_base, ks >> 2);
-            else if ((ks & 3) == 3) v41_write(dq_tile(step + 1), wave_base, ks >> 2, ch);
-          });
+          if constexpr (KVF == kKvFp8V41) {
+            V41Chunk ch;
+            qk(tile_off(step), sc, [&](int ks) {
+              if ((ks & 3) == 0) ch = v41_read(dq_raw(step + 1), wave_base, ks >> 2);
+              else if ((ks & 3) == 3) v41_write(dq_tile(step + 1), wave_base, ks >> 2, ch);
+            });
+          } else {
+            uint4 ch;
+            qk(tile_off(step), sc, [&](int ks) {
+              if ((ks & 3) == 0) ch = v32_read(dq_raw(step + 1), wave_base, ks >> 2);
+              else if ((ks & 3) == 3) v32_write(dq_tile(step + 1), wave_base, ks >> 2, ch);
+            });
+          }
         } else if (hk) {
           qk(tile_off(step), sc, [](int) {});
         } else if (dq) {
-          dequant_v41(dq_tile(step + 1), dq_raw(step + 1), tid);
+          dequant_all(step + 1);
         }
         if (hk) {
 #pragma unroll
@@ -1457,7 +1510,7 @@ k_decode(DecodeArgs a) {
         }
       }
     } else {
-      // ---- FP8 V3.2: one fp16 tile (code times scale, rounded once),
+      // ---- fused FP8 V3.2: one fp16 tile (code times scale, rounded once),
       // dequantised from the raw ring each step; S^T and P.V as on bf16 KV
       for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
         if (ps > 0) {
