@@ -61,13 +61,31 @@ namespace mla {
 // s_memrealtime clock at kernel start, at each piece's start, after its
 // prologue, after its main loop and at its end (up to kTrPieces pieces), and
 // at kernel end, with vector stores into a static array that
-// mla_phase_trace_copy() returns.
+// mla_phase_trace_copy() returns.  Wave 0 also sums the shader clock
+// (s_memtime) spent in each phase of its 32-key steps (kTrSteps phases:
+// load wait; barrier, with the fused fp16 conversion or the one-tile FP8
+// dequantisation; load issue; S^T, with the next tile's dequantisation on
+// the two-tile FP8 path; softmax; P.V issue) into slots kTrStepOff..,
+// and its step count after them.
 // ---------------------------------------------------------------------------
 #ifdef MLA_PHASE_TRACE
-constexpr int kTrPieces = 7, kTrPer = 32, kTrWgs = 4096;
+constexpr int kTrPieces = 7, kTrPer = 40, kTrWgs = 4096, kTrSteps = 6, kTrStepOff = 32;
 __device__ uint64_t g_phase_t[kTrWgs * kTrPer];
 __device__ int g_phase_items[kTrWgs * kTrPieces];
-#define MLA_TR_KERNEL_START const uint64_t tr_t0 = __builtin_amdgcn_s_memrealtime(); int tr_p = 0;
+#define MLA_TR_KERNEL_START                                                               \
+  const uint64_t tr_t0 = __builtin_amdgcn_s_memrealtime();                                \
+  int tr_p = 0;                                                                           \
+  uint64_t tr_acc[kTrSteps] = {};                                                         \
+  uint64_t tr_last = 0;                                                                   \
+  int tr_steps = 0;
+#define MLA_ST_BEGIN do { tr_last = __builtin_amdgcn_s_memtime(); } while (0)
+#define MLA_ST(i)                                                                         \
+  do {                                                                                    \
+    const uint64_t t_ = __builtin_amdgcn_s_memtime();                                     \
+    tr_acc[i] += t_ - tr_last;                                                            \
+    tr_last = t_;                                                                         \
+  } while (0)
+#define MLA_ST_STEP do { ++tr_steps; } while (0)
 #define MLA_TR_WG_ACTIVE \
   if (threadIdx.x == 0 && blockIdx.x < kTrWgs) g_phase_t[blockIdx.x * kTrPer] = tr_t0;
 #define MLA_TR(k)                                                                              \
@@ -81,8 +99,12 @@ __device__ int g_phase_items[kTrWgs * kTrPieces];
       g_phase_items[blockIdx.x * kTrPieces + tr_p] = (n);                                      \
   } while (0)
 #define MLA_TR_NEXT_PIECE ++tr_p;
-#define MLA_TR_KERNEL_END \
-  if (threadIdx.x == 0 && blockIdx.x < kTrWgs) g_phase_t[blockIdx.x * kTrPer + kTrPer - 1] = __builtin_amdgcn_s_memrealtime();
+#define MLA_TR_KERNEL_END                                                                 \
+  if (threadIdx.x == 0 && blockIdx.x < kTrWgs) {                                          \
+    g_phase_t[blockIdx.x * kTrPer + kTrPer - 1] = __builtin_amdgcn_s_memrealtime();       \
+    for (int i_ = 0; i_ < kTrSteps; ++i_) g_phase_t[blockIdx.x * kTrPer + kTrStepOff + i_] = tr_acc[i_]; \
+    g_phase_t[blockIdx.x * kTrPer + kTrStepOff + kTrSteps] = (uint64_t)tr_steps;          \
+  }
 #else
 #define MLA_TR_KERNEL_START
 #define MLA_TR_WG_ACTIVE
@@ -90,6 +112,9 @@ __device__ int g_phase_items[kTrWgs * kTrPieces];
 #define MLA_TR_ITEMS(n) do {} while (0)
 #define MLA_TR_NEXT_PIECE
 #define MLA_TR_KERNEL_END
+#define MLA_ST_BEGIN do {} while (0)
+#define MLA_ST(i) do {} while (0)
+#define MLA_ST_STEP do {} while (0)
 #endif
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -559,10 +584,6 @@ __device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t
     dma_glb16(lds_off(raw) + i * 1024, g);
   }
 }
-
-// Scales of an FP8 half tile in LDS, in the register order of the S^T
-// accumulator: [tile t][lane half h][i] holds the scale of dims 128t.. of
-// key key_of_row(8*(i/4) + i%4) + h.
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -1428,26 +1449,34 @@ k_decode(DecodeArgs a) {
       // one wave the softmax VALU work does not overlap the MFMAs (measured),
       // so the three phases run back to back on one resident tile.
       for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
+        MLA_ST_BEGIN;
         // Only the loads of the newest kDepth-1 steps (kLoadsPerHalf each,
         // issued after those steps' walker words) may still be in flight.
         wait_vmcnt<kLoadsPerHalf * (kDepth - 1)>();
+        MLA_ST(0);
         if constexpr (FUSED) own_chunks_to_f16(smem + tile_off(step), wave);  // this wave's rows -> fp16
         lds_barrier();  // ... for every wave; tile ps-1's slot is free
+        MLA_ST(1);
         land();
         prepare_load(step + kDepth);
         fetch_next_ids(step);
 #pragma unroll
         for (int k = 0; k < kLoadsPerHalf; ++k) emit_load(k);
+        MLA_ST(2);
         if (has_keys(ps)) {
           f32x16 sc;
           SmState st;
           qk(tile_off(step), sc, [](int) {});
+          MLA_ST(3);
 #pragma unroll
           for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc, st, key0_of(ps), step);
           rescale_o(st);
           valu_to_mfma_settle(st.pf[0], st.pf[1]);
+          MLA_ST(4);
           pv(tile_off(step), st.pf);
+          MLA_ST(5);
         }
+        MLA_ST_STEP;
       }
     } else if constexpr (dq_ahead<KVF, FUSED>()) {
       // ---- FP8 records, two tiles.  Step s runs S^T, softmax and P.V on
@@ -1468,6 +1497,7 @@ k_decode(DecodeArgs a) {
         lds_barrier();
       }
       for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
+        MLA_ST_BEGIN;
         if (ps > 0) {
           // The previous step issued raw(step+2) (if any) and, sparse,
           // ids(step+4) (if any), after everything this step needs:
@@ -1475,9 +1505,12 @@ k_decode(DecodeArgs a) {
           if (step + 2 >= nsteps) wait_vmcnt<0>();
           else if (SPARSE && step + 4 >= nsteps) wait_vmcnt<Lay::kVmPerStep - 1>();
           else wait_vmcnt<Lay::kVmPerStep>();
+          MLA_ST(0);
           lds_barrier();  // tile step%2 staged by every wave; P.V(step-1) done with the other
+          MLA_ST(1);
         }
         issue_next(step);
+        MLA_ST(2);
         const bool hk = has_keys(ps);
         const bool dq = step + 1 < nsteps;
         f32x16 sc;
@@ -1501,18 +1534,23 @@ k_decode(DecodeArgs a) {
         } else if (dq) {
           dequant_all(step + 1);
         }
+        MLA_ST(3);
         if (hk) {
 #pragma unroll
           for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc, st, key0_of(ps), step);
           rescale_o(st);
           valu_to_mfma_settle(st.pf[0], st.pf[1]);
+          MLA_ST(4);
           pv(tile_off(step), st.pf);
+          MLA_ST(5);
         }
+        MLA_ST_STEP;
       }
     } else {
       // ---- fused FP8 V3.2: one fp16 tile (code times scale, rounded once),
       // dequantised from the raw ring each step; S^T and P.V as on bf16 KV
       for (int ps = 0; ps < 2 * (piece_end - cj); ++ps, ++step) {
+        MLA_ST_BEGIN;
         if (ps > 0) {
           // This step's loads were issued two steps ago; the previous step
           // then issued the loads of step+1 (if any) and, sparse, the ids of
@@ -1521,24 +1559,31 @@ k_decode(DecodeArgs a) {
           if (step + 1 >= nsteps) wait_vmcnt<0>();
           else if (SPARSE && step + 3 >= nsteps) wait_vmcnt<kLoadsPerStep>();
           else wait_vmcnt<Lay::kVmPerStep>();
+          MLA_ST(0);
           lds_barrier();  // every wave's loads of this step landed
         }
         dequant_codes(smem + Lay::kTileOff, smem + Lay::kRawOff + (step % kRing) * kRawSlotBytes, tid);
         lds_barrier();  // the tile is staged; raw slot (step+2)%3 (dequantised last step) is free
+        MLA_ST(1);
         const bool hk = has_keys(ps);
         f32x16 sc;
         SmState st;
         if (hk) qk(tile_off(step), sc, [](int) {});
+        MLA_ST(3);
         // The loads of step+2 go out after S^T: the register reloads inside
         // S^T wait for every older load, and would otherwise wait for these.
         issue_next(step);
+        MLA_ST(2);
         if (hk) {
 #pragma unroll
           for (int k = 0; k < kSmSlices; ++k) sm_slice(k, sc, st, key0_of(ps), step);
           rescale_o(st);
           valu_to_mfma_settle(st.pf[0], st.pf[1]);
+          MLA_ST(4);
           pv(tile_off(step), st.pf);
+          MLA_ST(5);
         }
+        MLA_ST_STEP;
       }
     }
 

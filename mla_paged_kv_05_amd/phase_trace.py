@@ -2,7 +2,8 @@
 (libmla_phase_trace.so, built by build.build_phase_trace()): where a
 workgroup's time goes between its start, each piece's prologue, main loop and
 finalize, and its end, and how long the launch's tail waits for the slowest
-workgroup.
+workgroup; then where a 32-key step's time goes, from wave 0's per-phase
+sums of the shader clock.
 
     python -m mla_paged_kv_05_amd.phase_trace --workload dense_b64_h128_L1k-8k
 
@@ -23,7 +24,11 @@ from . import binding as B
 from . import build as hip_build
 from . import workloads as W
 
-KTR_PER, KTR_PIECES = 32, 7   # the layout the traced kernel writes
+KTR_PER, KTR_PIECES = 40, 7   # the layout the traced kernel writes
+KTR_STEP_OFF, KTR_STEPS = 32, 6
+STEP_PHASES = ["load wait", "barrier (fused bf16: with the fp16 conversion; one-tile FP8: with the dequantisation)",
+               "load issue", "S^T (two-tile FP8: with the next tile's dequantisation)", "softmax and lazy rescale",
+               "P.V issue"]
 CLOCK_MHZ = 100.0             # s_memrealtime
 
 
@@ -89,6 +94,11 @@ def run(name: str, warmup: int = 6) -> str:
             nit.append(items[w, pc])
     pro, loop, fin, nit = map(np.array, (pro, loop, fin, nit))
     nact = int(act.sum())
+    acc = tr[act, KTR_STEP_OFF:KTR_STEP_OFF + KTR_STEPS].sum(0)
+    nsteps = int(tr[act, KTR_STEP_OFF + KTR_STEPS].sum())
+    # shader-clock ticks per microsecond: the step sums against the same
+    # steps' main-loop time on the 100 MHz clock
+    ticks_per_us = acc.sum() / max(loop.sum(), 1e-9)
     first = (tr[act, 1] - tr[act, 0]) / CLOCK_MHZ
     lines = [
         f"Phase timeline of one `{name}` decode launch (`python -m mla_paged_kv_05_amd.phase_trace "
@@ -108,7 +118,15 @@ def run(name: str, warmup: int = 6) -> str:
         f"{fin.sum() / nact:.1f} us |",
         f"| tail: mean of (last end - own end) | {np.mean(end.max() - end):.1f} us |",
         "",
+        f"Per 32-key step (wave 0 of each workgroup, {nsteps} steps; shader clock {ticks_per_us:.0f} "
+        f"cycles per us; a step is {acc.sum() / max(nsteps, 1):.0f} cycles = "
+        f"{acc.sum() / max(nsteps, 1) / ticks_per_us:.3f} us):",
+        "",
+        "| Phase | cycles per step | share |", "|---|---|---|",
     ]
+    for name_, v in zip(STEP_PHASES, acc):
+        lines.append(f"| {name_} | {v / max(nsteps, 1):.0f} | {100 * v / max(acc.sum(), 1):.1f} % |")
+    lines.append("")
     return "\n".join(lines)
 
 
