@@ -510,30 +510,35 @@ __device__ __forceinline__ void load_half_bf16_dense(uint8_t* slot, const uint8_
 __device__ __forceinline__ bool id_in_pool(int id, int64_t ntok) { return id >= 0 && (int64_t)id < ntok; }
 
 // Sparse bf16: row r is flat pool token ids[r] when r < nvalid and the id
-// is in the pool, else zeros.  Same 9 loads per wave as the dense loader.
-__device__ __forceinline__ void load_row_bf16_sparse(uint8_t* slot, const uint8_t* kv, int64_t ntok,
-                                                     const int32_t* ids, int nvalid, int wave, int k) {
+// is in the pool, else zeros.  Same 9 loads per wave as the dense loader
+// (k < 8: main row wave + 4k, one id for the whole wave; k = 8: the rope
+// rows, one id per lane).  Every id is read before the first load: a load's
+// "memory" clobber keeps later LDS reads behind it, so reading each id just
+// before its load would wait out one LDS latency per load.
+__device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8_t* kv, int64_t ntok,
+                                                      const int32_t* ids, int nvalid, int wave, int /*lane*/) {
   const int l16 = fresh_lane() << 4;
   const uint32_t base = lds_off(slot);
-  if (k < kHalfRows / kWaves) {
-    const int r = wave + kWaves * k;
-    const int id = uni(r < nvalid ? ids[r] : -1);
-    const uint8_t* src = uni_ptr(id_in_pool(id, ntok) ? kv + (int64_t)id * kRowBytes : g_zero_row);
-    dma_glb16_s(base + r * kMainStride, l16, src);
-  } else {
-    const int rr = 8 * wave + (l16 >> 7);
-    const int id = rr < nvalid ? ids[rr] : -1;
-    const int cc = rope_phys_chunk(rr, (l16 >> 4) & 7);
-    const uint8_t* g = id_in_pool(id, ntok) ? kv + (int64_t)id * kRowBytes + 1024 + cc * 16
-                                            : g_zero_row + 1024 + cc * 16;
-    dma_glb16(base + kRopeOff + wave * 1024, g);
-  }
-}
-__device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8_t* kv, int64_t ntok,
-                                                      const int32_t* ids, int nvalid, int wave,
-                                                      int /*lane*/) {
+  const int rr = 8 * wave + (l16 >> 7);
+  int id[kLoadsPerHalf];
 #pragma unroll
-  for (int k = 0; k < kLoadsPerHalf; ++k) load_row_bf16_sparse(slot, kv, ntok, ids, nvalid, wave, k);
+  for (int k = 0; k < kLoadsPerHalf - 1; ++k) {
+    const int r = wave + kWaves * k;
+    id[k] = r < nvalid ? ids[r] : -1;
+  }
+  id[kLoadsPerHalf - 1] = rr < nvalid ? ids[rr] : -1;
+#pragma unroll
+  for (int k = 0; k < kLoadsPerHalf - 1; ++k) {
+    const int r = wave + kWaves * k;
+    const int idk = uni(id[k]);
+    const uint8_t* src = uni_ptr(id_in_pool(idk, ntok) ? kv + (int64_t)idk * kRowBytes : g_zero_row);
+    dma_glb16_s(base + r * kMainStride, l16, src);
+  }
+  const int cc = rope_phys_chunk(rr, (l16 >> 4) & 7);
+  const int idr = id[kLoadsPerHalf - 1];
+  const uint8_t* g = id_in_pool(idr, ntok) ? kv + (int64_t)idr * kRowBytes + 1024 + cc * 16
+                                           : g_zero_row + 1024 + cc * 16;
+  dma_glb16(base + kRopeOff + wave * 1024, g);
 }
 
 // FP8 V3.2 records of one half (32 x 656 B = 1312 chunks) are staged raw by
@@ -572,15 +577,22 @@ __device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t
                                                      int lane) {
   constexpr int kTok = tok_bytes<KVF>(), kChunks = kTok / 16, kHalfChunks = kHalfRows * kChunks;
   lane = fresh_lane();
+  // every id first, as in the bf16 loader
+  constexpr int kLoads = raw_loads_per_wave<KVF>();
+  int id[kLoads];
 #pragma unroll
-  for (int ii = 0; ii < raw_loads_per_wave<KVF>(); ++ii) {
+  for (int ii = 0; ii < kLoads; ++ii) {
+    const int pos_all = (ii * kWaves + wave) * 64 + lane;
+    const int r = pos_all / kChunks;
+    id[ii] = (pos_all < kHalfChunks && r < nvalid) ? ids[r] : -1;
+  }
+#pragma unroll
+  for (int ii = 0; ii < kLoads; ++ii) {
     const int i = ii * kWaves + wave;
     const int pos_all = i * 64 + lane;
-    const int r = pos_all / kChunks;
-    const int c = pos_all - r * kChunks;
-    const int id = (pos_all < kHalfChunks && r < nvalid) ? ids[r] : -1;
+    const int c = pos_all - (pos_all / kChunks) * kChunks;
     const uint8_t* g =
-        id_in_pool(id, ntok) ? kv + (int64_t)id * kTok + c * 16 : g_zero_row + (pos_all & 63) * 16;
+        id_in_pool(id[ii], ntok) ? kv + (int64_t)id[ii] * kTok + c * 16 : g_zero_row + (pos_all & 63) * 16;
     dma_glb16(lds_off(raw) + i * 1024, g);
   }
 }
@@ -1053,7 +1065,7 @@ k_decode(DecodeArgs a) {
   };
 
   // bf16 path: the loads of step+kDepth are captured by prepare_load() at
-  // the start of step `step` and issued by emit_load(k), k < kLoadsPerHalf,
+  // the start of step `step` and issued by emit_loads() (kLoadsPerHalf loads),
   // after the walker's and the ids' word loads of that step.  Past the
   // slot's last step the same instructions stage zeros into the free slot,
   // so every step issues exactly kLoadsPerHalf tile loads, last.  (Issuing
@@ -1073,10 +1085,14 @@ k_decode(DecodeArgs a) {
     }
     if (do_load) advance_load();
   };
-  auto emit_load = [&](int k) {
+  auto emit_loads = [&]() {
     uint8_t* slot = smem + Lay::kTileOff + (pl_step % kTileRing) * kHalfBytes;
-    if constexpr (!SPARSE) load_row_bf16_dense(slot, a.kv, pl_phys, pl_valid, pl_h, wave, k);
-    else load_row_bf16_sparse(slot, a.kv, ntok, ids_slot(pl_step), pl_nvalid, wave, k);
+    if constexpr (!SPARSE) {
+#pragma unroll
+      for (int k = 0; k < kLoadsPerHalf; ++k) load_row_bf16_dense(slot, a.kv, pl_phys, pl_valid, pl_h, wave, k);
+    } else {
+      load_half_bf16_sparse(slot, a.kv, ntok, ids_slot(pl_step), pl_nvalid, wave, 0);
+    }
   };
 
   // loads of step+2 and (sparse) ids of step+4, issued at step `step`
@@ -1460,8 +1476,7 @@ k_decode(DecodeArgs a) {
         land();
         prepare_load(step + kDepth);
         fetch_next_ids(step);
-#pragma unroll
-        for (int k = 0; k < kLoadsPerHalf; ++k) emit_load(k);
+        emit_loads();
         MLA_ST(2);
         if (has_keys(ps)) {
           f32x16 sc;
