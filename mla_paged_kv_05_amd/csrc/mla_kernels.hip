@@ -647,33 +647,33 @@ __device__ __forceinline__ uint4 codes_to_f16x8(uint32_t c0, uint32_t c1, float 
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
+// Thread (wave w, lane l) converts chunk kk*256 + 64w + l of the half's
+// 32 x 64 code chunks: record 4kk + w, codes 8l..8l+7 (block l/16), and the
+// 16 bytes of RoPE dims at record 8w + l/8, chunk l%8.  The record index is
+// uniform, so every address is a wave-uniform base, the lane's offset and an
+// immediate.
 __device__ __forceinline__ void dequant_codes(uint8_t* tile, const uint8_t* raw, int tid) {
-  tid = (tid & ~63) | fresh_lane();  // keep the per-thread addresses out of the loop's live set
+  const int wave = uni(tid >> 6), ln = fresh_lane();  // lane id not held across the loop
   // All code and scale reads first, then the conversions and writes: the
   // compiler cannot move a read of the raw slot above a write to the tile
   // (same LDS array), so interleaved they would each wait out an LDS latency.
   constexpr int kPer = kHalfRows * 64 / kThreads;
-  const int blk = (tid & 63) >> 4;  // chunk k = kk*256 + tid: every one in 128-dim block blk
   uint2 codes[kPer];
   float scl[kPer];
 #pragma unroll
   for (int kk = 0; kk < kPer; ++kk) {
-    const int k = kk * kThreads + tid;
-    const uint8_t* rec = raw + (k >> 6) * kFp8TokenBytes;
-    codes[kk] = *reinterpret_cast<const uint2*>(rec + (k & 63) * 8);
-    scl[kk] = *reinterpret_cast<const float*>(rec + 512 + 4 * blk);
+    const uint8_t* rec = raw + (kk * kWaves + wave) * kFp8TokenBytes;
+    codes[kk] = *reinterpret_cast<const uint2*>(rec + ln * 8);
+    scl[kk] = *reinterpret_cast<const float*>(rec + 512 + 4 * (ln >> 4));
   }
-  uint4 rope = *reinterpret_cast<const uint4*>(raw + (tid >> 3) * kFp8TokenBytes + 528 + (tid & 7) * 16);
+  const int rr = wave * 8 + (ln >> 3), rc = ln & 7;
+  uint4 rope = *reinterpret_cast<const uint4*>(raw + rr * kFp8TokenBytes + 528 + rc * 16);
 #pragma unroll
-  for (int kk = 0; kk < kPer; ++kk) {
-    const int k = kk * kThreads + tid;
-    *reinterpret_cast<uint4*>(tile + (k >> 6) * kMainStride + (k & 63) * 16) =
+  for (int kk = 0; kk < kPer; ++kk)
+    *reinterpret_cast<uint4*>(tile + (kk * kWaves + wave) * kMainStride + ln * 16) =
         codes_to_f16x8(codes[kk].x, codes[kk].y, scl[kk]);
-  }
-  {
-    const int r = tid >> 3, c = tid & 7;
-    *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = bf16x8_to_f16x8(rope);
-  }
+  *reinterpret_cast<uint4*>(tile + kRopeOff + rr * kRopeStride + (rope_phys_chunk(rr, rc) << 4)) =
+      bf16x8_to_f16x8(rope);
 }
 
 // The same conversion one chunk at a time, for spreading it between the
@@ -682,24 +682,22 @@ __device__ __forceinline__ void dequant_codes(uint8_t* tile, const uint8_t* raw,
 // dims this thread converts.
 constexpr int kV32Chunks = kHalfRows * 64 / kThreads + 1;  // 9
 static_assert(4 * kV32Chunks == 36, "one V3.2 chunk per four S^T k-steps");
-__device__ __forceinline__ uint4 v32_read(const uint8_t* raw, int wave_base, int kk) {
-  const int t = wave_base | fresh_lane();
+__device__ __forceinline__ uint4 v32_read(const uint8_t* raw, int wave, int kk) {
+  const int ln = fresh_lane();
   if (kk < kV32Chunks - 1) {
-    const int k = kk * kThreads + t;
-    const uint8_t* rec = raw + (k >> 6) * kFp8TokenBytes;
-    const uint2 c = *reinterpret_cast<const uint2*>(rec + (k & 63) * 8);
-    return make_uint4(c.x, c.y, *reinterpret_cast<const uint32_t*>(rec + 512 + 4 * ((k & 63) >> 4)), 0u);
+    const uint8_t* rec = raw + (kk * kWaves + wave) * kFp8TokenBytes;
+    const uint2 c = *reinterpret_cast<const uint2*>(rec + ln * 8);
+    return make_uint4(c.x, c.y, *reinterpret_cast<const uint32_t*>(rec + 512 + 4 * (ln >> 4)), 0u);
   }
-  return *reinterpret_cast<const uint4*>(raw + (t >> 3) * kFp8TokenBytes + 528 + (t & 7) * 16);
+  return *reinterpret_cast<const uint4*>(raw + (wave * 8 + (ln >> 3)) * kFp8TokenBytes + 528 + (ln & 7) * 16);
 }
-__device__ __forceinline__ void v32_write(uint8_t* tile, int wave_base, int kk, uint4 ch) {
-  const int t = wave_base | fresh_lane();
+__device__ __forceinline__ void v32_write(uint8_t* tile, int wave, int kk, uint4 ch) {
+  const int ln = fresh_lane();
   if (kk < kV32Chunks - 1) {
-    const int k = kk * kThreads + t;
-    *reinterpret_cast<uint4*>(tile + (k >> 6) * kMainStride + (k & 63) * 16) =
+    *reinterpret_cast<uint4*>(tile + (kk * kWaves + wave) * kMainStride + ln * 16) =
         codes_to_f16x8(ch.x, ch.y, __uint_as_float(ch.z));
   } else {
-    const int r = t >> 3, c = t & 7;
+    const int r = wave * 8 + (ln >> 3), c = ln & 7;
     *reinterpret_cast<uint4*>(tile + kRopeOff + r * kRopeStride + (rope_phys_chunk(r, c) << 4)) = bf16x8_to_f16x8(ch);
   }
 }
@@ -714,21 +712,19 @@ __device__ __forceinline__ float e8m0_scale(uint32_t e) { return __builtin_ldexp
 // each conversion (two codes, the scale folded in) is exact; no scale is
 // kept for later.  Code reads go out before any tile write, as above.
 __device__ __forceinline__ void dequant_v41(uint8_t* tile, const uint8_t* raw, int tid) {
-  tid = (tid & ~63) | fresh_lane();
+  const int wave = uni(tid >> 6), ln = fresh_lane();  // chunks as in dequant_codes
   constexpr int kPer = kHalfRows * 64 / kThreads;
   uint2 codes[kPer];
   uint32_t ebits[kPer];
 #pragma unroll
   for (int kk = 0; kk < kPer; ++kk) {
-    const int k = kk * kThreads + tid;
-    const uint8_t* rec = raw + (k >> 6) * kFp8V41TokenBytes;
-    codes[kk] = *reinterpret_cast<const uint2*>(rec + (k & 63) * 8);
-    ebits[kk] = rec[512 + ((k & 63) >> 2)];  // 8 codes of dims 8c.. share scale c/4
+    const uint8_t* rec = raw + (kk * kWaves + wave) * kFp8V41TokenBytes;
+    codes[kk] = *reinterpret_cast<const uint2*>(rec + ln * 8);
+    ebits[kk] = rec[512 + (ln >> 2)];  // 8 codes of dims 8l.. share scale l/4
   }
 #pragma unroll
   for (int kk = 0; kk < kPer; ++kk) {
-    const int k = kk * kThreads + tid;
-    const int r = k >> 6, c = k & 63;
+    const int r = kk * kWaves + wave, c = ln;
     const float scale = e8m0_scale(ebits[kk]);
     const uint32_t cw[2] = {codes[kk].x, codes[kk].y};
     uint32_t w[4];
@@ -747,13 +743,13 @@ struct V41Chunk {
   uint2 code;
   uint32_t e;
 };
-__device__ __forceinline__ V41Chunk v41_read(const uint8_t* raw, int wave_base, int kk) {
-  const int k = kk * kThreads + (wave_base | fresh_lane());
-  const uint8_t* rec = raw + (k >> 6) * kFp8V41TokenBytes;
-  return V41Chunk{*reinterpret_cast<const uint2*>(rec + (k & 63) * 8), rec[512 + ((k & 63) >> 2)]};
+__device__ __forceinline__ V41Chunk v41_read(const uint8_t* raw, int wave, int kk) {
+  const int ln = fresh_lane();
+  const uint8_t* rec = raw + (kk * kWaves + wave) * kFp8V41TokenBytes;
+  return V41Chunk{*reinterpret_cast<const uint2*>(rec + ln * 8), rec[512 + (ln >> 2)]};
 }
-__device__ __forceinline__ void v41_write(uint8_t* tile, int wave_base, int kk, const V41Chunk& ch) {
-  const int k = kk * kThreads + (wave_base | fresh_lane());
+__device__ __forceinline__ void v41_write(uint8_t* tile, int wave, int kk, const V41Chunk& ch) {
+  const int ln = fresh_lane();
   const float scale = e8m0_scale(ch.e);
   const uint32_t cw[2] = {ch.code.x, ch.code.y};
   uint32_t w[4];
@@ -762,7 +758,7 @@ __device__ __forceinline__ void v41_write(uint8_t* tile, int wave_base, int kk, 
     w[2 * hh] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], scale, false));
     w[2 * hh + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hh], scale, true));
   }
-  *reinterpret_cast<uint4*>(tile + (k >> 6) * kMainStride + (k & 63) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(tile + (kk * kWaves + wave) * kMainStride + ln * 16) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // The 32 sparse ids of half `h` of work item j of (sequence b, query token
@@ -1500,7 +1496,6 @@ k_decode(DecodeArgs a) {
       // 36 k-steps; V4.1: 8 over 32); one barrier per step.  Raw records go
       // out three steps ahead (into the slot of the records dequantised a
       // step ago), ids five.
-      const int wave_base = tid & ~63;
       auto dq_tile = [&](int st) { return smem + tile_off(st); };
       auto dq_raw = [&](int st) { return smem + Lay::kRawOff + (st % kRing) * kRawSlotBytes; };
       auto dequant_all = [&](int st) {
@@ -1534,14 +1529,14 @@ k_decode(DecodeArgs a) {
           if constexpr (KVF == kKvFp8V41) {
             V41Chunk ch;
             qk(tile_off(step), sc, [&](int ks) {
-              if ((ks & 3) == 0) ch = v41_read(dq_raw(step + 1), wave_base, ks >> 2);
-              else if ((ks & 3) == 3) v41_write(dq_tile(step + 1), wave_base, ks >> 2, ch);
+              if ((ks & 3) == 0) ch = v41_read(dq_raw(step + 1), wave, ks >> 2);
+              else if ((ks & 3) == 3) v41_write(dq_tile(step + 1), wave, ks >> 2, ch);
             });
           } else {
             uint4 ch;
             qk(tile_off(step), sc, [&](int ks) {
-              if ((ks & 3) == 0) ch = v32_read(dq_raw(step + 1), wave_base, ks >> 2);
-              else if ((ks & 3) == 3) v32_write(dq_tile(step + 1), wave_base, ks >> 2, ch);
+              if ((ks & 3) == 0) ch = v32_read(dq_raw(step + 1), wave, ks >> 2);
+              else if ((ks & 3) == 3) v32_write(dq_tile(step + 1), wave, ks >> 2, ch);
             });
           }
         } else if (hk) {
