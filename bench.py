@@ -344,11 +344,15 @@ def main():
     src = os.path.join(ROOT, "mla_paged_kv_05_amd", "csrc", "mla_kernels.hip")
     tr = traffic_record(src, p.name)
     traffic = None if tr is None else tr["bytes_per_launch"]
+    # the type the products run in: bf16 on a bf16 cache and on V4.1 records
+    # (exact bf16 after dequantisation), fp16 on V3.2 records and on every
+    # fused decode
+    compute_dtype = "f16" if (p.fused or p.kv_format == "fp8v32") else "bf16"
     res = {
         "metric": "MLA paged decode effective HBM GB/s (algorithmic bytes) + TFLOPS, b=64 h_q=128 seq<=8K",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, shaped like the workload)",
+        "vs_baseline": None, "dtype": compute_dtype, "data": "synthetic (seeded, shaped like the workload)",
         "config": {"workload": p.name, "batch": p.batch, "s_q": p.s_q, "h_q": p.h_q, "d_qk": p.d_qk,
                    "d_v": 512, "page": 64, "kv_format": p.kv_format, "causal": bool(p.causal),
                    "sparse_topk": topk, "fused": bool(p.fused), "parallelism": "single GPU",
