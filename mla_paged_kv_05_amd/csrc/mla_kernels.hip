@@ -543,10 +543,9 @@ __device__ __forceinline__ void load_half_bf16_sparse(uint8_t* slot, const uint8
 
 // FP8 V3.2 records of one half (32 x 656 B = 1312 chunks) are staged raw by
 // LDS-DMA into a 24 KB slot (24 loads per half, 6 per wave; the tail of the
-// slot is padding), then dequantised LDS -> LDS into a bf16 half tile.
-// V4.1 records (32 x 528 B = 1056 chunks) use the same slot with 20 loads.
-constexpr int kFp8ChunksPerTok = kFp8TokenBytes / 16;        // 41
-constexpr int kRawHalfChunks = kHalfRows * kFp8ChunksPerTok;  // 1312
+// slot is padding), then dequantised LDS -> LDS into a 16-bit half tile
+// (fp16 for V3.2 records, bf16 for V4.1).  V4.1 records (32 x 528 B = 1056
+// chunks) use the same slot with 20 loads.
 constexpr int kRawSlotBytes = 24 * 1024;
 constexpr int kRawLoadsPerWave = kRawSlotBytes / 1024 / kWaves;  // 6
 template <int KVF>
@@ -870,14 +869,13 @@ constexpr int ids_slots() { return KVF == kKvBf16 ? 5 : raw_ahead<KVF, FUSED>() 
 
 template <int KVF, bool SPARSE, bool FUSED>
 struct DecodeLayout {
-  static constexpr int kTileOff = 0;                                   // bf16 half tiles
+  static constexpr int kTileOff = 0;                                   // 16-bit half tiles
   static constexpr int kTiles = KVF == kKvBf16 ? kTileRing : dq_ahead<KVF, FUSED>() ? 2 : 1;
   static constexpr int kRawOff = kTiles * kHalfBytes;                  // fp8 raw slots
   static constexpr int kQOff = kRawOff + (KVF == kKvBf16 ? 0 : kRing * kRawSlotBytes);
   static constexpr int kIdsOff = kQOff + kWaves * q_lds_wave_bytes<KVF, FUSED>();
   static constexpr int kWalkOff = kIdsOff + (SPARSE ? ids_slots<KVF, FUSED>() * 256 : 0);  // 2 words per wave
-  static constexpr int kSclOff = kWalkOff + (KVF == kKvBf16 && !SPARSE ? kWaves * 8 : 0);
-  static constexpr int kWOff = kSclOff;  // fused: norm weight row
+  static constexpr int kWOff = kWalkOff + (KVF == kKvBf16 && !SPARSE ? kWaves * 8 : 0);  // fused: norm weight row
   static constexpr int kSmem = kWOff + (FUSED ? kDqk * 2 : 0);
   // per-step VMEM instructions issued by every wave (loads + id fetch)
   static constexpr int kVmPerStep =
@@ -1910,7 +1908,8 @@ __global__ void __launch_bounds__(64) k_combine(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Debug gather: stage both halves of one work item with the decode kernel's
-// loaders (and dequantiser), copy them out un-swizzled as [64][576] bf16.
+// loaders (and dequantiser), copy them out un-swizzled as [64][576] 16-bit
+// values: bf16, or fp16 for V3.2 FP8 records (the tile the products read).
 // ---------------------------------------------------------------------------
 template <int KVF, bool SPARSE>
 __global__ void __launch_bounds__(kThreads) k_debug_gather(DecodeArgs a, int b, int t, int j,
