@@ -42,10 +42,10 @@ SCRATCH_BUDGET = {
     "_ZN3mla8k_decodeILi0ELb0ELb1EEEvNS_10DecodeArgsE": 524,  # bf16 dense fused
     "_ZN3mla8k_decodeILi0ELb1ELb1EEEvNS_10DecodeArgsE": 528,  # bf16 sparse fused
     "_ZN3mla8k_decodeILi1ELb0ELb0EEEvNS_10DecodeArgsE": 160,   # V3.2 FP8 dense
-    "_ZN3mla8k_decodeILi1ELb1ELb0EEEvNS_10DecodeArgsE": 80,    # V3.2 FP8 sparse
+    "_ZN3mla8k_decodeILi1ELb1ELb0EEEvNS_10DecodeArgsE": 68,    # V3.2 FP8 sparse
     "_ZN3mla8k_decodeILi1ELb0ELb1EEEvNS_10DecodeArgsE": 540,   # V3.2 FP8 dense fused
-    "_ZN3mla8k_decodeILi1ELb1ELb1EEEvNS_10DecodeArgsE": 536,   # V3.2 FP8 sparse fused
-    "_ZN3mla8k_decodeILi2ELb1ELb0EEEvNS_10DecodeArgsE": 80,    # V4.1 FP8 sparse
+    "_ZN3mla8k_decodeILi1ELb1ELb1EEEvNS_10DecodeArgsE": 528,   # V3.2 FP8 sparse fused
+    "_ZN3mla8k_decodeILi2ELb1ELb0EEEvNS_10DecodeArgsE": 68,    # V4.1 FP8 sparse
 }
 # Wait states an MFMA result needs before anything else reads or rewrites
 # its registers (at least the 16-pass XDL requirement; the kernels' own

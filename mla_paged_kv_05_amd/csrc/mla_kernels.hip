@@ -590,8 +590,9 @@ __device__ __forceinline__ void load_half_fp8_sparse(uint8_t* raw, const uint8_t
     const int i = ii * kWaves + wave;
     const int pos_all = i * 64 + lane;
     const int c = pos_all - (pos_all / kChunks) * kChunks;
-    const uint8_t* g =
-        id_in_pool(id[ii], ntok) ? kv + (int64_t)id[ii] * kTok + c * 16 : g_zero_row + (pos_all & 63) * 16;
+    const uint64_t rec = reinterpret_cast<uint64_t>(kv) + (uint64_t)((int64_t)id[ii] * kTok + c * 16);
+    const uint64_t zero = reinterpret_cast<uint64_t>(uni_ptr(g_zero_row)) + (uint32_t)((pos_all & 63) * 16);
+    const uint8_t* g = reinterpret_cast<const uint8_t*>(id_in_pool(id[ii], ntok) ? rec : zero);
     dma_glb16(lds_off(raw) + i * 1024, g);
   }
 }

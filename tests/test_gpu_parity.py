@@ -137,6 +137,20 @@ def test_fused_lse_short_rows():
 
 
 @gpu
+@pytest.mark.parametrize("log2_scale", [12, -12])
+def test_fused_query_scale(log2_scale):
+    """Fused decode of queries scaled by 2^12 (|q (.) w| past 2^14) and by
+    2^-12 (row RMS below 2^-8, where eps starts to matter): q-hat is
+    normalised before its fp16 rounding, so the bars are unchanged.  The
+    scaling is exact in bf16."""
+    import dataclasses
+    p = W.make_dense("fused_scaled", [1, 5, 70, 700], s_q=1, h_q=128, seed=31, fused=True)
+    q32 = (p.q.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** log2_scale)
+    q = (q32.view(np.uint32) >> 16).astype(np.uint16)
+    _parity(dataclasses.replace(p, q=q), num_slots=8, what=f"fused q*2^{log2_scale}")
+
+
+@gpu
 def test_metadata_bit_exact():
     torch = _torch_cuda()
     import mla_paged_kv_05_amd as mla
