@@ -1831,56 +1831,76 @@ __global__ void __launch_bounds__(64) k_combine(DecodeArgs a) {
   const int row = g * kRowsPerWg + wt * 32 + r32;
   const int64_t lstride = (int64_t)a.groups * kPartialLseFloats;
   const float* lsep = a.part_lse + (int64_t)s0 * lstride + (int64_t)g * kPartialLseFloats + wt * 32 + r32;
-  float m = -INFINITY, tot = 0.f;
-  for (int s = 0; s < ns; s += 8) {
-    float l[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) l[i] = s + i < ns ? lsep[(s + i) * lstride] : -INFINITY;
-    float mc = m;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) mc = fmaxf(mc, l[i]);
-    if (mc != -INFINITY) {
-      float t = m == -INFINITY ? 0.f : tot * expf(m - mc);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) t += l[i] == -INFINITY ? 0.f : expf(l[i] - mc);
-      tot = t;
-      m = mc;
-    }
-  }
-  const float lse = m == -INFINITY ? -INFINITY : m + logf(tot);
   const int64_t pstride = (int64_t)a.groups * kPartialOElems;
   const uint16_t* pb = a.part_o + (int64_t)s0 * pstride + (int64_t)g * kPartialOElems +
                        (size_t)((wt * 16 + mt) * 2) * 64 * 8 + (size_t)lane * 8;
+  // The first kInFlight splits' LSEs and partial chunks are read together
+  // (one round trip for the usual handful of splits); a sequence split over
+  // the whole machine (batch 1) has dozens, read kInFlight at a time after.
+  constexpr int kInFlight = 8;
+  float l[kInFlight];
+  uint4 v[kInFlight][2];
+#pragma unroll
+  for (int j = 0; j < kInFlight; ++j) {
+    const bool ok = j < ns;
+    l[j] = ok ? lsep[j * lstride] : -INFINITY;
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2)
+      v[j][q2] = ok ? *reinterpret_cast<const uint4*>(pb + j * pstride + q2 * 64 * 8) : make_uint4(0, 0, 0, 0);
+  }
+  // lse = ln sum_s e^{lse_s}, kInFlight splits at a time with a running
+  // maximum m and the sum tot of e^{lse_s - m}
+  float m = -INFINITY, tot = 0.f;
+  auto lse_group = [&](const float (&lj)[kInFlight]) {
+    float mc = m;
+#pragma unroll
+    for (int j = 0; j < kInFlight; ++j) mc = fmaxf(mc, lj[j]);
+    if (mc != -INFINITY) {
+      float t = m == -INFINITY ? 0.f : tot * expf(m - mc);
+#pragma unroll
+      for (int j = 0; j < kInFlight; ++j) t += lj[j] == -INFINITY ? 0.f : expf(lj[j] - mc);
+      tot = t;
+      m = mc;
+    }
+  };
+  lse_group(l);
+  for (int s = kInFlight; s < ns; s += kInFlight) {
+    float lx[kInFlight];
+#pragma unroll
+    for (int j = 0; j < kInFlight; ++j) lx[j] = s + j < ns ? lsep[(s + j) * lstride] : -INFINITY;
+    lse_group(lx);
+  }
+  const float lse = m == -INFINITY ? -INFINITY : m + logf(tot);
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  auto accumulate = [&](const float (&lj)[kInFlight], const uint4 (&vj)[kInFlight][2]) {
+#pragma unroll
+    for (int j = 0; j < kInFlight; ++j) {
+      const float w = lj[j] == -INFINITY ? 0.f : expf(lj[j] - lse);
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const uint32_t u[4] = {vj[j][q2].x, vj[j][q2].y, vj[j][q2].z, vj[j][q2].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[8 * q2 + 2 * e] += w * __uint_as_float(u[e] << 16);
+          acc[8 * q2 + 2 * e + 1] += w * __uint_as_float(u[e] & 0xffff0000u);
+        }
+      }
+    }
+  };
   if (m != -INFINITY) {
-    // kInFlight splits' chunks in flight at a time: a sequence split over
-    // the whole machine (batch 1) has dozens of splits
-    constexpr int kInFlight = 8;
-    for (int s = 0; s < ns; s += kInFlight) {
-      uint4 v[kInFlight][2];
-      float w[kInFlight];
+    accumulate(l, v);
+    for (int s = kInFlight; s < ns; s += kInFlight) {
 #pragma unroll
       for (int j = 0; j < kInFlight; ++j) {
         const bool ok = s + j < ns;
-        const float l = ok ? lsep[(s + j) * lstride] : -INFINITY;
-        w[j] = l == -INFINITY ? 0.f : expf(l - lse);
+        l[j] = ok ? lsep[(s + j) * lstride] : -INFINITY;
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2)
           v[j][q2] = ok ? *reinterpret_cast<const uint4*>(pb + (s + j) * pstride + q2 * 64 * 8) : make_uint4(0, 0, 0, 0);
       }
-#pragma unroll
-      for (int j = 0; j < kInFlight; ++j)
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          const uint32_t u[4] = {v[j][q2].x, v[j][q2].y, v[j][q2].z, v[j][q2].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[8 * q2 + 2 * e] += w[j] * __uint_as_float(u[e] << 16);
-            acc[8 * q2 + 2 * e + 1] += w[j] * __uint_as_float(u[e] & 0xffff0000u);
-          }
-        }
+      accumulate(l, v);
     }
   }
   if constexpr (FP32OUT) {
