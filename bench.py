@@ -193,6 +193,8 @@ def main():
     sl = torch.from_numpy(np.ascontiguousarray(p.seqlens)).to(dev)
     idx = None if p.indices is None else torch.from_numpy(p.indices).to(dev)
     topk = p.topk if idx is not None else 0
+    # the fused decode's query prologue costs about four items per piece
+    piece_cost = B.PIECE_COST_FUSED if p.fused else 0
     rows = p.s_q * p.h_q
     lib = B.load_library()
     S = B.num_sched_slots(rows, dev)
@@ -233,7 +235,7 @@ def main():
         # capturing stream
         pr = params[i % R]
         sh = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-        st = lib.mla_get_metadata(sl_p, p.batch, rows, 1, topk, S, meta_p, ns_p, sh)
+        st = lib.mla_get_metadata(sl_p, p.batch, rows, 1, topk, S, piece_cost, meta_p, ns_p, sh)
         if kev is not None:
             st |= lib.mla_decode_timed(ctypes.byref(pr), sh, kev[0], kev[1])
         else:
@@ -299,7 +301,7 @@ def main():
     mevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for i in range(args.steps):
         mevs[i][0].record(stream)
-        st = lib.mla_get_metadata(sl_p, p.batch, rows, 1, topk, S, meta_p, ns_p,
+        st = lib.mla_get_metadata(sl_p, p.batch, rows, 1, topk, S, piece_cost, meta_p, ns_p,
                                   ctypes.c_void_p(stream.cuda_stream))
         mevs[i][1].record(stream)
         if st != 0:
@@ -355,7 +357,8 @@ def main():
         "vs_baseline": None, "dtype": compute_dtype, "data": "synthetic (seeded, shaped like the workload)",
         "config": {"workload": p.name, "batch": p.batch, "s_q": p.s_q, "h_q": p.h_q, "d_qk": p.d_qk,
                    "d_v": 512, "page": 64, "kv_format": p.kv_format, "causal": bool(p.causal),
-                   "sparse_topk": topk, "fused": bool(p.fused), "parallelism": "single GPU",
+                   "sparse_topk": topk, "fused": bool(p.fused), "sched_piece_cost": piece_cost,
+                   "parallelism": "single GPU",
                    "kv_copies_rotated": R,
                    "launch": "eager" if graphs is None else "hipGraph per step (metadata, decode, combine)",
                    "combine": "separate launch"},

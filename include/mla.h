@@ -71,6 +71,11 @@ typedef enum {
 #define MLA_D_QK_V41 512
 #define MLA_D_V 512
 #define MLA_MAX_BATCH 16384
+/* Piece cost (in 64-key items) that suits the fused decode, whose query
+ * prologue (RMSNorm, RoPE, q-hat) costs about four items: mla_get_metadata's
+ * piece_cost for metadata that fused decode calls will use. */
+#define MLA_PIECE_COST_FUSED 4
+#define MLA_MAX_PIECE_COST 64
 
 /* [host] Number of scheduler slots S to use on `device` for decode calls
  * with `rows_per_kv_head` = s_q*h_q/h_kv query rows: one slot per compute
@@ -88,25 +93,30 @@ size_t mla_num_splits_ints(int32_t batch);      /* = batch + 1      */
  *   h_kv              must be 1
  *   topk              0 = dense; > 0: sparse with topk indices per query row
  *   num_slots         S, normally mla_num_sched_slots()
+ *   piece_cost        F below, in 64-key items: 0 = the default
+ *                     max(1, ceil(min(rows,128)/64)) (about two for 128 rows,
+ *                     a plain piece's query load, pipeline fill and
+ *                     finalize), else 1..MLA_MAX_PIECE_COST
+ *                     (MLA_PIECE_COST_FUSED for the fused decode)
  *   sched_meta        int32 [S][8] out: per slot {b0, j0, b1, j1_end, k0, items, 0, 0}
  *   num_splits        int32 [mla_num_splits_ints(batch)] out: [0..batch] prefix
  *                     offsets of per-sequence splits (sequence b has
  *                     num_splits[b+1] - num_splits[b] of them)
  * The split rule: a sequence has n_b = ceil(len/64) work items (ceil(topk/64)
- * when sparse; an empty sequence keeps one item with no KV); with
- * F = max(1, ceil(min(rows,128)/64)) (a piece's fixed cost -- query load,
- * pipeline fill and finalize -- in items: about two for 128 rows), the
- * items are laid on a line where
+ * when sparse; an empty sequence keeps one item with no KV); with F the
+ * piece cost (a piece's fixed cost in items), the items are laid on a line
+ * where
  * sequence b starts at U_b = sum_{b'<b}(F + n_b') and its item j sits at
  * U_b + F + j; with cap = ceil((U_batch+1)/S), slot s takes the items at
  * positions [s*cap, (s+1)*cap).  A small total (U_batch < S) thus gives
  * every item a slot of its own, so even one sequence spreads over the
- * machine.  Errors: INVALID_ARG for null pointers or bad sizes,
+ * machine.  Errors: INVALID_ARG for null pointers, bad sizes or a piece
+ * cost outside [0, MLA_MAX_PIECE_COST],
  * UNSUPPORTED for h_kv != 1 or batch > MLA_MAX_BATCH. */
 mla_status mla_get_metadata(const int32_t* cache_seqlens, int32_t batch,
                             int32_t rows_per_kv_head, int32_t h_kv, int32_t topk,
-                            int32_t num_slots, int32_t* sched_meta, int32_t* num_splits,
-                            void* stream);
+                            int32_t num_slots, int32_t piece_cost, int32_t* sched_meta,
+                            int32_t* num_splits, void* stream);
 
 /* [host] Workspace bytes a decode call needs: split partials, O in bf16
  * (128 rows x 512 per row group) and LSE in fp32 (128 per row group). */

@@ -100,7 +100,7 @@ def load_library(path: str = LIB_PATH):
     lib.mla_num_splits_ints.argtypes = [c.c_int32]
     lib.mla_get_metadata.restype = c.c_int
     lib.mla_get_metadata.argtypes = [c.c_void_p, c.c_int32, c.c_int32, c.c_int32, c.c_int32,
-                                     c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p]
+                                     c.c_int32, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p]
     lib.mla_workspace_bytes.restype = c.c_size_t
     lib.mla_workspace_bytes.argtypes = [c.c_int32, c.c_int32, c.c_int32, c.c_int32]
     lib.mla_decode.restype = c.c_int
@@ -144,10 +144,15 @@ def num_sched_slots(rows_per_kv_head: int, device=None) -> int:
     return n
 
 
+# Piece cost for metadata that fused decode calls use (MLA_PIECE_COST_FUSED).
+PIECE_COST_FUSED = 4
+
+
 def get_mla_metadata(cache_seqlens: torch.Tensor, rows_per_kv_head: int, h_kv: int = 1,
-                     topk: int = 0, num_slots: Optional[int] = None):
+                     topk: int = 0, num_slots: Optional[int] = None, piece_cost: int = 0):
     """Split-KV schedule for one decoding step: (sched_meta int32 [S][8],
-    num_splits int32 [batch+1]), both on cache_seqlens' device."""
+    num_splits int32 [batch+1]), both on cache_seqlens' device.  piece_cost
+    0 takes the default piece cost; PIECE_COST_FUSED suits fused decodes."""
     lib = load_library()
     dev = cache_seqlens.device
     if cache_seqlens.dim() != 1:
@@ -160,7 +165,7 @@ def get_mla_metadata(cache_seqlens: torch.Tensor, rows_per_kv_head: int, h_kv: i
     meta = torch.empty((S, 8), dtype=torch.int32, device=dev)
     ns = torch.empty(int(lib.mla_num_splits_ints(B)), dtype=torch.int32, device=dev)
     _check(lib.mla_get_metadata(_ptr(cache_seqlens), B, int(rows_per_kv_head), int(h_kv), int(topk),
-                                S, _ptr(meta), _ptr(ns), _stream(dev)))
+                                S, int(piece_cost), _ptr(meta), _ptr(ns), _stream(dev)))
     return meta, ns
 
 

@@ -74,18 +74,19 @@ size_t mla_sched_meta_ints(int32_t num_slots) { return num_slots > 0 ? 8 * (size
 size_t mla_num_splits_ints(int32_t batch) { return batch >= 0 ? mla::splits_ints(batch) : 0; }
 
 mla_status mla_get_metadata(const int32_t* cache_seqlens, int32_t batch, int32_t rows_per_kv_head,
-                            int32_t h_kv, int32_t topk, int32_t num_slots, int32_t* sched_meta,
-                            int32_t* num_splits, void* stream) {
-  if (batch < 0 || rows_per_kv_head < 1 || num_slots < 1 || topk < 0)
-    return fail(MLA_ERR_INVALID_ARG, "mla_get_metadata: batch=%d rows=%d num_slots=%d topk=%d",
-                batch, rows_per_kv_head, num_slots, topk);
+                            int32_t h_kv, int32_t topk, int32_t num_slots, int32_t piece_cost,
+                            int32_t* sched_meta, int32_t* num_splits, void* stream) {
+  if (batch < 0 || rows_per_kv_head < 1 || num_slots < 1 || topk < 0 || piece_cost < 0 ||
+      piece_cost > MLA_MAX_PIECE_COST)
+    return fail(MLA_ERR_INVALID_ARG, "mla_get_metadata: batch=%d rows=%d num_slots=%d topk=%d piece_cost=%d",
+                batch, rows_per_kv_head, num_slots, topk, piece_cost);
   if (h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "mla_get_metadata: h_kv=%d (only 1)", h_kv);
   if (batch > MLA_MAX_BATCH)
     return fail(MLA_ERR_UNSUPPORTED, "mla_get_metadata: batch %d > %d", batch, MLA_MAX_BATCH);
   if (!sched_meta || !num_splits || (batch > 0 && !cache_seqlens))
     return fail(MLA_ERR_INVALID_ARG, "mla_get_metadata: null pointer");
-  hipError_t e = mla::launch_sched(cache_seqlens, batch, rows_per_kv_head, topk, num_slots,
-                                   sched_meta, num_splits, (hipStream_t)stream);
+  hipError_t e = mla::launch_sched(cache_seqlens, batch, mla::sched_piece_cost(rows_per_kv_head, piece_cost),
+                                   topk, num_slots, sched_meta, num_splits, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "mla_get_metadata launch");
   return MLA_OK;
 }

@@ -17,9 +17,11 @@ constexpr int kFp8TokenBytes = 656;
 constexpr int kMaxBatch = 16384;
 constexpr int kMaxRows = 65536;
 
-// Piece cost F of the split rule (in KV-block units): a piece's query load,
-// pipeline fill and finalize cost about two 64-key items at 128 rows.
-inline int sched_piece_cost(int rows) {
+// Piece cost F of the split rule (in 64-key items): the caller's value, or
+// by default ceil(min(rows, 128) / 64), about two items at 128 rows (a
+// plain piece's query load, pipeline fill and finalize).
+inline int sched_piece_cost(int rows, int piece_cost) {
+  if (piece_cost > 0) return piece_cost;
   int m = rows < kRowsPerWg ? rows : kRowsPerWg;
   int f = (m + 63) / 64;
   return f < 1 ? 1 : f;
@@ -66,7 +68,7 @@ constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 // Device address of the current device's scratch array (looked up once).
 hipError_t noalloc_scratch(void** ptr);
 
-hipError_t launch_sched(const int32_t* seqlens, int batch, int rows, int topk, int num_slots,
+hipError_t launch_sched(const int32_t* seqlens, int batch, int piece_cost, int topk, int num_slots,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool fused,
                          hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);

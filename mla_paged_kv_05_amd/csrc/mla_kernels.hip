@@ -329,18 +329,13 @@ __device__ int block_scan_exclusive(int v, int* wsum, int* total) {
 
 template <int NT, int MAXB>
 __global__ void __launch_bounds__(NT)
-k_sched(const int32_t* __restrict__ seqlens, int B, int rows, int topk, int S,
+k_sched(const int32_t* __restrict__ seqlens, int B, int F, int topk, int S,
         int32_t* __restrict__ meta, int32_t* __restrict__ num_splits) {
   constexpr int kSchedThreads = NT;
   __shared__ int32_t U[MAXB + 1];   // cost prefix: start of sequence b on the line
   __shared__ int32_t I[MAXB + 1];   // item prefix
   __shared__ int wsum[NT / 64];
   const int tid = threadIdx.x;
-  const int F = [&] {
-    int m = rows < kRowsPerWg ? rows : kRowsPerWg;
-    int f = (m + 63) / 64;
-    return f < 1 ? 1 : f;
-  }();
   const int per = (B + kSchedThreads - 1) / kSchedThreads;
   const int lo = tid * per, hi = min(B, lo + per);
   auto nblk = [&](int b) -> int {
@@ -1977,13 +1972,13 @@ __global__ void __launch_bounds__(kThreads) k_debug_gather(DecodeArgs a, int b, 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_sched(const int32_t* seqlens, int batch, int rows, int topk, int num_slots,
+hipError_t launch_sched(const int32_t* seqlens, int batch, int piece_cost, int topk, int num_slots,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream) {
   if (batch <= kSchedSmallBatch)
-    hipLaunchKernelGGL((k_sched<256, kSchedSmallBatch>), dim3(1), dim3(256), 0, stream, seqlens, batch, rows,
-                       topk, num_slots, meta, num_splits);
+    hipLaunchKernelGGL((k_sched<256, kSchedSmallBatch>), dim3(1), dim3(256), 0, stream, seqlens, batch,
+                       piece_cost, topk, num_slots, meta, num_splits);
   else
-    hipLaunchKernelGGL((k_sched<1024, kMaxBatch>), dim3(1), dim3(1024), 0, stream, seqlens, batch, rows,
+    hipLaunchKernelGGL((k_sched<1024, kMaxBatch>), dim3(1), dim3(1024), 0, stream, seqlens, batch, piece_cost,
                        topk, num_slots, meta, num_splits);
   return hipGetLastError();
 }

@@ -54,7 +54,8 @@ def run(name: str, warmup: int = 6) -> str:
     idx = None if p.indices is None else torch.from_numpy(p.indices).to(dev)
     rows = p.s_q * p.h_q
     S = B.num_sched_slots(rows, dev)
-    meta, ns = B.get_mla_metadata(sl, rows, 1, topk=p.topk if idx is not None else 0, num_slots=S)
+    meta, ns = B.get_mla_metadata(sl, rows, 1, topk=p.topk if idx is not None else 0, num_slots=S,
+                                  piece_cost=B.PIECE_COST_FUSED if p.fused else 0)
     fz = None
     if p.fused:
         fz = {"norm_weight": torch.from_numpy(p.norm_w.view(np.int16)).view(torch.bfloat16).to(dev),

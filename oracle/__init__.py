@@ -90,7 +90,7 @@ def _load():
                                           P(ctypes.c_double), P(ctypes.c_double)]
     lib.orc_sched_plan.restype = ctypes.c_int
     lib.orc_sched_plan.argtypes = [P(ctypes.c_int32), ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_int, P(ctypes.c_int32), P(ctypes.c_int32)]
+                                   ctypes.c_int, ctypes.c_int, P(ctypes.c_int32), P(ctypes.c_int32)]
     _lib = lib
     return lib
 
@@ -253,15 +253,16 @@ def decode_row_subset(p, b, t, h, key_pos):
     return o, float(lse[0])
 
 
-def sched_plan(seqlens, rows, topk, num_slots):
-    """The split-KV plan: (meta int32 [S][8], num_splits int32 [B+1])."""
+def sched_plan(seqlens, rows, topk, num_slots, piece_cost=0):
+    """The split-KV plan: (meta int32 [S][8], num_splits int32 [B+1]);
+    piece_cost 0 takes the default piece cost."""
     lib = _load()
     sl = np.ascontiguousarray(seqlens, dtype=np.int32)
     B = int(sl.shape[0])
     meta = np.zeros((num_slots, 8), dtype=np.int32)
     ns = np.zeros(B + 1, dtype=np.int32)
     rc = lib.orc_sched_plan(sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), B, int(rows),
-                            int(topk), int(num_slots),
+                            int(topk), int(num_slots), int(piece_cost),
                             meta.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                             ns.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
     if rc != 0:

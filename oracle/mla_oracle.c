@@ -378,7 +378,7 @@ int orc_decode_row_subset(const orc_problem* p, int b, int t, int h, int64_t n,
 /* ------------------------------------------------------------------ */
 /*
  * n_b   = ceil(topk/64) if topk > 0 else ceil(seqlens[b]/64)   (work items)
- * F     = max(1, ceil(min(M,128)/64))                            (piece cost)
+ * F     = piece_cost if > 0, else max(1, ceil(min(M,128)/64))     (piece cost)
  * U_0 = 0, U_{b+1} = U_b + F + n_b, T = U_B
  * cap   = ceil((T+1)/S)
  * Batch b has max(n_b,1) items; item j sits at P(b,j) = U_b + F + j and
@@ -389,11 +389,11 @@ int orc_decode_row_subset(const orc_problem* p, int b, int t, int h, int64_t n,
  * last (b1,j1) item of slot s, k0 = s - floor(P(b0,0)/cap) being the split
  * index of batch b0 that slot s computes; an empty slot is {-1,0,-1,0,0,0,0,0}.
  */
-int orc_sched_plan(const int32_t* seqlens, int B, int M, int topk, int S, int32_t* meta,
-                   int32_t* num_splits) {
-  if (B < 0 || S < 1 || M < 1) return 1;
+int orc_sched_plan(const int32_t* seqlens, int B, int M, int topk, int S, int piece_cost,
+                   int32_t* meta, int32_t* num_splits) {
+  if (B < 0 || S < 1 || M < 1 || piece_cost < 0) return 1;
   int mm = M < 128 ? M : 128;
-  int64_t F = (mm + 63) / 64;
+  int64_t F = piece_cost > 0 ? piece_cost : (mm + 63) / 64;
   if (F < 1) F = 1;
   int64_t* U = (int64_t*)malloc(sizeof(int64_t) * (size_t)(B + 1));
   int64_t* nb = (int64_t*)malloc(sizeof(int64_t) * (size_t)(B > 0 ? B : 1));

@@ -40,11 +40,12 @@ def upload(p, dev="cuda:0"):
 def run(p, t=None, num_slots=None):
     """Metadata + decode on the GPU; returns numpy results."""
     import mla_paged_kv_05_amd as mla
+    from mla_paged_kv_05_amd import binding
 
     if t is None:
         t = upload(p)
     meta, ns = mla.get_mla_metadata(t["seqlens"], p.s_q * p.h_q, 1, topk=p.topk if p.indices is not None else 0,
-                                    num_slots=num_slots)
+                                    num_slots=num_slots, piece_cost=binding.PIECE_COST_FUSED if p.fused else 0)
     fused = None
     if p.fused:
         fused = {"norm_weight": t["norm_w"], "eps": p.eps, "rope_base": p.rope_base}

@@ -134,12 +134,14 @@ def test_row_groups_need_slots_multiple_of_8():
 def test_metadata_rejects():
     lib = B.load_library()
     a = Fake.ADDR
-    assert lib.mla_get_metadata(a, 4, 128, 2, 0, 8, a, a, None) == 2
-    assert lib.mla_get_metadata(a, 4, 0, 1, 0, 8, a, a, None) == 1
-    assert lib.mla_get_metadata(a, 4, 128, 1, 0, 0, a, a, None) == 1
-    assert lib.mla_get_metadata(None, 4, 128, 1, 0, 8, a, a, None) == 1
-    assert lib.mla_get_metadata(a, 20000, 128, 1, 0, 8, a, a, None) == 2
-    assert lib.mla_get_metadata(a, 4, 128, 1, -1, 8, a, a, None) == 1
+    assert lib.mla_get_metadata(a, 4, 128, 2, 0, 8, 0, a, a, None) == 2
+    assert lib.mla_get_metadata(a, 4, 0, 1, 0, 8, 0, a, a, None) == 1
+    assert lib.mla_get_metadata(a, 4, 128, 1, 0, 0, 0, a, a, None) == 1
+    assert lib.mla_get_metadata(None, 4, 128, 1, 0, 8, 0, a, a, None) == 1
+    assert lib.mla_get_metadata(a, 20000, 128, 1, 0, 8, 0, a, a, None) == 2
+    assert lib.mla_get_metadata(a, 4, 128, 1, -1, 8, 0, a, a, None) == 1
+    assert lib.mla_get_metadata(a, 4, 128, 1, 0, 8, -1, a, a, None) == 1   # piece cost below 0
+    assert lib.mla_get_metadata(a, 4, 128, 1, 0, 8, 65, a, a, None) == 1   # above MLA_MAX_PIECE_COST
 
 
 def test_zero_batch_is_a_noop():

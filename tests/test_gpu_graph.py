@@ -29,7 +29,7 @@ def _step_fn(torch, lib, B, p, t, S):
 
     def step():
         sh = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-        st = lib.mla_get_metadata(ctypes.c_void_p(t["seqlens"].data_ptr()), p.batch, rows, 1, topk, S,
+        st = lib.mla_get_metadata(ctypes.c_void_p(t["seqlens"].data_ptr()), p.batch, rows, 1, topk, S, 0,
                                   ctypes.c_void_p(meta.data_ptr()), ctypes.c_void_p(ns.data_ptr()), sh)
         st |= lib.mla_decode(ctypes.byref(pr), sh)
         st |= lib.mla_combine(ctypes.byref(pr), sh)

@@ -160,12 +160,16 @@ def test_metadata_bit_exact():
              (list(rng.integers(0, 3000, 2000)), 32, 0, 256), ([], 128, 0, 8),
              # the one-wave scheduler's largest batch, and the first on 1024 threads
              (list(rng.integers(0, 9000, 256)), 128, 0, 256), (list(rng.integers(0, 9000, 257)), 128, 0, 256)]
-    for sl, rows, topk, S in cases:
-        say(f"metadata B={len(sl)} rows={rows} topk={topk} S={S}")
+    # with the default piece cost, then with explicit ones (the fused decode's 4, a large 64)
+    cases = [c + (0,) for c in cases] + [(list(rng.integers(2048, 16385, 32)), 128, 0, 256, 4),
+                                         ([3000], 128, 0, 256, 4), (list(rng.integers(0, 9000, 64)), 128, 0, 256, 64),
+                                         ([7] * 64, 128, 2048, 256, 3)]
+    for sl, rows, topk, S, pc in cases:
+        say(f"metadata B={len(sl)} rows={rows} topk={topk} S={S} piece_cost={pc}")
         t = torch.tensor(np.array(sl, dtype=np.int32), device="cuda:0")
-        meta, ns = mla.get_mla_metadata(t, rows, 1, topk=topk, num_slots=S)
+        meta, ns = mla.get_mla_metadata(t, rows, 1, topk=topk, num_slots=S, piece_cost=pc)
         torch.cuda.synchronize()
-        rm, rn = oracle.sched_plan(np.array(sl, dtype=np.int32), rows, topk, S)
+        rm, rn = oracle.sched_plan(np.array(sl, dtype=np.int32), rows, topk, S, piece_cost=pc)
         assert np.array_equal(meta.cpu().numpy(), rm)
         assert np.array_equal(ns.cpu().numpy(), rn)
 
@@ -316,7 +320,7 @@ def test_decode_timed_matches_decode():
     meta = torch.empty((S, 8), dtype=torch.int32, device="cuda:0")
     ns = torch.empty(int(lib.mla_num_splits_ints(p.batch)), dtype=torch.int32, device="cuda:0")
     sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    assert lib.mla_get_metadata(ctypes.c_void_p(t["seqlens"].data_ptr()), p.batch, 128, 1, 0, S,
+    assert lib.mla_get_metadata(ctypes.c_void_p(t["seqlens"].data_ptr()), p.batch, 128, 1, 0, S, 0,
                                 ctypes.c_void_p(meta.data_ptr()), ctypes.c_void_p(ns.data_ptr()), sh) == 0
     ws = torch.empty(B.workspace_bytes(p.batch, 1, 128, S), dtype=torch.uint8, device="cuda:0")
     outs = []

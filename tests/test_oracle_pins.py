@@ -462,12 +462,17 @@ def test_fused_pipeline_order_and_cast():
 
 
 # ----------------------------------------------------------- scheduler
-def sched_check(seqlens, rows, topk, S):
-    meta, ns = oracle.sched_plan(seqlens, rows, topk, S)
+def sched_check(seqlens, rows, topk, S, piece_cost=0):
+    meta, ns = oracle.sched_plan(seqlens, rows, topk, S, piece_cost=piece_cost)
     B = len(seqlens)
     nb = [(-(-topk // 64)) if topk else -(-max(int(L), 0) // 64) for L in seqlens]
     items = [max(n, 1) for n in nb]
-    F = max(1, -(-min(rows, 128) // 64))
+    F = piece_cost if piece_cost > 0 else max(1, -(-min(rows, 128) // 64))
+    # the rule itself: item j of sequence b sits at U_b + F + j on the line
+    # and belongs to slot floor(position / cap)
+    U = np.concatenate([[0], np.cumsum([F + n for n in nb])])
+    line_cap = -(-(int(U[-1]) + 1) // S)
+    slot_of = {(b, j): (int(U[b]) + F + j) // line_cap for b in range(B) for j in range(items[b])}
     # walk the slots: every (b, item) exactly once, in order, contiguous
     seen = []
     for s in range(S):
@@ -481,6 +486,7 @@ def sched_check(seqlens, rows, topk, S):
             hi = j1 if b == b1 else items[b]
             run += [(b, j) for j in range(lo, hi)]
         assert len(run) == cnt
+        assert all(slot_of[x] == s for x in run)
         cost = len(run) + F * sum(1 for (b, j) in run if j == 0)
         tot = sum(items) + F * B
         cap = -(-(tot + 1) // S)
@@ -520,6 +526,30 @@ def sched_check(seqlens, rows, topk, S):
 ])
 def test_sched_plan_invariants(seqlens, rows, topk, S):
     sched_check(np.array(seqlens, dtype=np.int32), rows, topk, S)
+
+
+@pytest.mark.parametrize("seqlens,rows,topk,S,piece_cost", [
+    ([2048, 16384, 0, 9000], 128, 0, 64, 4),   # the fused decode's piece cost
+    ([3000], 128, 0, 256, 4),                  # one sequence still spreads item by item
+    (list(range(0, 4000, 97)), 128, 0, 256, 1),
+    ([10] * 64, 128, 2048, 256, 3),
+    ([65536] * 3 + [300] * 20, 256, 0, 128, 64),
+])
+def test_sched_plan_piece_cost(seqlens, rows, topk, S, piece_cost):
+    sched_check(np.array(seqlens, dtype=np.int32), rows, topk, S, piece_cost)
+
+
+def test_sched_piece_cost_moves_the_plan():
+    """A larger piece cost gives the sequences' first items more room on the
+    line: fewer items go to the slots that start a piece."""
+    sl = np.random.default_rng(5).integers(2048, 16385, 32).astype(np.int32)
+    m2, n2 = oracle.sched_plan(sl, 128, 0, 256, piece_cost=2)
+    m4, n4 = oracle.sched_plan(sl, 128, 0, 256, piece_cost=4)
+    assert not np.array_equal(m2, m4)
+    starts = lambda m: [int(r[5]) for r in m if r[0] >= 0 and r[1] == 0]  # slots whose run starts a sequence
+    assert np.mean(starts(m4)) < np.mean(starts(m2))
+    with pytest.raises(ValueError):
+        oracle.sched_plan(sl, 128, 0, 256, piece_cost=-1)
 
 
 def test_sched_plan_workload_sizes():
