@@ -1805,9 +1805,14 @@ __global__ void __launch_bounds__(256) k_fused_epilogue(DecodeArgs a) {
   }
 }
 
-// The combine: one 64-lane workgroup per (sequence b, row group g,
-// 32-row tile wt, 32-dim tile mt), so that even one sequence with many
-// splits spreads over many CUs.  Lane l takes the place of the decode's
+// Row groups (batch x groups) up to which the combine gives each tile four
+// waves: fewer sequences over the same slots means more splits each.
+constexpr int kCombineWideRowGroups = 8;
+
+// The combine: one workgroup per (sequence b, row group g, 32-row tile
+// wt, 32-dim tile mt), so that even one sequence with many splits spreads
+// over many CUs; one wave, or (few row groups, many splits) four that
+// share the tile's splits.  Lane l takes the place of the decode's
 // lane l: row 32wt + l%32 and the 16 values of d-tile mt it held, two
 // 16-byte chunks per split (the partials are stored in that order).
 //   lse = ln sum_s e^{lse_s};  O = sum_s e^{lse_s - lse} O_s,
@@ -1816,32 +1821,40 @@ __global__ void __launch_bounds__(256) k_fused_epilogue(DecodeArgs a) {
 // over the tile's own slices of splits s0 and s0+1, which no other
 // workgroup reads (lane l rewrites exactly the four chunks it read there),
 // for k_fused_epilogue; the LSE is written either way.
-template <bool FP32OUT>
-__global__ void __launch_bounds__(64) k_combine(DecodeArgs a) {
+template <bool FP32OUT, int NW>
+__global__ void __launch_bounds__(64 * NW) k_combine(DecodeArgs a) {
   const int mt = blockIdx.x & 15, wt = (blockIdx.x >> 4) & 3;
   const int g = (blockIdx.x >> 6) % a.groups, b = (blockIdx.x >> 6) / a.groups;
   const int s0 = a.num_splits[b], ns = a.num_splits[b + 1] - s0;
   if (ns <= 1) return;
-  const int lane = threadIdx.x, half = lane >> 5, r32 = lane & 31;
+  // NW waves share the tile: wave w takes splits w, w + NW, ... and the
+  // waves' LSE sums and weighted partials are added through LDS
+  const int w = NW > 1 ? (int)(threadIdx.x >> 6) : 0;
+  const int lane = threadIdx.x & 63, half = lane >> 5, r32 = lane & 31;
   const int row = g * kRowsPerWg + wt * 32 + r32;
   const int64_t lstride = (int64_t)a.groups * kPartialLseFloats;
-  const float* lsep = a.part_lse + (int64_t)s0 * lstride + (int64_t)g * kPartialLseFloats + wt * 32 + r32;
+  const float* lsep0 = a.part_lse + (int64_t)s0 * lstride + (int64_t)g * kPartialLseFloats + wt * 32 + r32;
   const int64_t pstride = (int64_t)a.groups * kPartialOElems;
   const uint16_t* pb = a.part_o + (int64_t)s0 * pstride + (int64_t)g * kPartialOElems +
                        (size_t)((wt * 16 + mt) * 2) * 64 * 8 + (size_t)lane * 8;
-  // The first kInFlight splits' LSEs and partial chunks are read together
-  // (one round trip for the usual handful of splits); a sequence split over
-  // the whole machine (batch 1) has dozens, read kInFlight at a time after.
+  const int nsw = ns > w ? (ns - w + NW - 1) / NW : 0;  // this wave's splits
+  const float* lsep = lsep0 + w * lstride;
+  const uint16_t* pbw = pb + w * pstride;
+  const int64_t lstep = lstride * NW, pstep = pstride * NW;
+  // The first kInFlight of the wave's splits: LSEs and partial chunks are
+  // read together (one round trip for the usual handful of splits); more
+  // splits (batch 1 spreads one sequence over the machine) follow
+  // kInFlight at a time.
   constexpr int kInFlight = 8;
   float l[kInFlight];
   uint4 v[kInFlight][2];
 #pragma unroll
   for (int j = 0; j < kInFlight; ++j) {
-    const bool ok = j < ns;
-    l[j] = ok ? lsep[j * lstride] : -INFINITY;
+    const bool ok = j < nsw;
+    l[j] = ok ? lsep[j * lstep] : -INFINITY;
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2)
-      v[j][q2] = ok ? *reinterpret_cast<const uint4*>(pb + j * pstride + q2 * 64 * 8) : make_uint4(0, 0, 0, 0);
+      v[j][q2] = ok ? *reinterpret_cast<const uint4*>(pbw + j * pstep + q2 * 64 * 8) : make_uint4(0, 0, 0, 0);
   }
   // lse = ln sum_s e^{lse_s}, kInFlight splits at a time with a running
   // maximum m and the sum tot of e^{lse_s - m}
@@ -1859,11 +1872,27 @@ __global__ void __launch_bounds__(64) k_combine(DecodeArgs a) {
     }
   };
   lse_group(l);
-  for (int s = kInFlight; s < ns; s += kInFlight) {
+  for (int s = kInFlight; s < nsw; s += kInFlight) {
     float lx[kInFlight];
 #pragma unroll
-    for (int j = 0; j < kInFlight; ++j) lx[j] = s + j < ns ? lsep[(s + j) * lstride] : -INFINITY;
+    for (int j = 0; j < kInFlight; ++j) lx[j] = s + j < nsw ? lsep[(s + j) * lstep] : -INFINITY;
     lse_group(lx);
+  }
+  if constexpr (NW > 1) {
+    __shared__ float red_m[NW][64], red_t[NW][64];
+    red_m[w][lane] = m;
+    red_t[w][lane] = tot;
+    __syncthreads();
+    float mm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) mm = fmaxf(mm, red_m[i][lane]);
+    float tt = 0.f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) tt += red_m[i][lane] == -INFINITY ? 0.f : red_t[i][lane] * expf(red_m[i][lane] - mm);
+    }
+    m = mm;
+    tot = tt;
   }
   const float lse = m == -INFINITY ? -INFINITY : m + logf(tot);
   float acc[16];
@@ -1872,31 +1901,46 @@ __global__ void __launch_bounds__(64) k_combine(DecodeArgs a) {
   auto accumulate = [&](const float (&lj)[kInFlight], const uint4 (&vj)[kInFlight][2]) {
 #pragma unroll
     for (int j = 0; j < kInFlight; ++j) {
-      const float w = lj[j] == -INFINITY ? 0.f : expf(lj[j] - lse);
+      const float wj = lj[j] == -INFINITY ? 0.f : expf(lj[j] - lse);
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         const uint32_t u[4] = {vj[j][q2].x, vj[j][q2].y, vj[j][q2].z, vj[j][q2].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[8 * q2 + 2 * e] += w * __uint_as_float(u[e] << 16);
-          acc[8 * q2 + 2 * e + 1] += w * __uint_as_float(u[e] & 0xffff0000u);
+          acc[8 * q2 + 2 * e] += wj * __uint_as_float(u[e] << 16);
+          acc[8 * q2 + 2 * e + 1] += wj * __uint_as_float(u[e] & 0xffff0000u);
         }
       }
     }
   };
   if (m != -INFINITY) {
     accumulate(l, v);
-    for (int s = kInFlight; s < ns; s += kInFlight) {
+    for (int s = kInFlight; s < nsw; s += kInFlight) {
 #pragma unroll
       for (int j = 0; j < kInFlight; ++j) {
-        const bool ok = s + j < ns;
-        l[j] = ok ? lsep[(s + j) * lstride] : -INFINITY;
+        const bool ok = s + j < nsw;
+        l[j] = ok ? lsep[(s + j) * lstep] : -INFINITY;
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2)
-          v[j][q2] = ok ? *reinterpret_cast<const uint4*>(pb + (s + j) * pstride + q2 * 64 * 8) : make_uint4(0, 0, 0, 0);
+          v[j][q2] = ok ? *reinterpret_cast<const uint4*>(pbw + (s + j) * pstep + q2 * 64 * 8) : make_uint4(0, 0, 0, 0);
       }
       accumulate(l, v);
     }
+  }
+  if constexpr (NW > 1) {
+    // waves 1.. hand their sums to wave 0, which writes the tile (after
+    // this barrier no wave reads a partial any more)
+    __shared__ float red_acc[NW - 1][16][64];
+    if (w > 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red_acc[w - 1][i][lane] = acc[i];
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int k = 0; k < NW - 1; ++k)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += red_acc[k][i][lane];
   }
   if constexpr (FP32OUT) {
     // chunk k (split s0 + (k & 1), 16-byte chunk k >> 1) takes values 4k .. 4k+3
@@ -2016,13 +2060,18 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_format, bool sparse, bool f
 hipError_t launch_combine(const DecodeArgs& a, bool fused, hipStream_t stream) {
   const int grid = a.batch * a.groups * 4;
   if (grid == 0) return hipSuccess;
+  // A few sequences spread over the machine have many splits each: four
+  // waves share each tile's splits.  Otherwise one wave per tile.
+  const bool wide = a.batch * a.groups <= kCombineWideRowGroups;
   if (fused) {
-    hipLaunchKernelGGL(k_combine<true>, dim3(16 * grid), dim3(64), 0, stream, a);
+    if (wide) hipLaunchKernelGGL((k_combine<true, 4>), dim3(16 * grid), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_combine<true, 1>), dim3(16 * grid), dim3(64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_fused_epilogue, dim3(grid), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(k_combine<false>, dim3(16 * grid), dim3(64), 0, stream, a);
+    if (wide) hipLaunchKernelGGL((k_combine<false, 4>), dim3(16 * grid), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_combine<false, 1>), dim3(16 * grid), dim3(64), 0, stream, a);
   }
   return hipGetLastError();
 }
