@@ -39,12 +39,12 @@ LLVM_BIN = "/opt/rocm/llvm/bin"
 SCRATCH_BUDGET = {
     "_ZN3mla8k_decodeILi0ELb0ELb0EEEvNS_10DecodeArgsE": 16,    # bf16 dense
     "_ZN3mla8k_decodeILi0ELb1ELb0EEEvNS_10DecodeArgsE": 104,   # bf16 sparse
-    "_ZN3mla8k_decodeILi0ELb0ELb1EEEvNS_10DecodeArgsE": 524,  # bf16 dense fused
-    "_ZN3mla8k_decodeILi0ELb1ELb1EEEvNS_10DecodeArgsE": 528,  # bf16 sparse fused
+    "_ZN3mla8k_decodeILi0ELb0ELb1EEEvNS_10DecodeArgsE": 316,   # bf16 dense fused
+    "_ZN3mla8k_decodeILi0ELb1ELb1EEEvNS_10DecodeArgsE": 256,   # bf16 sparse fused
     "_ZN3mla8k_decodeILi1ELb0ELb0EEEvNS_10DecodeArgsE": 160,   # V3.2 FP8 dense
     "_ZN3mla8k_decodeILi1ELb1ELb0EEEvNS_10DecodeArgsE": 68,    # V3.2 FP8 sparse
-    "_ZN3mla8k_decodeILi1ELb0ELb1EEEvNS_10DecodeArgsE": 540,   # V3.2 FP8 dense fused
-    "_ZN3mla8k_decodeILi1ELb1ELb1EEEvNS_10DecodeArgsE": 528,   # V3.2 FP8 sparse fused
+    "_ZN3mla8k_decodeILi1ELb0ELb1EEEvNS_10DecodeArgsE": 328,   # V3.2 FP8 dense fused
+    "_ZN3mla8k_decodeILi1ELb1ELb1EEEvNS_10DecodeArgsE": 268,   # V3.2 FP8 sparse fused
     "_ZN3mla8k_decodeILi2ELb1ELb0EEEvNS_10DecodeArgsE": 68,    # V4.1 FP8 sparse
 }
 # Wait states an MFMA result needs before anything else reads or rewrites

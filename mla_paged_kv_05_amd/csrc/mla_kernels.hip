@@ -214,6 +214,12 @@ __device__ __forceinline__ int opaque(int v) {
   asm volatile("" : "+v"(v));
   return v;
 }
+// The same for a wave-uniform value: e.g. a divisor whose reciprocal would
+// otherwise be hoisted to the kernel's start and spilled.
+__device__ __forceinline__ int opaque_s(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
 // This lane's index, recomputed (mbcnt) where it is used, so per-lane LDS
 // address bases live only inside a step, never across the KV loop: there the
 // allocator may spill them, and each reload of a spill would cost a full
@@ -769,8 +775,8 @@ __device__ __forceinline__ void fetch_ids_dma(int32_t* ids_lds, const int32_t* i
 
 // ---------------------------------------------------------------------------
 // Fused prologue / epilogue helpers.  The RoPE angle of pair i at position
-// pos is theta = pos * base^(-2i/64) (the inverse frequencies come from the
-// host in fp64).  Positions reach 10^4 radians, so theta is formed and
+// pos is theta = pos * base^(-2i/64), the inverse frequency formed in fp64
+// on the device.  Positions reach 10^4 radians, so theta is formed and
 // reduced by quarter turns in fp64 (pi/2 as hi + lo); the remainder
 // |r| <= pi/4 is then exact to ~1e-12 and goes to fp32, where Taylor series
 // (sin to r^9, cos to r^10: truncation below 2e-9) give sin and cos to about
@@ -791,29 +797,35 @@ __device__ __forceinline__ void rope_cs(double pos, double inv_freq, float sign,
 }
 
 // RoPE angles of one wave's rows.  A lane needs pair i0 when it holds the
-// low half of its row's dims and i1 for the high half.  When every row of
+// low half of its row's dims and i1 for the high half.  Lane l forms the
+// inverse frequency of pair l & 31 once, and the other lanes read it by
+// lane index (so no lane evaluates exp2 for every pair).  When every row of
 // the wave sits at one position (always with one query token per sequence),
-// each of the 32 pairs is computed once, pair lane & 31 on each lane, and
-// read back by lane index; otherwise each lane computes its own pairs.
+// each of the 32 angles is computed once, pair lane & 31 on each lane, and
+// read back by lane index too; otherwise each lane computes its own pairs.
 struct RopeRow {
   bool shared;
   double pos;
+  double inv;  // inverse frequency of pair lane & 31
   float c, s;
 };
 // Inverse frequency of pair i: base^(-2i/64) = 2^(-(i/32) log2(base)), in fp64.
 __device__ __forceinline__ double rope_inv_freq(int i, double log2_base) { return exp2(-(double)i / 32.0 * log2_base); }
-__device__ __forceinline__ RopeRow rope_row(double pos, bool row_ok, double log2_base, float sign) {
+// inv: the inverse frequency of pair lane & 31 (rope_inv_freq), formed once
+// per launch by the caller.
+__device__ __forceinline__ RopeRow rope_row(double pos, bool row_ok, double inv, float sign) {
   RopeRow r;
   const double pos0 = __builtin_bit_cast(double, uni_u64(__builtin_bit_cast(uint64_t, pos)));
   r.shared = __builtin_amdgcn_ballot_w64(row_ok && pos != pos0) == 0;
   r.pos = pos;
+  r.inv = inv;
   r.c = 0.f;
   r.s = 0.f;
-  if (r.shared) rope_cs(pos0, rope_inv_freq(fresh_lane() & 31, log2_base), sign, r.c, r.s);
+  if (r.shared) rope_cs(pos0, r.inv, sign, r.c, r.s);
   return r;
 }
-__device__ __forceinline__ void rope_pair(const RopeRow& r, double log2_base, float sign, int i0, int i1,
-                                          bool hi, float& c, float& s) {
+__device__ __forceinline__ void rope_pair(const RopeRow& r, float sign, int i0, int i1, bool hi, float& c,
+                                          float& s) {
   if (r.shared) {
     const float c0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r.c), i0));
     const float c1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r.c), i1));
@@ -822,7 +834,7 @@ __device__ __forceinline__ void rope_pair(const RopeRow& r, double log2_base, fl
     c = hi ? c1 : c0;
     s = hi ? s1 : s0;
   } else {
-    rope_cs(r.pos, rope_inv_freq(hi ? i1 : i0, log2_base), sign, c, s);
+    rope_cs(r.pos, __shfl(r.inv, hi ? i1 : i0, 64), sign, c, s);
   }
 }
 
@@ -1138,6 +1150,11 @@ k_decode(DecodeArgs a) {
   f32x16 o[16];
   bool first_piece = true;
 
+  // fused RoPE: the inverse frequency of pair lane & 31, once per launch
+  // (inside the piece loop the compiler hoists the fp64 exp2 anyway, with
+  // its constants spilled and each reload waiting for every load in flight)
+  const double rope_inv = FUSED ? rope_inv_freq(lane & 31, a.rope_log2_base) : 0.0;
+
   int cb = b0, cj = j0, step = 0;
   while (step < nsteps) {
     // ======== one piece: sequence cb, items cj .. piece_end-1
@@ -1169,8 +1186,11 @@ k_decode(DecodeArgs a) {
         if (ks < kQR) {
           qf[ks] = v;
         } else {
-          const int cq = 2 * (ks - kQR) + half;
-          *reinterpret_cast<bf16x8*>(qlds + r32 * q_lds_row_bytes<KVF, FUSED>() + ((cq ^ x) << 4)) = v;
+          // the LDS address is formed here from a fresh lane index, so the
+          // twelve slot addresses are not precomputed and spilled
+          const int ln = fresh_lane(), lr = ln & 31;
+          const int cq = 2 * (ks - kQR) + (ln >> 5);
+          *reinterpret_cast<bf16x8*>(qlds + lr * q_lds_row_bytes<KVF, FUSED>() + ((cq ^ ((lr >> 1) & 7)) << 4)) = v;
         }
       };
       if constexpr (!FUSED) {
@@ -1187,85 +1207,137 @@ k_decode(DecodeArgs a) {
         // + eps) over the row's 576 dims (RMSNorm, then RoPE on dims
         // 512..575 at position len - s_q + t; RoPE is linear, so the row
         // factor may come first), rounded once to fp16 for the fp16 products.
-        // Pass 1 reads the row for its sum of squares only (all 36 chunks in
-        // flight, none kept); pass 2 reads it again (from L2 now) in groups
-        // of four chunks, two groups ahead, and forms q-hat chunk by chunk
-        // with the weight row staged in LDS.  Keeping the row in registers
-        // from pass 1 to pass 2 instead would need 144 VGPRs beside the
-        // fragments and spills them.
-        const RopeRow rr = rope_row(pos, row_ok, a.rope_log2_base, 1.0f);
+        // Pass 1 reads the row for its sum of squares (all 36 chunks in
+        // flight) and leaves the chunks bound for LDS (k-steps kQR..35) raw
+        // in their slots; pass 2 forms q-hat of those in place and reads the
+        // register chunks again (from L2 now), with the weight row staged in
+        // LDS.  Keeping the register chunks from pass 1 to pass 2 instead
+        // would need 96 VGPRs beside the fragments and spills them.
+        // This lane's row and query row address are formed here from a
+        // fresh lane index: hoisted out of the piece loop they are spilled,
+        // and each reload of a spill waits for every load in flight.
+        const int fln = fresh_lane();
+        const int frow = g * kRowsPerWg + wave * 32 + (fln & 31);
+        const bool frow_ok = frow < a.rows;
+        // chunk ks of this lane (dims 16ks + 8half ..) sits at fq + 16ks
+        const uint16_t* fq = a.q + ((int64_t)cb * a.rows + (frow_ok ? frow : 0)) * dqk_of<KVF>() + (fln >> 5) * 8;
         // The first piece also reads the norm weight row beside the query
         // (stored to LDS after pass 1, for every later piece too) and issues
         // its first KV loads here, so that they land during the prologue.
         uint4 wrow = make_uint4(0, 0, 0, 0);
-        if (first_piece && tid < kDqk / 8) wrow = reinterpret_cast<const uint4*>(a.norm_w)[tid];
+        if (first_piece && tid < kDqk / 8) wrow = reinterpret_cast<const uint4*>(a.norm_w)[wave * 64 + fresh_lane()];
+        // LDS slot of query chunk ks >= kQR of this lane (where q-hat goes),
+        // formed from a fresh lane index
+        auto qslot = [&](int ks) -> bf16x8* {
+          const int ln = fresh_lane(), lr = ln & 31;
+          const int cq = 2 * (ks - kQR) + (ln >> 5);
+          return reinterpret_cast<bf16x8*>(qlds + lr * q_lds_row_bytes<KVF, FUSED>() + ((cq ^ ((lr >> 1) & 7)) << 4));
+        };
         float ss = 0.f;
         {
           bf16x8 v[ksteps<KVF>()];
 #pragma unroll
-          for (int ks = 0; ks < ksteps<KVF>(); ++ks) v[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
+          for (int ks = 0; ks < ksteps<KVF>(); ++ks) v[ks] = *reinterpret_cast<const bf16x8*>(fq + 16 * ks);
           if constexpr (KVF == kKvBf16) {
             if (first_piece) issue_first_loads();
           }
+
 #pragma unroll
           for (int ks = 0; ks < ksteps<KVF>(); ++ks) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss += (float)v[ks][e] * (float)v[ks][e];
           }
+          // the chunks that end in LDS are kept there raw for pass 2
+#pragma unroll
+          for (int ks = kQR; ks < ksteps<KVF>(); ++ks) *qslot(ks) = v[ks];
         }
         ss = row_sum2(ss);
         const float inv = 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
         if (first_piece) {
-          if (tid < kDqk / 8) *reinterpret_cast<uint4*>(smem + Lay::kWOff + tid * 16) = wrow;
+          if (tid < kDqk / 8) *reinterpret_cast<uint4*>(smem + Lay::kWOff + (wave * 64 + fresh_lane()) * 16) = wrow;
           lds_barrier();
         }
         const uint16_t* wl = reinterpret_cast<const uint16_t*>(smem + Lay::kWOff);
-        // the second read must not reuse the first one's registers
-        const uint16_t* qrow2 = qrow + opaque(0);
-        constexpr int kG = 4, kNG = ksteps<KVF>() / kG;
-        static_assert(ksteps<KVF>() % kG == 0, "whole groups");
-        bf16x8 cur[kG], nxt[kG], nx2[kG];
+        auto wchunk = [&](int ks) {
+          return *reinterpret_cast<const bf16x8*>(wl + (2 * ks + (fresh_lane() >> 5)) * 8);
+        };
+        // q-hat of raw chunk v (k-step ks) with weight chunk wv; rr only for
+        // the RoPE dims
+        auto qhat = [&](int ks, const bf16x8& v, const bf16x8& wv, const RopeRow& rr) {
+          float y[8];
 #pragma unroll
-        for (int i = 0; i < kG; ++i) cur[i] = *reinterpret_cast<const bf16x8*>(qrow2 + (2 * i + half) * 8);
+          for (int e = 0; e < 8; ++e) y[e] = (float)v[e] * (float)wv[e] * inv;
+          if (ks >= 32) {
 #pragma unroll
-        for (int i = 0; i < kG; ++i) nxt[i] = *reinterpret_cast<const bf16x8*>(qrow2 + (2 * (kG + i) + half) * 8);
+            for (int pp = 0; pp < 4; ++pp) {
+              float cs, sn;
+              rope_pair(rr, 1.0f, 8 * (ks - 32) + pp, 8 * (ks - 32) + 4 + pp, half, cs, sn);
+              const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
+              y[2 * pp] = x0 * cs - x1 * sn;
+              y[2 * pp + 1] = x0 * sn + x1 * cs;
+            }
+          }
+          bf16x8 h;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = to_op16<kF16>(y[e]);
+          put_q(ks, h);
+          return h;
+        };
+        // Pass 2 re-reads only the chunks that stay in registers (k-steps
+        // below kQR), in groups of four, four groups ahead (two or three
+        // ahead measured slower, six no faster); the first four groups'
+        // reads go out first, and the LDS chunks (with the RoPE dims) are
+        // turned into q-hat in place while they are in flight.  The
+        // second read must not reuse the first one's registers, and its
+        // window must hold: each group's reads take their offset from the
+        // q-hat of the group before, so they cannot be hoisted to the top
+        // (all reads at once spill, and every spill reload then waits for
+        // all of them).
+        int qoff = opaque(0);
+        const uint16_t* qrow2 = fq + qoff;
+        constexpr int kG = 4, kNG = kQR / kG, kAhead = 4;
+        static_assert(kQR % kG == 0 && kNG >= kAhead && kQR <= 32, "whole groups; the RoPE dims in LDS");
+        bf16x8 buf[kNG][kG];
+#pragma unroll
+        for (int gg = 0; gg < kAhead; ++gg)
+#pragma unroll
+          for (int i = 0; i < kG; ++i) buf[gg][i] = *reinterpret_cast<const bf16x8*>(qrow2 + 16 * (gg * kG + i));
+        {
+          // the RoPE angles are formed here, right before their use
+          // (position len - s_q + t in integers, converted once: exact)
+          const int r2 = g * kRowsPerWg + wave * 32 + (fresh_lane() & 31);
+          const bool r2_ok = r2 < a.rows;
+          const int t2 = r2_ok ? r2 / opaque_s(a.h_q) : 0;
+          const RopeRow rr = rope_row((double)(Lb - a.s_q + t2), r2_ok, rope_inv, 1.0f);
+          // every raw chunk and weight is read before any q-hat goes back
+          // (a read after a write to LDS is not moved above it, so chunk by
+          // chunk each would wait out the LDS latency)
+          constexpr int kL = ksteps<KVF>() - kQR;
+          bf16x8 raw[kL], wv[kL];
+#pragma unroll
+          for (int j = 0; j < kL; ++j) {
+            raw[j] = *qslot(kQR + j);
+            wv[j] = wchunk(kQR + j);
+          }
+#pragma unroll
+          for (int j = 0; j < kL; ++j) qhat(kQR + j, raw[j], wv[j], rr);
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int g = 0; g < kNG; ++g) {
-          if (g + 2 < kNG) {
+          if (g + kAhead < kNG) {
 #pragma unroll
             for (int i = 0; i < kG; ++i)
-              nx2[i] = *reinterpret_cast<const bf16x8*>(qrow2 + (2 * ((g + 2) * kG + i) + half) * 8);
+              buf[g + kAhead][i] = *reinterpret_cast<const bf16x8*>(fq + qoff + 16 * ((g + kAhead) * kG + i));
           }
+          uint32_t hlast = 0;
 #pragma unroll
-          for (int i = 0; i < kG; ++i) {
-            const int ks = g * kG + i;
-            const bf16x8 v = cur[i];
-            const bf16x8 wv = *reinterpret_cast<const bf16x8*>(wl + (2 * ks + half) * 8);
-            float y[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = (float)v[e] * (float)wv[e] * inv;
-            if (ks >= 32) {
-#pragma unroll
-              for (int pp = 0; pp < 4; ++pp) {
-                float cs, sn;
-                rope_pair(rr, a.rope_log2_base, 1.0f, 8 * (ks - 32) + pp, 8 * (ks - 32) + 4 + pp, half, cs, sn);
-                const float x0 = y[2 * pp], x1 = y[2 * pp + 1];
-                y[2 * pp] = x0 * cs - x1 * sn;
-                y[2 * pp + 1] = x0 * sn + x1 * cs;
-              }
-            }
-            bf16x8 h;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = to_op16<kF16>(y[e]);
-            put_q(ks, h);
-          }
-#pragma unroll
-          for (int i = 0; i < kG; ++i) {
-            cur[i] = nxt[i];
-            nxt[i] = nx2[i];
-          }
-          // one group at a time: the next two groups' reads are in flight,
-          // the weight reads are not hoisted past it
+          for (int i = 0; i < kG; ++i)
+            hlast = __builtin_bit_cast(uint4, qhat(g * kG + i, buf[g][i], wchunk(g * kG + i), RopeRow{})).x;
+          asm volatile("" : "+v"(qoff) : "v"(hlast));
+          // one group at a time: the next groups' reads are in flight, the
+          // weight reads are not hoisted past it
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1626,7 +1698,7 @@ k_decode(DecodeArgs a) {
           // move the 256 accumulators into VGPRs).  amax(O/l) = amax(O)/l
           // exactly, since scaling by a positive constant keeps the order.
           const double pos = (double)Lb - (double)a.s_q + (double)tok;
-          const RopeRow rr = rope_row(pos, row_ok, a.rope_log2_base, -1.0f);
+          const RopeRow rr = rope_row(pos, row_ok, rope_inv, -1.0f);
           float rot[2][16];
 #pragma unroll
           for (int t = 0; t < 2; ++t)
@@ -1636,7 +1708,7 @@ k_decode(DecodeArgs a) {
               for (int pp = 0; pp < 2; ++pp) {
                 const int k0 = 16 * t + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * half
                 float cs, sn;
-                rope_pair(rr, a.rope_log2_base, -1.0f, k0, k0 + 2, half, cs, sn);
+                rope_pair(rr, -1.0f, k0, k0 + 2, half, cs, sn);
                 const float x0 = o[14 + t][4 * qd + 2 * pp] * inv, x1 = o[14 + t][4 * qd + 2 * pp + 1] * inv;
                 rot[t][4 * qd + 2 * pp] = x0 * cs - x1 * sn;
                 rot[t][4 * qd + 2 * pp + 1] = x0 * sn + x1 * cs;
@@ -1762,7 +1834,7 @@ __global__ void __launch_bounds__(256) k_fused_epilogue(DecodeArgs a) {
   const int Lb = a.seqlens[b];
   const int tok = row_ok ? row / a.h_q : 0;
   const double pos = (double)Lb - (double)a.s_q + (double)tok;
-  const RopeRow rr = rope_row(pos, row_ok, a.rope_log2_base, -1.0f);
+  const RopeRow rr = rope_row(pos, row_ok, rope_inv_freq(lane & 31, a.rope_log2_base), -1.0f);
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int e = sub * 16 + k, mt = e >> 2, qd = e & 3;
@@ -1771,7 +1843,7 @@ __global__ void __launch_bounds__(256) k_fused_epilogue(DecodeArgs a) {
     for (int pp = 0; pp < 2; ++pp) {
       const int k0 = 16 * (mt - 14) + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * half
       float cs, sn;
-      rope_pair(rr, a.rope_log2_base, -1.0f, k0, k0 + 2, half, cs, sn);
+      rope_pair(rr, -1.0f, k0, k0 + 2, half, cs, sn);
       const float x0 = acc[k][2 * pp], x1 = acc[k][2 * pp + 1];
       acc[k][2 * pp] = x0 * cs - x1 * sn;
       acc[k][2 * pp + 1] = x0 * sn + x1 * cs;
