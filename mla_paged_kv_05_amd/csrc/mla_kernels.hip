@@ -824,6 +824,7 @@ __device__ __forceinline__ RopeRow rope_row(double pos, bool row_ok, double inv,
   if (r.shared) rope_cs(pos0, r.inv, sign, r.c, r.s);
   return r;
 }
+// i0 and i1 are the same on every lane of the wave (read by lane index).
 __device__ __forceinline__ void rope_pair(const RopeRow& r, float sign, int i0, int i1, bool hi, float& c,
                                           float& s) {
   if (r.shared) {
@@ -835,6 +836,18 @@ __device__ __forceinline__ void rope_pair(const RopeRow& r, float sign, int i0, 
     s = hi ? s1 : s0;
   } else {
     rope_cs(r.pos, __shfl(r.inv, hi ? i1 : i0, 64), sign, c, s);
+  }
+}
+// The same where i0 and i1 may differ between lanes of the wave (readlane
+// needs one lane index for the whole wave; a lane shuffle does not).
+__device__ __forceinline__ void rope_pair_lanes(const RopeRow& r, float sign, int i0, int i1, bool hi, float& c,
+                                                float& s) {
+  const int i = hi ? i1 : i0;
+  if (r.shared) {
+    c = __shfl(r.c, i, 64);
+    s = __shfl(r.s, i, 64);
+  } else {
+    rope_cs(r.pos, __shfl(r.inv, i, 64), sign, c, s);
   }
 }
 
@@ -1792,7 +1805,7 @@ k_decode(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Fused combine, second launch: the epilogue of the 32 rows wt*32.. of row
-// group g of sequence b, once k_combine<true> has merged them.  That merge
+// group g of sequence b, once k_combine<kCombF32, 4> has merged them.  That merge
 // leaves each (32-row tile, 32-dim tile mt)'s fp32 O in the slices of the
 // tile that splits s0 and s0+1 held (every lane's 16 values in the four
 // 16-byte chunks it read there).  Wave `sub` (lanes `lane`) takes d-tiles
@@ -1889,26 +1902,46 @@ constexpr int kCombineWideRowGroups = 8;
 // 16-byte chunks per split (the partials are stored in that order).
 //   lse = ln sum_s e^{lse_s};  O = sum_s e^{lse_s - lse} O_s,
 // splits in ascending order, -inf partials with weight 0.
-// FP32OUT (the fused path's first launch) writes the merged fp32 values
-// over the tile's own slices of splits s0 and s0+1, which no other
+// Output modes: kCombBf16 writes bf16 O.  kCombF32 (the fused path's first
+// launch when few row groups have many splits) writes the merged fp32
+// values over the tile's own slices of splits s0 and s0+1, which no other
 // workgroup reads (lane l rewrites exactly the four chunks it read there),
-// for k_fused_epilogue; the LSE is written either way.
-template <bool FP32OUT, int NW>
-__global__ void __launch_bounds__(64 * NW) k_combine(DecodeArgs a) {
-  const int mt = blockIdx.x & 15, wt = (blockIdx.x >> 4) & 3;
-  const int g = (blockIdx.x >> 6) % a.groups, b = (blockIdx.x >> 6) / a.groups;
+// for k_fused_epilogue.  kCombEpi (the fused path otherwise) gives one
+// workgroup of 8 waves to each 16-row half of a 32-row tile, and runs the
+// row epilogue (conjugate RoPE, row amax through LDS, e4m3 cast) in the
+// same launch: wave v merges d-tiles 2v (lanes 0..31) and 2v+1 (lanes
+// 32..63) of the half's 16 rows, lane 16h + r taking the decode lane
+// 32h + 16*half + r's values.  The LSE is written in every mode.
+constexpr int kCombBf16 = 0, kCombF32 = 1, kCombEpi = 2;
+template <int MODE, int NW>
+__global__ void __launch_bounds__(MODE == kCombEpi ? 512 : 64 * NW) k_combine(DecodeArgs a) {
+  static_assert(MODE != kCombEpi || NW == 1, "one wave per pair of d-tiles");
+  const int lane = threadIdx.x & 63;
+  int tile, mt, half, r32, lane_p;  // lane_p: the decode lane whose values this lane merges
+  if constexpr (MODE == kCombEpi) {
+    tile = blockIdx.x >> 1;
+    mt = 2 * (int)(threadIdx.x >> 6) + (lane >> 5);
+    half = (lane >> 4) & 1;
+    r32 = (blockIdx.x & 1) * 16 + (lane & 15);
+  } else {
+    tile = blockIdx.x >> 4;
+    mt = blockIdx.x & 15;
+    half = lane >> 5;
+    r32 = lane & 31;
+  }
+  lane_p = r32 + 32 * half;
+  const int wt = tile & 3, g = (tile >> 2) % a.groups, b = (tile >> 2) / a.groups;
   const int s0 = a.num_splits[b], ns = a.num_splits[b + 1] - s0;
-  if (ns <= 1) return;
+  if (ns <= 1) return;  // uniform over the workgroup
   // NW waves share the tile: wave w takes splits w, w + NW, ... and the
   // waves' LSE sums and weighted partials are added through LDS
   const int w = NW > 1 ? (int)(threadIdx.x >> 6) : 0;
-  const int lane = threadIdx.x & 63, half = lane >> 5, r32 = lane & 31;
   const int row = g * kRowsPerWg + wt * 32 + r32;
   const int64_t lstride = (int64_t)a.groups * kPartialLseFloats;
   const float* lsep0 = a.part_lse + (int64_t)s0 * lstride + (int64_t)g * kPartialLseFloats + wt * 32 + r32;
   const int64_t pstride = (int64_t)a.groups * kPartialOElems;
   const uint16_t* pb = a.part_o + (int64_t)s0 * pstride + (int64_t)g * kPartialOElems +
-                       (size_t)((wt * 16 + mt) * 2) * 64 * 8 + (size_t)lane * 8;
+                       (size_t)((wt * 16 + mt) * 2) * 64 * 8 + (size_t)lane_p * 8;
   const int nsw = ns > w ? (ns - w + NW - 1) / NW : 0;  // this wave's splits
   const float* lsep = lsep0 + w * lstride;
   const uint16_t* pbw = pb + w * pstride;
@@ -2014,7 +2047,7 @@ __global__ void __launch_bounds__(64 * NW) k_combine(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] += red_acc[k][i][lane];
   }
-  if constexpr (FP32OUT) {
+  if constexpr (MODE == kCombF32) {
     // chunk k (split s0 + (k & 1), 16-byte chunk k >> 1) takes values 4k .. 4k+3
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -2022,6 +2055,54 @@ __global__ void __launch_bounds__(64 * NW) k_combine(DecodeArgs a) {
       *reinterpret_cast<float4*>(dst) = make_float4(acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]);
     }
     if (row < a.rows && mt == 0 && half == 0) a.lse[(int64_t)b * a.rows + row] = lse;
+  } else if constexpr (MODE == kCombEpi) {
+    // value i = 4qd + c sits at d = 32mt + 8qd + 4half + c, so RoPE pair
+    // (d - 448) / 2 of d-tiles 14, 15 is k0 + 2half, k0 = 16(mt - 14) + 4qd + pp
+    __shared__ float amax_s[16][16];
+    const bool row_ok = row < a.rows;
+    const int64_t orow = (int64_t)b * a.rows + row;
+    if (mt >= 14) {  // conjugate RoPE on dims 448..511 (the last wave)
+      const int tok = row_ok ? row / a.h_q : 0;
+      const double pos = (double)a.seqlens[b] - (double)a.s_q + (double)tok;
+      const RopeRow rr = rope_row(pos, row_ok, rope_inv_freq(lane & 31, a.rope_log2_base), -1.0f);
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int k0 = 16 * (mt - 14) + 4 * qd + pp;  // mt differs between the wave's halves
+          float cs, sn;
+          rope_pair_lanes(rr, -1.0f, k0, k0 + 2, half, cs, sn);
+          const float x0 = acc[4 * qd + 2 * pp], x1 = acc[4 * qd + 2 * pp + 1];
+          acc[4 * qd + 2 * pp] = x0 * cs - x1 * sn;
+          acc[4 * qd + 2 * pp + 1] = x0 * sn + x1 * cs;
+        }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(acc[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));  // the row's other half of d-tile mt
+    if (half == 0) amax_s[mt][lane & 15] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, amax_s[i][lane & 15]);
+    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+    const float rs = amax > 0.f ? 448.0f / amax : 1.0f;
+    if (row_ok) {
+      uint8_t* op = reinterpret_cast<uint8_t*>(a.out) + orow * kDv;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        float v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = fminf(fmaxf(acc[4 * qd + c] * rs, -448.f), 448.f);
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], pk, true);
+        *reinterpret_cast<int*>(op + 32 * mt + 8 * qd + 4 * half) = pk;
+      }
+      if (mt == 0 && half == 0) {
+        a.out_scale[orow] = sc;
+        a.lse[orow] = lse;
+      }
+    }
   } else if (row < a.rows) {
     const int64_t orow = (int64_t)b * a.rows + row;
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + orow * kDv;
@@ -2134,16 +2215,22 @@ hipError_t launch_combine(const DecodeArgs& a, bool fused, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   // A few sequences spread over the machine have many splits each: four
   // waves share each tile's splits.  Otherwise one wave per tile.
+  // The fused path with many row groups merges and runs the row epilogue
+  // in one launch (a workgroup per 16 rows); with few, the parallel fp32
+  // merge and the epilogue are two launches.
   const bool wide = a.batch * a.groups <= kCombineWideRowGroups;
   if (fused) {
-    if (wide) hipLaunchKernelGGL((k_combine<true, 4>), dim3(16 * grid), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((k_combine<true, 1>), dim3(16 * grid), dim3(64), 0, stream, a);
+    if (!wide) {
+      hipLaunchKernelGGL((k_combine<kCombEpi, 1>), dim3(2 * grid), dim3(512), 0, stream, a);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((k_combine<kCombF32, 4>), dim3(16 * grid), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_fused_epilogue, dim3(grid), dim3(256), 0, stream, a);
   } else {
-    if (wide) hipLaunchKernelGGL((k_combine<false, 4>), dim3(16 * grid), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((k_combine<false, 1>), dim3(16 * grid), dim3(64), 0, stream, a);
+    if (wide) hipLaunchKernelGGL((k_combine<kCombBf16, 4>), dim3(16 * grid), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_combine<kCombBf16, 1>), dim3(16 * grid), dim3(64), 0, stream, a);
   }
   return hipGetLastError();
 }

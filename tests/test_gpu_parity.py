@@ -129,6 +129,25 @@ def test_fused_multi_token(h_q):
 
 
 @gpu
+@pytest.mark.parametrize("kind", ["dense", "sparse", "s_q2"])
+def test_fused_many_row_groups(kind):
+    """More than eight row groups (sequences x row groups of 128): the fused
+    combine then merges and runs the row epilogue in one launch, one
+    workgroup per 32-row tile, instead of the fp32 merge and a second
+    launch.  Sequences of 1 and 5 keys give rows whose LSE is about one
+    score."""
+    lens = [70, 1500, 5, 700, 2048, 1, 333, 900, 64, 1200]
+    if kind == "s_q2":
+        p = W.make_dense("fmg2", lens[:5], s_q=2, h_q=128, seed=61, fused=True)
+    else:
+        p = W.make_dense("fmg", lens, s_q=1, h_q=128, seed=60, fused=True)
+    if kind == "sparse":
+        p = W.make_sparse_bf16_from_dense(p, topk=300, seed=62)
+    assert p.batch * ((p.s_q * p.h_q + 127) // 128) > 8
+    _parity(p, num_slots=16, what=f"fused many row groups {kind}")
+
+
+@gpu
 def test_fused_lse_short_rows():
     """Rows with a few keys: the LSE is then about one score, so it shows
     the rounding of q-hat directly; it must meet the 1e-3 bar."""
