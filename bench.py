@@ -280,6 +280,10 @@ def main():
     # would time the kernel at another clock.
     stream = torch.cuda.current_stream(dev)
     kevs = [(hip_event(), hip_event()) for _ in range(args.steps)]
+    # one event at each step boundary (eager launches): the per-step
+    # distribution.  Between graph replays they would cost a few
+    # microseconds of the replay pipelining, so graphs go without.
+    sevs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -288,6 +292,7 @@ def main():
         run_steps(args.warmup)
     else:
         for i in range(args.steps):
+            sevs[i].record(stream)
             step(args.warmup + i, kevs[i])
     end.record(stream)
     host = time.perf_counter() - wall0  # host time to enqueue the steps
@@ -323,6 +328,8 @@ def main():
         hip.hipEventDestroy(k0)
         hip.hipEventDestroy(k1)
     meta_ms = [mevs[i][0].elapsed_time(mevs[i][1]) for i in range(args.steps)]
+    step_ms = None if graphs is not None else [
+        sevs[i].elapsed_time(sevs[i + 1] if i + 1 < args.steps else end) for i in range(args.steps)]
     dec_avg = float(np.mean(dec_ms))
     log(f"step {ms * 1e3:.1f} us ({'eager launches' if graphs is None else 'hipGraph replay'}; wall "
         f"{wall / args.steps * 1e6:.1f} us, host enqueue {host / args.steps * 1e6:.1f} us); decode kernel avg {dec_avg * 1e3:.1f} us (p10 "
@@ -354,6 +361,11 @@ def main():
         "metric": "MLA paged decode effective HBM GB/s (algorithmic bytes) + TFLOPS, b=64 h_q=128 seq<=8K",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "step_us": None if step_ms is None else {
+            "median": round(float(np.median(step_ms)) * 1e3, 2),
+            "p10": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
+            "p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+            "timing": "HIP events at each step boundary in the timed region"},
         "vs_baseline": None, "dtype": compute_dtype, "data": "synthetic (seeded, shaped like the workload)",
         "config": {"workload": p.name, "batch": p.batch, "s_q": p.s_q, "h_q": p.h_q, "d_qk": p.d_qk,
                    "d_v": 512, "page": 64, "kv_format": p.kv_format, "causal": bool(p.causal),
