@@ -41,8 +41,10 @@
 //    dequantise exactly to bf16.
 //  * Split rows: the decode stores bf16 partial O and fp32 partial LSE; the
 //    combine (k_combine) merges them on one 64-lane workgroup per 32x32 tile
-//    of O; in the fused path it leaves fp32 tiles that k_fused_epilogue
-//    turns into the rotated, scaled e4m3 output.
+//    of O (four waves sharing the splits when few row groups have many).
+//    The fused path merges and runs the row epilogue (rotated, scaled e4m3
+//    output) in the same launch, or, with few row groups, leaves fp32 tiles
+//    that k_fused_epilogue turns into that output.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 #include <cstdint>
