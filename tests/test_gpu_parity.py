@@ -129,16 +129,19 @@ def test_fused_multi_token(h_q):
 
 
 @gpu
-@pytest.mark.parametrize("kind", ["dense", "sparse", "s_q2"])
+@pytest.mark.parametrize("kind", ["dense", "sparse", "s_q2", "h8_s_q2"])
 def test_fused_many_row_groups(kind):
     """More than eight row groups (sequences x row groups of 128): the fused
     combine then merges and runs the row epilogue in one launch, one
-    workgroup per 32-row tile, instead of the fp32 merge and a second
-    launch.  Sequences of 1 and 5 keys give rows whose LSE is about one
-    score."""
+    workgroup per 16 rows, instead of the fp32 merge and a second launch.
+    Sequences of 1 and 5 keys give rows whose LSE is about one score; with
+    h_q 8 and two query tokens a workgroup's 16 rows sit at two positions,
+    so its conjugate RoPE takes the per-lane angles."""
     lens = [70, 1500, 5, 700, 2048, 1, 333, 900, 64, 1200]
     if kind == "s_q2":
         p = W.make_dense("fmg2", lens[:5], s_q=2, h_q=128, seed=61, fused=True)
+    elif kind == "h8_s_q2":
+        p = W.make_dense("fmg8", lens, s_q=2, h_q=8, seed=64, fused=True)
     else:
         p = W.make_dense("fmg", lens, s_q=1, h_q=128, seed=60, fused=True)
     if kind == "sparse":
