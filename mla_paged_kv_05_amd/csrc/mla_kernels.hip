@@ -62,7 +62,8 @@ namespace mla {
 // has none of it.  Lane 0 of wave 0 of each workgroup records the 100 MHz
 // s_memrealtime clock at kernel start, at each piece's start, after its
 // prologue, after its main loop and at its end (up to kTrPieces pieces), and
-// at kernel end, with vector stores into a static array that
+// at kernel end (and, in the first piece, after the slot's metadata read and
+// the fused prologue's two passes), with vector stores into a static array that
 // mla_phase_trace_copy() returns.  Wave 0 also sums the shader clock
 // (s_memtime) spent in each phase of its 32-key steps (kTrSteps phases:
 // load wait; barrier, with the fused fp16 conversion or the one-tile FP8
@@ -88,6 +89,16 @@ __device__ int g_phase_items[kTrWgs * kTrPieces];
     tr_last = t_;                                                                         \
   } while (0)
 #define MLA_ST_STEP do { ++tr_steps; } while (0)
+// First piece only: a stamp once `dep` is computed (the scalar-memory wait
+// also drains outstanding LDS operations), in slot k (29: the slot's
+// metadata read; fused prologue 30: pass 1's row sum, 31: pass 2 done).
+#define MLA_TR_FIRST(k, cons, dep)                                                        \
+  do {                                                                                    \
+    asm volatile("" ::cons(dep));                                                         \
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                    \
+    if (threadIdx.x == 0 && blockIdx.x < kTrWgs && tr_p == 0)                             \
+      g_phase_t[blockIdx.x * kTrPer + (k)] = __builtin_amdgcn_s_memrealtime();            \
+  } while (0)
 #define MLA_TR_WG_ACTIVE \
   if (threadIdx.x == 0 && blockIdx.x < kTrWgs) g_phase_t[blockIdx.x * kTrPer] = tr_t0;
 #define MLA_TR(k)                                                                              \
@@ -117,6 +128,7 @@ __device__ int g_phase_items[kTrWgs * kTrPieces];
 #define MLA_ST_BEGIN do {} while (0)
 #define MLA_ST(i) do {} while (0)
 #define MLA_ST_STEP do {} while (0)
+#define MLA_TR_FIRST(k, cons, dep) do {} while (0)
 #endif
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -959,6 +971,7 @@ k_decode(DecodeArgs a) {
   const int j0 = uni(sload(ms, 1)), b1 = uni(sload(ms, 2)), j1 = uni(sload(ms, 3)),
             nitems = uni(sload(ms, 5));
   int split_k = uni(sload(ms, 4));
+  MLA_TR_FIRST(29, "s", split_k);
   const int nsteps = 2 * nitems;
 
   // this lane's query row within the sequence
@@ -1267,6 +1280,7 @@ k_decode(DecodeArgs a) {
           for (int ks = kQR; ks < ksteps<KVF>(); ++ks) *qslot(ks) = v[ks];
         }
         ss = row_sum2(ss);
+        MLA_TR_FIRST(30, "v", ss);
         const float inv = 1.0f / sqrtf(ss / (float)kDqk + a.norm_eps);
         if (first_piece) {
           if (tid < kDqk / 8) *reinterpret_cast<uint4*>(smem + Lay::kWOff + (wave * 64 + fresh_lane()) * 16) = wrow;
@@ -1355,6 +1369,7 @@ k_decode(DecodeArgs a) {
           // weight reads are not hoisted past it
           __builtin_amdgcn_sched_barrier(0);
         }
+        MLA_TR_FIRST(31, "v", qoff);
       }
     }
     if constexpr (KVF == kKvBf16 && !FUSED) {

@@ -26,6 +26,7 @@ from . import workloads as W
 
 KTR_PER, KTR_PIECES = 40, 7   # the layout the traced kernel writes
 KTR_STEP_OFF, KTR_STEPS = 32, 6
+KTR_META, KTR_PASS1, KTR_PASS2 = 29, 30, 31   # first-piece stamps
 STEP_PHASES = ["load wait", "barrier (fused bf16: with the fp16 conversion; one-tile FP8: with the dequantisation)",
                "load issue", "S^T (two-tile FP8: with the next tile's dequantisation)", "softmax and lazy rescale",
                "P.V issue"]
@@ -101,6 +102,11 @@ def run(name: str, warmup: int = 6) -> str:
     # steps' main-loop time on the 100 MHz clock
     ticks_per_us = acc.sum() / max(loop.sum(), 1e-9)
     first = (tr[act, 1] - tr[act, 0]) / CLOCK_MHZ
+
+    def span(a, b):  # median of slot b - slot a over the workgroups that stamped both
+        ta, tb = tr[act, a], tr[act, b]
+        ok = (ta > 0) & (tb > 0)
+        return float(np.median((tb[ok] - ta[ok]) / CLOCK_MHZ)) if ok.any() else float("nan")
     lines = [
         f"Phase timeline of one `{name}` decode launch (`python -m mla_paged_kv_05_amd.phase_trace "
         f"--workload {name}`):",
@@ -111,8 +117,12 @@ def run(name: str, warmup: int = 6) -> str:
         f"| workgroup start spread | {start.max():.1f} us |",
         f"| workgroup end: min / median / max | {end.min():.1f} / {np.median(end):.1f} / {end.max():.1f} us |",
         f"| pieces | {len(pro)} ({len(pro) / nact:.2f} per workgroup) |",
-        f"| start to first piece, median | {np.median(first):.2f} us |",
+        f"| start to first piece, median | {np.median(first):.2f} us "
+        f"(to the slot's metadata read {span(0, KTR_META):.2f}, then {span(KTR_META, 1):.2f}) |",
         f"| piece prologue (query, first loads, drain): median / p90 | {np.median(pro):.2f} / {np.percentile(pro, 90):.2f} us |",
+        *([f"| first piece's fused prologue: pass 1 (query reads, first KV loads, row sum) / pass 2 (q-hat) / "
+           f"drain, median | {span(1, KTR_PASS1):.2f} / {span(KTR_PASS1, KTR_PASS2):.2f} / {span(KTR_PASS2, 2):.2f} us |"]
+          if p.fused else []),
         f"| main loop per 64-key item, median | {np.median(loop / np.maximum(nit, 1)):.3f} us |",
         f"| piece finalize: median / p90 | {np.median(fin):.2f} / {np.percentile(fin, 90):.2f} us |",
         f"| per workgroup: prologue / main loop / finalize | {pro.sum() / nact:.1f} / {loop.sum() / nact:.1f} / "
