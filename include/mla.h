@@ -133,7 +133,7 @@ typedef struct mla_decode_params {
   const int32_t* block_table;  /* int32 [batch][max_blocks_per_seq]; may be NULL if sparse  */
   int32_t max_blocks_per_seq;
   const int32_t* cache_seqlens;/* int32 [batch]                                            */
-  float softmax_scale;         /* applied to q.K (typically 576^-0.5)                     */
+  float softmax_scale;         /* applied to q.K (typically 576^-0.5); positive and finite */
   int32_t causal;              /* bottom-right aligned: token t sees keys j <= len-s_q+t    */
   const int32_t* indices;      /* NULL = dense; else int32 [batch][s_q][topk] flat token ids, -1 = masked */
   int32_t topk;

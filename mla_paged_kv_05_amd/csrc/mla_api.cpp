@@ -129,6 +129,8 @@ static mla_status build_args(const mla_decode_params* p, mla::DecodeArgs& a, boo
   if (p->flags & ~MLA_FLAG_DEFER_COMBINE)
     return fail(MLA_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
   if (p->num_blocks < 0) return fail(MLA_ERR_INVALID_ARG, "num_blocks=%lld", (long long)p->num_blocks);
+  if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be positive and finite (got %g)", (double)p->softmax_scale);
   sparse = p->indices != nullptr;
   if (sparse) {
     if (p->topk < 1) return fail(MLA_ERR_INVALID_ARG, "topk=%d with indices", p->topk);

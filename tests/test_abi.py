@@ -91,6 +91,10 @@ def status(p):
     ({"s_q": 1024, "h_q": 128}, 2),
     ({"batch": 20000}, 2),
     ({"fused": 1}, 1),
+    ({"softmax_scale": 0.0}, 1),
+    ({"softmax_scale": -0.04}, 1),
+    ({"softmax_scale": float("inf")}, 1),
+    ({"softmax_scale": float("nan")}, 1),
 ])
 def test_rejects(kw, expect):
     st, msg = status(good_params(**kw))
