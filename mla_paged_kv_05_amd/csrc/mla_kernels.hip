@@ -1698,20 +1698,27 @@ k_decode(DecodeArgs a) {
     // ======== finalize the piece: O / l and LSE; direct output or partial
     o_settle(o);
     {
+      // this lane's row, formed again from a fresh lane index: kept from the
+      // kernel start, these values would be spilled and reloaded here
+      const int fln = fresh_lane();
+      const int frow = g * kRowsPerWg + wave * 32 + (fln & 31);
+      const bool frow_ok = frow < a.rows;
+      const int fhalf = fln >> 5;
+      const int ftok = frow_ok ? frow / a.h_q : 0;
       const float lt = row_sum2(lsum);
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
       const float lse2 = lt > 0.f ? m_used + __builtin_amdgcn_logf(lt) : -INFINITY;
       const int nsplit = uni(sload(a.num_splits, cb + 1) - sload(a.num_splits, cb));
       if (nsplit == 1) {
-        const int64_t orow = (int64_t)cb * a.rows + row;
+        const int64_t orow = (int64_t)cb * a.rows + frow;
         if constexpr (!FUSED) {
-          if (row_ok) {
+          if (frow_ok) {
             uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + orow * kDv;
 #pragma unroll
             for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
               for (int qd = 0; qd < 4; ++qd) {
-                const int d = 32 * mt + 8 * qd + 4 * half;
+                const int d = 32 * mt + 8 * qd + 4 * fhalf;
                 const __bf16 v0 = (__bf16)(o[mt][4 * qd] * inv), v1 = (__bf16)(o[mt][4 * qd + 1] * inv);
                 const __bf16 v2 = (__bf16)(o[mt][4 * qd + 2] * inv), v3 = (__bf16)(o[mt][4 * qd + 3] * inv);
                 uint2 pk;
@@ -1719,7 +1726,7 @@ k_decode(DecodeArgs a) {
                 pk.y = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
                 *reinterpret_cast<uint2*>(op + d) = pk;
               }
-            if (half == 0) a.lse[orow] = lse2 * kLn2;
+            if (fhalf == 0) a.lse[orow] = lse2 * kLn2;
           }
         } else {
           // conjugate RoPE on dims 448..511 (d-tiles 14, 15), amax over the
@@ -1727,8 +1734,8 @@ k_decode(DecodeArgs a) {
           // rotated values are held in VGPRs (scaling all of O at once would
           // move the 256 accumulators into VGPRs).  amax(O/l) = amax(O)/l
           // exactly, since scaling by a positive constant keeps the order.
-          const double pos = (double)Lb - (double)a.s_q + (double)tok;
-          const RopeRow rr = rope_row(pos, row_ok, rope_inv, -1.0f);
+          const double pos = (double)Lb - (double)a.s_q + (double)ftok;
+          const RopeRow rr = rope_row(pos, frow_ok, rope_inv, -1.0f);
           float rot[2][16];
 #pragma unroll
           for (int t = 0; t < 2; ++t)
@@ -1736,9 +1743,9 @@ k_decode(DecodeArgs a) {
             for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
               for (int pp = 0; pp < 2; ++pp) {
-                const int k0 = 16 * t + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * half
+                const int k0 = 16 * t + 4 * qd + pp;  // RoPE pair (d - 448) / 2 = k0 + 2 * fhalf
                 float cs, sn;
-                rope_pair(rr, -1.0f, k0, k0 + 2, half, cs, sn);
+                rope_pair(rr, -1.0f, k0, k0 + 2, fhalf, cs, sn);
                 const float x0 = o[14 + t][4 * qd + 2 * pp] * inv, x1 = o[14 + t][4 * qd + 2 * pp + 1] * inv;
                 rot[t][4 * qd + 2 * pp] = x0 * cs - x1 * sn;
                 rot[t][4 * qd + 2 * pp + 1] = x0 * sn + x1 * cs;
@@ -1756,10 +1763,10 @@ k_decode(DecodeArgs a) {
           amax = row_max2(amax);
           const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
           const float rs = amax > 0.f ? 448.0f / amax : 1.0f;
-          if (row_ok) {
+          if (frow_ok) {
             uint8_t* op = reinterpret_cast<uint8_t*>(a.out) + orow * kDv;
             auto put = [&](int mt, int qd, float v0, float v1, float v2, float v3) {
-              const int d = 32 * mt + 8 * qd + 4 * half;
+              const int d = 32 * mt + 8 * qd + 4 * fhalf;
               v0 = fminf(fmaxf(v0 * rs, -448.f), 448.f);
               v1 = fminf(fmaxf(v1 * rs, -448.f), 448.f);
               v2 = fminf(fmaxf(v2 * rs, -448.f), 448.f);
@@ -1779,7 +1786,7 @@ k_decode(DecodeArgs a) {
 #pragma unroll
               for (int qd = 0; qd < 4; ++qd)
                 put(14 + t, qd, rot[t][4 * qd], rot[t][4 * qd + 1], rot[t][4 * qd + 2], rot[t][4 * qd + 3]);
-            if (half == 0) {
+            if (fhalf == 0) {
               a.lse[orow] = lse2 * kLn2;
               a.out_scale[orow] = sc;
             }
@@ -1790,7 +1797,7 @@ k_decode(DecodeArgs a) {
         // to bf16, stored in register order [wave][d-tile][quad pair][lane][8]
         const int64_t pidx = (int64_t)uni(sload(a.num_splits, cb) + split_k) * a.groups + g;
         const __amdgpu_buffer_rsrc_t prs = buf_rsrc(uni_ptr(a.part_o + pidx * kPartialOElems), kPartialOElems * 2);
-        const int vbase = (wave * (16 * 2 * 64 * 8) + lane * 8) * 2;
+        const int vbase = (wave * (16 * 2 * 64 * 8) + fln * 8) * 2;
 #pragma unroll
         for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
@@ -1803,10 +1810,10 @@ k_decode(DecodeArgs a) {
             }
             __builtin_amdgcn_raw_buffer_store_b128(w, prs, vbase + (mt * 2 + q2) * 64 * 8 * 2, 0, kPastL2);
           }
-        if (half == 0)
+        if (fhalf == 0)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2 * kLn2),
                                                 buf_rsrc(uni_ptr(a.part_lse + pidx * kPartialLseFloats), kPartialLseFloats * 4),
-                                                (wave * 32 + r32) * 4, 0, kPastL2);
+                                                (wave * 32 + (fln & 31)) * 4, 0, kPastL2);
       }
     }
     MLA_TR(4);
