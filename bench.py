@@ -377,6 +377,13 @@ def main():
         "tflops": round(tflops, 2),
         "roofline": dict(roof, **{
             "traffic": traffic,
+            # the same counters' bytes beside it: the decode's over its
+            # algorithmic bytes (split partials, query re-reads), and what
+            # the combine of those partials reads and writes per step
+            "traffic_over_algorithmic": None if tr is None else round(traffic / nbytes, 4),
+            "combine_traffic": None if tr is None else {
+                "read_bytes": tr["combine_read_bytes_per_launch"],
+                "write_bytes": tr["combine_write_bytes_per_launch"]},
             "kernel": "k_decode",
             "kernel_avg_us": round(dec_avg * 1e3, 2),
             "kernel_median_us": round(float(np.median(dec_ms)) * 1e3, 2),
