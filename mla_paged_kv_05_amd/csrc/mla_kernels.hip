@@ -1159,7 +1159,9 @@ k_decode(DecodeArgs a) {
       fetch_ids(fb, fj, fh, s);
       advance(fb, fj, fh);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    // plain FP8 decodes wait for these ids in the first piece's prologue,
+    // with its query loads in flight
+    if constexpr (KVF == kKvBf16 || FUSED) __builtin_amdgcn_s_waitcnt(0);
   }
   auto issue_first_loads = [&]() {
     for (int s = 0; s < min(KVF == kKvBf16 ? kDepth : kRawAhead, nsteps); ++s) {
@@ -1167,7 +1169,7 @@ k_decode(DecodeArgs a) {
       advance_load();
     }
   };
-  if constexpr (KVF != kKvBf16) issue_first_loads();
+  if constexpr (KVF != kKvBf16 && FUSED) issue_first_loads();
 
   constexpr int kQR = q_reg_steps<KVF, FUSED>();
   uint8_t* qlds = smem + Lay::kQOff + wave * q_lds_wave_bytes<KVF, FUSED>();
@@ -1222,9 +1224,23 @@ k_decode(DecodeArgs a) {
         }
       };
       if constexpr (!FUSED) {
+        bf16x8 vq[ksteps<KVF>()];
+#pragma unroll
+        for (int ks = 0; ks < ksteps<KVF>(); ++ks) vq[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
+        if constexpr (KVF != kKvBf16) {
+          // FP8 records: the first piece's first record loads go out behind
+          // the query loads, so that the two latencies overlap.  Sparse
+          // record loads read their ids from LDS: the id loads went out
+          // before the query loads, so waiting until only the query loads
+          // may be outstanding lands them.
+          if (first_piece) {
+            if constexpr (SPARSE) wait_vmcnt<ksteps<KVF>()>();
+            issue_first_loads();
+          }
+        }
 #pragma unroll
         for (int ks = 0; ks < ksteps<KVF>(); ++ks) {
-          const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + half) * 8);
+          const bf16x8 v = vq[ks];
           // fp16 products (the V3.2 FP8 cache): bf16 q converts exactly
           // (magnitudes in [2^-14, 65504])
           if constexpr (kF16) put_q(ks, __builtin_bit_cast(bf16x8, bf16x8_to_f16x8(__builtin_bit_cast(uint4, v))));
