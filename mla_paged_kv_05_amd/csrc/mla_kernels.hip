@@ -1067,11 +1067,14 @@ k_decode(DecodeArgs a) {
   };
   fetch_phys();
   fetch_next_len();
-  if constexpr (kVecWalk) {
+  // The plain dense decode reads its first walker words in the first
+  // piece's prologue, once its query loads are out; the fused one here.
+  constexpr bool kLateLand = kVecWalk && !FUSED;
+  if constexpr (kVecWalk && !kLateLand) {
     __builtin_amdgcn_s_waitcnt(0);  // kernel start: nothing else is in flight yet
     lds_barrier();
   }
-  land();
+  if constexpr (!kLateLand) land();
   // stage the walker's step as step `step` into its ring slot
   auto issue_load = [&](int step) {
     const int rs = step % (KVF == kKvBf16 ? kTileRing : kRing);
@@ -1389,7 +1392,16 @@ k_decode(DecodeArgs a) {
       }
     }
     if constexpr (KVF == kKvBf16 && !FUSED) {
-      if (first_piece) issue_first_loads();  // after the query loads: latencies overlap
+      // after the query loads, so that the latencies overlap; the walker
+      // words went out before them, so waiting until only the query loads
+      // may be outstanding lands the words (each wave reads its own)
+      if (first_piece) {
+        if constexpr (kLateLand) {
+          wait_vmcnt<ksteps<KVF>()>();
+          land();
+        }
+        issue_first_loads();
+      }
     }
     wait_vmcnt<0>();
     lds_barrier();  // every wave's loads of the piece's first step (and Q in LDS) landed
